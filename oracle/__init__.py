@@ -1,0 +1,160 @@
+"""CPU oracle for the tiled GEMM: a float64 triple loop over the exact input bytes.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline leg of the
+benchmark may import this package.  It shares no code with the HIP library and imports nothing
+from it.  The arithmetic lives in oracle.c (plain C, gcc -O3 -fopenmp -ffp-contract=off); this
+module only marshals numpy arrays into it.  See oracle.c for the definition that is computed and
+the passages of the pages it follows.
+
+Parity pins (tests/test_oracle.py): exact brute force with fractions.Fraction on every shape in
+{1..4}^3, identity and permutation matrices, rank-1 closed forms, alpha/beta linearity,
+A*B == (B^T A^T)^T, an exhaustive OCP E4M3 table, bf16 ties-to-even, closed-form GELU values, and
+a numpy float64 matmul cross-check.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+TYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
+EPI_BIAS = 1
+EPI_GELU = 2
+
+_lib = None
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_dbl = ctypes.c_double
+_vp = ctypes.c_void_p
+_PROBLEM = [_i64, _i64, _i64, _int, _int, _dbl, _vp, _i64, _dbl, _vp, _i64, _dbl, _dbl, _vp,
+            _i64, _int, _int, _int, ctypes.c_uint, _vp]
+
+
+def lib():
+    """Load liboracle.so, building it with gcc first if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build
+            _build.build()
+        L = ctypes.CDLL(LIB_PATH)
+        L.oracle_decode.argtypes = [_int, _vp, _i64, _vp]
+        L.oracle_decode.restype = _int
+        L.oracle_gelu.argtypes = [_dbl]
+        L.oracle_gelu.restype = _dbl
+        L.oracle_gemm.argtypes = _PROBLEM + [_vp, _vp]
+        L.oracle_gemm.restype = _int
+        L.oracle_gemm_rows.argtypes = _PROBLEM + [_i64, _i64, _vp, _vp]
+        L.oracle_gemm_rows.restype = _int
+        L.oracle_gemm_points.argtypes = _PROBLEM + [_i64, _vp, _vp, _vp, _vp]
+        L.oracle_gemm_points.restype = _int
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = _int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def decode(dtype: str, stored: np.ndarray) -> np.ndarray:
+    """Decode stored words/bytes of `dtype` to float64 with the oracle's own decoders."""
+    a = np.ascontiguousarray(stored)
+    n = a.size
+    out = np.empty(a.shape, dtype=np.float64)
+    rc = lib().oracle_decode(TYPE_CODE[dtype], _ptr(a), n, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_decode({dtype}) failed: {rc}")
+    return out
+
+
+def gelu(t: float) -> float:
+    return lib().oracle_gelu(float(t))
+
+
+def _args(M, N, K, trans_a, trans_b, alpha, A, lda, scale_a, B, ldb, scale_b, beta, C, ldc,
+          a_type, b_type, c_type, epilogue, bias):
+    return (M, N, K, int(bool(trans_a)), int(bool(trans_b)), float(alpha), _ptr(A), lda,
+            float(scale_a), _ptr(B), ldb, float(scale_b), float(beta),
+            _ptr(C) if beta != 0.0 else None, ldc, TYPE_CODE[a_type], TYPE_CODE[b_type],
+            TYPE_CODE[c_type], int(epilogue), _ptr(bias))
+
+
+def _problem_args(p):
+    A = np.ascontiguousarray(p.A)
+    B = np.ascontiguousarray(p.B)
+    C = np.ascontiguousarray(p.C)
+    bias = None if p.bias is None else np.ascontiguousarray(p.bias, dtype=np.float32)
+    keep = (A, B, C, bias)
+    return keep, _args(p.M, p.N, p.K, p.trans_a, p.trans_b, p.alpha, A, p.lda, p.scale_a, B,
+                       p.ldb, p.scale_b, p.beta, C, p.ldc, p.a_type, p.b_type, p.c_type,
+                       p.epilogue, bias)
+
+
+def gemm(p) -> Tuple[np.ndarray, np.ndarray]:
+    """Full reference (Cref, D), each M x N float64, for a problem with the fields of
+    workloads.Problem (M, N, K, trans_a, trans_b, alpha, beta, a_type, b_type, c_type,
+    epilogue, A, B, C, bias, scale_a, scale_b, lda, ldb, ldc)."""
+    keep, args = _problem_args(p)
+    Cref = np.empty((p.M, p.N), dtype=np.float64)
+    D = np.empty((p.M, p.N), dtype=np.float64)
+    rc = lib().oracle_gemm(*args, _ptr(Cref), _ptr(D))
+    del keep
+    if rc != 0:
+        raise ValueError(f"oracle_gemm failed: {rc}")
+    return Cref, D
+
+
+def gemm_raw(M, N, K, trans_a, trans_b, alpha, A, lda, scale_a, B, ldb, scale_b, beta, C, ldc,
+             a_type, b_type, c_type, epilogue=0, bias=None) -> Tuple[np.ndarray, np.ndarray]:
+    """(Cref, D) for explicit BLAS-style arguments, including leading dimensions larger than
+    the logical ones.  A, B, C are flat or 2-D arrays of storage words."""
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    C = None if C is None else np.ascontiguousarray(C)
+    bias = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    Cref = np.empty((M, N), dtype=np.float64)
+    D = np.empty((M, N), dtype=np.float64)
+    rc = lib().oracle_gemm(*_args(M, N, K, trans_a, trans_b, alpha, A, lda, scale_a, B, ldb,
+                                  scale_b, beta, C, ldc, a_type, b_type, c_type, epilogue,
+                                  bias), _ptr(Cref), _ptr(D))
+    if rc != 0:
+        raise ValueError(f"oracle_gemm failed: {rc}")
+    return Cref, D
+
+
+def gemm_rows(p, row0: int, nrows: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Rows [row0, row0+nrows) of (Cref, D)."""
+    keep, args = _problem_args(p)
+    Cref = np.empty((nrows, p.N), dtype=np.float64)
+    D = np.empty((nrows, p.N), dtype=np.float64)
+    rc = lib().oracle_gemm_rows(*args, row0, nrows, _ptr(Cref), _ptr(D))
+    del keep
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_rows failed: {rc}")
+    return Cref, D
+
+
+def gemm_points(p, rows: np.ndarray, cols: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """(Cref, D) at the listed output entries, each computed on its own."""
+    keep, args = _problem_args(p)
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    c = np.ascontiguousarray(cols, dtype=np.int64)
+    Cref = np.empty(r.size, dtype=np.float64)
+    D = np.empty(r.size, dtype=np.float64)
+    rc = lib().oracle_gemm_points(*args, r.size, _ptr(r), _ptr(c), _ptr(Cref), _ptr(D))
+    del keep
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_points failed: {rc}")
+    return Cref, D
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()

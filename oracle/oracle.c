@@ -1,0 +1,239 @@
+/*
+ * CPU oracle for the tiled GEMM  C = epi(alpha * sa*sb * op(A) op(B) + beta * C_in [+ bias]).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct definition that
+ * the HIP library is checked against.  It shares no code with the HIP library: its decoders,
+ * its loops and its GELU are its own.  Only tests, the smoke check and the CPU-baseline leg of
+ * the benchmark may load it.
+ *
+ * What it computes (the textbook product that every page's tiling only reorganises:
+ * "Case Study: The Tiled GEMM" ends in the BLAS form alpha*AB + beta*C; "Case Study: Steel's
+ * BlockMMA" applies bias / activation / scaling per element after the product; "Rigel"
+ * (arXiv 2606.12765) section 3 builds its reference in float64 from the exact quantised
+ * bytes the GPU consumes):
+ *
+ *   a(i,k) = transA ? A[k*lda + i] : A[i*lda + k]      decoded exactly to double
+ *   b(k,j) = transB ? B[j*ldb + k] : B[k*ldb + j]      decoded exactly to double
+ *   S(i,j) = sum_k a(i,k) b(k,j)                        double, k ascending
+ *   D(i,j) = sa*sb * sum_k |a(i,k) b(k,j)|             double (denominator of the gate)
+ *   t      = alpha*(sa*sb)*S + (beta != 0 ? beta*C_in(i,j) : 0) + (BIAS ? bias[j] : 0)
+ *   Cref   = GELU ? 0.5*t*(1 + erf(t/sqrt(2))) : t      double, libm erf
+ *
+ * Every product of two decoded inputs is exact in double (at most 24+24 significant bits), so
+ * the only roundings are the k-ordered sums and the epilogue, each at 2^-53.
+ * Build: gcc -O3 -fopenmp -ffp-contract=off (no fast-math: no reassociation, no FMA).
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_E4M3 = 3 };
+enum { OR_EPI_BIAS = 1u, OR_EPI_GELU = 2u };
+
+static int esize_of(int t) {
+  switch (t) {
+    case OR_F32: return 4;
+    case OR_F16: return 2;
+    case OR_BF16: return 2;
+    case OR_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 mantissa bits; subnormals m * 2^-24. */
+static double dec_f16(uint16_t h) {
+  int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0) v = ldexp((double)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexp((double)(1024 + m), e - 25);
+  return s ? -v : v;
+}
+
+/* bfloat16 is the upper half of an IEEE binary32 word. */
+static double dec_bf16(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* OCP 8-bit E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa bits, no infinities, NaN only at
+ * S.1111.111, largest finite 448, subnormals m * 2^-9. */
+static double dec_e4m3(uint8_t q) {
+  int s = q >> 7, e = (q >> 3) & 15, m = q & 7;
+  double v;
+  if (e == 15 && m == 7) v = NAN;
+  else if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp((double)(8 + m), e - 10);
+  return s ? -v : v;
+}
+
+static double dec_f32(const void* p) {
+  float f;
+  memcpy(&f, p, 4);
+  return (double)f;
+}
+
+static double dec_one(int t, const uint8_t* base, int64_t idx) {
+  switch (t) {
+    case OR_F32: return dec_f32(base + 4 * idx);
+    case OR_F16: { uint16_t h; memcpy(&h, base + 2 * idx, 2); return dec_f16(h); }
+    case OR_BF16: { uint16_t h; memcpy(&h, base + 2 * idx, 2); return dec_bf16(h); }
+    case OR_E4M3: return dec_e4m3(base[idx]);
+    default: return NAN;
+  }
+}
+
+/* Decode n consecutive stored values of type t into doubles. Returns 0, or -1 on bad type. */
+int oracle_decode(int t, const void* src, int64_t n, double* dst) {
+  if (esize_of(t) == 0) return -1;
+  const uint8_t* p = (const uint8_t*)src;
+  for (int64_t i = 0; i < n; ++i) dst[i] = dec_one(t, p, i);
+  return 0;
+}
+
+/* GELU with the Gauss error function: x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)). */
+double oracle_gelu(double t) { return 0.5 * t * (1.0 + erf(t / sqrt(2.0))); }
+
+typedef struct {
+  int64_t M, N, K;
+  int transA, transB;
+  double alpha, sa, sb, beta;
+  const uint8_t *A, *B, *Cin;
+  int64_t lda, ldb, ldc;
+  int at, bt, ct;
+  unsigned epi;
+  const float* bias;
+} problem_t;
+
+static int check(const problem_t* p) {
+  if (p->M < 0 || p->N < 0 || p->K < 0) return -1;
+  if (!esize_of(p->at) || !esize_of(p->bt) || !esize_of(p->ct)) return -1;
+  if (p->K > 0 && (!p->A || !p->B)) return -1;
+  if (p->beta != 0.0 && !p->Cin) return -1;
+  if ((p->epi & OR_EPI_BIAS) && !p->bias) return -1;
+  return 0;
+}
+
+/* op(B) as a K x N row-major double matrix. */
+static double* decode_opB(const problem_t* p) {
+  double* b = (double*)malloc(sizeof(double) * (size_t)(p->K > 0 ? p->K : 1) *
+                              (size_t)(p->N > 0 ? p->N : 1));
+  if (!b) return NULL;
+#pragma omp parallel for schedule(static)
+  for (int64_t k = 0; k < p->K; ++k)
+    for (int64_t j = 0; j < p->N; ++j)
+      b[k * p->N + j] = dec_one(p->bt, p->B, p->transB ? j * p->ldb + k : k * p->ldb + j);
+  return b;
+}
+
+static double apply_epilogue(const problem_t* p, int64_t i, int64_t j, double s) {
+  double t = p->alpha * (p->sa * p->sb) * s;
+  if (p->beta != 0.0) t += p->beta * dec_one(p->ct, p->Cin, i * p->ldc + j);
+  if (p->epi & OR_EPI_BIAS) t += (double)p->bias[j];
+  if (p->epi & OR_EPI_GELU) t = oracle_gelu(t);
+  return t;
+}
+
+/* Rows [row0, row0 + nrows) of Cref and D (each nrows x N, row-major). */
+static int run_rows(const problem_t* p, int64_t row0, int64_t nrows, double* Cref, double* D) {
+  if (check(p)) return -1;
+  if (row0 < 0 || nrows < 0 || row0 + nrows > p->M) return -1;
+  if (nrows == 0 || p->N == 0) return 0;
+  double* b = decode_opB(p);
+  if (!b) return -2;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)p->N);
+    double* d = (double*)malloc(sizeof(double) * (size_t)p->N);
+    if (!s || !d) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = row0 + r;
+        for (int64_t j = 0; j < p->N; ++j) { s[j] = 0.0; d[j] = 0.0; }
+        for (int64_t k = 0; k < p->K; ++k) {
+          const double a = dec_one(p->at, p->A, p->transA ? k * p->lda + i : i * p->lda + k);
+          const double* brow = b + k * p->N;
+          for (int64_t j = 0; j < p->N; ++j) {
+            const double prod = a * brow[j];
+            s[j] += prod;
+            d[j] += fabs(prod);
+          }
+        }
+        for (int64_t j = 0; j < p->N; ++j) {
+          Cref[r * p->N + j] = apply_epilogue(p, i, j, s[j]);
+          D[r * p->N + j] = (p->sa * p->sb) * d[j];
+        }
+      }
+    }
+    free(s);
+    free(d);
+  }
+  free(b);
+  return fail ? -2 : 0;
+}
+
+#define PROBLEM_ARGS                                                                       \
+  int64_t M, int64_t N, int64_t K, int transA, int transB, double alpha, const void* A,   \
+      int64_t lda, double scale_a, const void* B, int64_t ldb, double scale_b, double beta, \
+      const void* Cin, int64_t ldc, int a_type, int b_type, int c_type, unsigned epilogue,  \
+      const float* bias
+
+#define FILL_PROBLEM(p)                                                                     \
+  problem_t p = {M, N, K, transA, transB, alpha, scale_a, scale_b, beta,                    \
+                 (const uint8_t*)A, (const uint8_t*)B, (const uint8_t*)Cin, lda, ldb, ldc,  \
+                 a_type, b_type, c_type, epilogue, bias}
+
+/* Full M x N result: Cref and D are caller-owned M*N double arrays.  Returns 0 on success. */
+int oracle_gemm(PROBLEM_ARGS, double* Cref, double* D) {
+  FILL_PROBLEM(p);
+  return run_rows(&p, 0, M, Cref, D);
+}
+
+/* Rows [row0, row0+nrows): a bounded slice of the full result (used to time the oracle). */
+int oracle_gemm_rows(PROBLEM_ARGS, int64_t row0, int64_t nrows, double* Cref, double* D) {
+  FILL_PROBLEM(p);
+  return run_rows(&p, row0, nrows, Cref, D);
+}
+
+/* Selected entries (rows[t], cols[t]), t < npts, each computed on its own with k ascending. */
+int oracle_gemm_points(PROBLEM_ARGS, int64_t npts, const int64_t* rows, const int64_t* cols,
+                       double* Cref, double* D) {
+  FILL_PROBLEM(p);
+  if (check(&p)) return -1;
+  for (int64_t t = 0; t < npts; ++t)
+    if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N) return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < npts; ++t) {
+    const int64_t i = rows[t], j = cols[t];
+    double s = 0.0, d = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double a = dec_one(p.at, p.A, transA ? k * lda + i : i * lda + k);
+      const double b = dec_one(p.bt, p.B, transB ? j * ldb + k : k * ldb + j);
+      const double prod = a * b;
+      s += prod;
+      d += fabs(prod);
+    }
+    Cref[t] = apply_epilogue(&p, i, j, s);
+    D[t] = (p.sa * p.sb) * d;
+  }
+  return 0;
+}
+
+/* Number of OpenMP threads a parallel region of the oracle uses. */
+int oracle_num_threads(void) {
+  int n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    n = omp_get_num_threads();
+  }
+  return n;
+}

@@ -1,0 +1,262 @@
+"""Seeded synthetic inputs for the tiled GEMM  C = alpha * op(A) * op(B) + beta * C.
+
+This module only draws random matrices and turns float64 draws into the exact bytes that a
+GEMM call consumes: fp32, fp16 or bf16 words, or OCP fp8-E4M3 bytes plus one fp32 scale per
+tensor.  It holds none of the GEMM arithmetic.  Both the HIP library and the CPU oracle receive
+the very same bytes from here, so input quantisation error cancels when the two are compared
+(the checksum gate of "Rigel" (arXiv 2606.12765), section 3: the float64 reference is built from
+the exact quantised bytes the GPU consumes).
+
+Workloads (all square sizes come from the pages' square benchmarks; the distributions and seeds
+are fixed here):
+  * fp32 256^3, alpha=1, beta=0, A,B ~ U[-1,1], seed 0.
+  * fp32 1000^3, alpha=1.5, beta=-0.5, A,B,C_in ~ U[-1,1], seed 1; also with A stored K x M.
+  * fp16 n^3 for n in {512,1024,2048,4096}, A,B ~ N(0, 0.5^2), seed 2, fp16 output.
+  * bf16 n^3 + bias + erf-GELU, A ~ N(0,1), B ~ N(0,1/K), bias ~ N(0, 0.1^2) fp32, seed 3.
+  * fp8-E4M3 4096^3 with per-tensor scales (max|x| -> 448) and its bf16 twin, A,B ~ N(0,1),
+    seed 4, bf16 output.
+Draw order is always: logical A (M x K, row-major), then logical B (K x N), then C_in (M x N),
+then bias (N).  A transposed operand is the same logical matrix stored as its transpose.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import json
+from typing import Optional
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16", "e4m3")
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
+ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
+STORAGE = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8}
+
+EPI_NONE = 0
+EPI_BIAS = 1
+EPI_GELU = 2
+
+# Output type for each supported input type.
+OUT_TYPE = {"f32": "f32", "f16": "f16", "bf16": "bf16", "e4m3": "bf16"}
+
+
+# --------------------------------------------------------------------------------------------
+# Encoders: float64 draws -> storage bytes (round to nearest, ties to even).
+# --------------------------------------------------------------------------------------------
+
+def to_f32(x: np.ndarray) -> np.ndarray:
+    """float64 -> IEEE binary32, round to nearest even (numpy's cast)."""
+    return np.ascontiguousarray(x, dtype=np.float64).astype(np.float32)
+
+
+def to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """float64 -> IEEE binary16 bit patterns, round to nearest even (numpy's cast)."""
+    return np.ascontiguousarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float64 -> fp32 (RNE) -> bfloat16 bit patterns (RNE on the low 16 bits)."""
+    f = np.ascontiguousarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(f)
+    if nan.any():
+        out[nan] = ((f.view(np.uint32)[nan] >> 16) | 0x0040).astype(np.uint16)
+    return out
+
+
+def _e4m3_magnitudes() -> np.ndarray:
+    """Magnitudes of the 127 finite non-negative OCP E4M3 codes 0x00..0x7E, increasing."""
+    vals = np.empty(127, dtype=np.float64)
+    for code in range(127):
+        e, m = code >> 3, code & 7
+        vals[code] = m * 2.0 ** -9 if e == 0 else (8 + m) * 2.0 ** (e - 10)
+    return vals
+
+
+_E4M3_MAG = _e4m3_magnitudes()
+E4M3_MAX = 448.0
+
+
+def to_e4m3_bits(y: np.ndarray) -> np.ndarray:
+    """float64 -> OCP E4M3 bytes: nearest code, ties to the even code, saturating at +-448.
+
+    NaN maps to 0x7F.  Values beyond +-448 saturate instead of producing NaN, so that a tensor
+    scaled to max|x| = 448 never rounds its maximum into the NaN code.
+    """
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    mag = np.minimum(np.abs(y), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_E4M3_MAG, mag, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_hi = _E4M3_MAG[hi] - mag
+    d_lo = mag - _E4M3_MAG[lo]
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & ((lo & 1) == 0))
+    code = np.where(pick_lo, lo, hi).astype(np.uint8)
+    code |= (np.signbit(y).astype(np.uint8) << 7)
+    code[np.isnan(y)] = 0x7F
+    return code
+
+
+def e4m3_scale(x: np.ndarray) -> np.float32:
+    """Per-tensor dequantisation scale: fp32(max|x| / 448), or 1 for an all-zero tensor."""
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    return np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+
+
+def encode(x: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
+    """Encode float64 values to the storage of `dtype` (E4M3 encodes x / scale)."""
+    if dtype == "f32":
+        return to_f32(x)
+    if dtype == "f16":
+        return to_f16_bits(x)
+    if dtype == "bf16":
+        return to_bf16_bits(x)
+    if dtype == "e4m3":
+        return to_e4m3_bits(np.asarray(x, dtype=np.float64) / float(scale))
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# --------------------------------------------------------------------------------------------
+# Problems
+# --------------------------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Problem:
+    """One GEMM call's inputs, as storage bytes, plus the call's scalars.
+
+    A is stored M x K (row-major, lda = K) or, with trans_a, K x M (lda = M); B is stored K x N
+    (ldb = N) or, with trans_b, N x K (ldb = K).  C holds C_in in the output type (all zero
+    when beta == 0) and is M x N with ldc = N.
+    """
+    name: str
+    M: int
+    N: int
+    K: int
+    trans_a: bool
+    trans_b: bool
+    alpha: float
+    beta: float
+    a_type: str
+    b_type: str
+    c_type: str
+    epilogue: int
+    A: np.ndarray
+    B: np.ndarray
+    C: np.ndarray
+    bias: Optional[np.ndarray]
+    scale_a: float = 1.0
+    scale_b: float = 1.0
+    recipe: dict = dataclasses.field(default_factory=dict)
+
+    @property
+    def lda(self) -> int:
+        return self.M if self.trans_a else self.K
+
+    @property
+    def ldb(self) -> int:
+        return self.K if self.trans_b else self.N
+
+    @property
+    def ldc(self) -> int:
+        return self.N
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.M * self.N * self.K
+
+    def recipe_hash(self) -> str:
+        blob = json.dumps(self.recipe, sort_keys=True).encode()
+        return hashlib.sha256(blob).hexdigest()[:16]
+
+
+def _draw(rng: np.random.Generator, shape, dist) -> np.ndarray:
+    kind, p = dist
+    if kind == "uniform":
+        lo, hi = p
+        return rng.uniform(lo, hi, size=shape)
+    if kind == "normal":
+        return rng.normal(0.0, p, size=shape)
+    if kind == "int":
+        lo, hi = p
+        return rng.integers(lo, hi + 1, size=shape).astype(np.float64)
+    raise ValueError(kind)
+
+
+def make_problem(M: int, N: int, K: int, *, a_type: str = "f32", c_type: Optional[str] = None,
+                 trans_a: bool = False, trans_b: bool = False, alpha: float = 1.0,
+                 beta: float = 0.0, epilogue: int = EPI_NONE, seed: int = 0,
+                 dist_a=("uniform", (-1.0, 1.0)), dist_b=("uniform", (-1.0, 1.0)),
+                 dist_c=("uniform", (-1.0, 1.0)), bias_std: float = 0.1,
+                 fp8_scaled: bool = True, name: str = "") -> Problem:
+    """Draw a seeded problem.  `dist_*` is ("uniform", (lo, hi)), ("normal", std) or
+    ("int", (lo, hi)).  For E4M3 inputs each operand gets its own per-tensor scale when
+    `fp8_scaled`, else scale 1 (the draws must then already be E4M3 values)."""
+    c_type = c_type or OUT_TYPE[a_type]
+    rng = np.random.default_rng(seed)
+    a = _draw(rng, (M, K), dist_a)
+    b = _draw(rng, (K, N), dist_b)
+    c_in = _draw(rng, (M, N), dist_c) if beta != 0.0 else None
+    bias = (rng.normal(0.0, bias_std, size=N).astype(np.float32)
+            if epilogue & EPI_BIAS else None)
+    sa = sb = np.float32(1.0)
+    if a_type == "e4m3" and fp8_scaled:
+        sa, sb = e4m3_scale(a), e4m3_scale(b)
+    a_st = np.ascontiguousarray(a.T if trans_a else a)
+    b_st = np.ascontiguousarray(b.T if trans_b else b)
+    A = encode(a_st, a_type, float(sa))
+    B = encode(b_st, a_type, float(sb))
+    C = (encode(c_in, c_type) if c_in is not None
+         else np.zeros((M, N), dtype=STORAGE[c_type]))
+    recipe = dict(name=name, M=M, N=N, K=K, a_type=a_type, c_type=c_type, trans_a=trans_a,
+                  trans_b=trans_b, alpha=alpha, beta=beta, epilogue=epilogue, seed=seed,
+                  dist_a=list(map(str, dist_a)), dist_b=list(map(str, dist_b)),
+                  dist_c=list(map(str, dist_c)), bias_std=bias_std, fp8_scaled=fp8_scaled,
+                  rng="numpy.default_rng(PCG64)", order="A,B,C_in,bias")
+    return Problem(name=name or f"{a_type}_{M}x{N}x{K}", M=M, N=N, K=K, trans_a=trans_a,
+                   trans_b=trans_b, alpha=float(alpha), beta=float(beta), a_type=a_type,
+                   b_type=a_type, c_type=c_type, epilogue=epilogue, A=A, B=B, C=C, bias=bias,
+                   scale_a=float(sa), scale_b=float(sb), recipe=recipe)
+
+
+# The named workloads.
+
+def fp32_256() -> Problem:
+    """fp32 C = A*B, 256^3, row-major, alpha=1, beta=0, U[-1,1], seed 0."""
+    return make_problem(256, 256, 256, a_type="f32", seed=0, name="fp32_256")
+
+
+def fp32_1000_ragged(trans_a: bool = False) -> Problem:
+    """fp32 C = 1.5*A*B - 0.5*C, 1000^3 (ragged against every tile), U[-1,1], seed 1."""
+    return make_problem(1000, 1000, 1000, a_type="f32", trans_a=trans_a, alpha=1.5, beta=-0.5,
+                        seed=1, name="fp32_1000_" + ("tn" if trans_a else "nn"))
+
+
+def fp16_square(n: int) -> Problem:
+    """fp16 C = A*B, n^3, A,B ~ N(0, 0.5^2) rounded to fp16, fp16 output, seed 2."""
+    return make_problem(n, n, n, a_type="f16", seed=2, dist_a=("normal", 0.5),
+                        dist_b=("normal", 0.5), name=f"fp16_{n}")
+
+
+def bf16_bias_gelu(n: int, epilogue: int = EPI_BIAS | EPI_GELU) -> Problem:
+    """bf16 C = GELU(A*B + bias), n^3, A ~ N(0,1), B ~ N(0,1/K), bias ~ N(0,0.1^2), seed 3.
+
+    The bias is drawn for every epilogue value, so the unfused run (epilogue 0 in the GEMM,
+    then a separate bias+GELU pass) sees the same bias as the fused run."""
+    p = make_problem(n, n, n, a_type="bf16", seed=3, dist_a=("normal", 1.0),
+                     dist_b=("normal", 1.0 / np.sqrt(n)), epilogue=EPI_BIAS | EPI_GELU,
+                     name=f"bf16_bias_gelu_{n}")
+    p.epilogue = epilogue
+    return p
+
+
+def fp8_4096(n: int = 4096) -> Problem:
+    """fp8-E4M3 C = (sa*sb)*A*B, n^3, A,B ~ N(0,1), per-tensor scale max|x| -> 448, bf16 out."""
+    return make_problem(n, n, n, a_type="e4m3", c_type="bf16", seed=4, dist_a=("normal", 1.0),
+                        dist_b=("normal", 1.0), name=f"fp8_{n}")
+
+
+def bf16_twin_of_fp8(n: int = 4096) -> Problem:
+    """The same float64 draws as fp8_4096, rounded to bf16 instead, bf16 out, no epilogue."""
+    return make_problem(n, n, n, a_type="bf16", c_type="bf16", seed=4, dist_a=("normal", 1.0),
+                        dist_b=("normal", 1.0), name=f"bf16_{n}")

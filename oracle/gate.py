@@ -1,15 +1,22 @@
 """The parity gate between a GEMM result and the oracle (test infrastructure only).
 
 Normalised error per output entry:
-    err(i,j) = |C(i,j) - Cref(i,j)| / (D(i,j) + |beta * C_in(i,j)|)
+    err(i,j) = |C(i,j) - Cref(i,j)| / max(D(i,j) + |beta * C_in(i,j)|, |Cref(i,j)|)
 with D = sum_k |a(i,k) b(k,j)| over the dequantised inputs.  A result passes when
-    max err <= K * 2^-23 + u_out,
+    |C - Cref| <= tol * denominator + eta_out,   tol = K * 2^-23 + u_out + e_epi,
 u_out being the unit roundoff of the output format (2^-24 fp32, 2^-11 fp16, 2^-8 bf16; the
 fp8 path writes bf16).  K * 2^-23 is twice the first-order bound K*u_fp32 of any fp32
-accumulation order; u_out covers the single final rounding.  The test is written as
-`not (err <= tol)` so that NaN or Inf fails.  Where the denominator is zero (an all-zero row of
-op(A) or column of op(B) with beta = 0) the entry must instead satisfy
-|C - Cref| <= u_out * |Cref|.
+accumulation order; u_out covers the single final rounding.  Three terms extend the bare
+formula K * 2^-23 + u_out over D + |beta C_in| where it cannot hold:
+  * max(.., |Cref|): the final rounding is relative to the value rounded, which a bias can make
+    far larger than D (e.g. K = 1 with a tiny product);
+  * e_epi: the epilogue runs in fp32 (alpha*acc, beta*C, + bias: up to 4 roundings; GELU adds
+    the device erfc and its products), which matters only for fp32 output at tiny K;
+  * eta_out: half the smallest subnormal of the output format, the absolute error of rounding
+    into the subnormal range.
+On the named workloads (bias ~ N(0, 0.1^2) against D ~ sqrt(K)) the denominator is exactly
+D + |beta C_in| and e_epi, eta_out are below 1e-6 of tol, so the gate is the bare formula there.
+The test is written as `not (err <= tol)` so that NaN or Inf fails.
 
 "Rigel" (arXiv 2606.12765), section 3, names a per-dtype tolerance against a float64 reference
 built from the same quantised bytes but prints no values; the bound above is the one this
@@ -22,18 +29,23 @@ import dataclasses
 import numpy as np
 
 UNIT_ROUNDOFF = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+# half the smallest positive subnormal of each output format
+UNDERFLOW = {"f32": 2.0 ** -150, "f16": 2.0 ** -25, "bf16": 2.0 ** -134}
+EPI_FP32 = 4 * 2.0 ** -24          # alpha*acc, beta*C, + bias, in fp32
+EPI_GELU_FP32 = 16 * 2.0 ** -24    # device erfc (a few ulp) and the products around it
 # max over x of d/dx [x Phi(x)] = Phi(sqrt 2) + sqrt 2 phi(sqrt 2)
 GELU_MAX_SLOPE = 1.1289
 
 
-def tolerance(K: int, c_type: str, roundings: int = 1) -> float:
-    """K * 2^-23 + u_out.  With `roundings` = 2 (an unfused GEMM that rounds to the output type
-    and then a separate bias+GELU pass that rounds again) the first rounding passes through
-    GELU (slope <= 1.129) before the second: K * 2^-23 + (1 + 1.129) * u_out."""
+def tolerance(K: int, c_type: str, roundings: int = 1, gelu: bool = True) -> float:
+    """K * 2^-23 + u_out + e_epi.  With `roundings` = 2 (an unfused GEMM that rounds to the
+    output type and then a separate bias+GELU pass that rounds again) the first rounding passes
+    through GELU (slope <= 1.129) before the second: K * 2^-23 + (1 + 1.129) * u_out + e_epi."""
     u = UNIT_ROUNDOFF[c_type]
+    e_epi = EPI_FP32 + (EPI_GELU_FP32 if gelu else 0.0)
     if roundings == 1:
-        return K * 2.0 ** -23 + u
-    return K * 2.0 ** -23 + (1.0 + GELU_MAX_SLOPE) * u
+        return K * 2.0 ** -23 + u + e_epi
+    return K * 2.0 ** -23 + (1.0 + GELU_MAX_SLOPE) * u + e_epi
 
 
 @dataclasses.dataclass
@@ -55,16 +67,19 @@ def check(C: np.ndarray, Cref: np.ndarray, D: np.ndarray, tol: float, c_type: st
           beta: float = 0.0, Cin: np.ndarray | None = None) -> GateResult:
     """Apply the gate to decoded results C (float64) against the oracle's Cref and D."""
     C = np.asarray(C, dtype=np.float64)
+    Cref = np.asarray(Cref, dtype=np.float64)
     denom = np.asarray(D, dtype=np.float64).copy()
     if beta != 0.0 and Cin is not None:
         denom = denom + np.abs(beta * np.asarray(Cin, dtype=np.float64))
+    denom = np.maximum(denom, np.abs(Cref))
     diff = np.abs(C - Cref)
+    # subtract the absolute underflow allowance, then normalise
+    excess = np.maximum(diff - UNDERFLOW[c_type], 0.0)
     zero = denom == 0.0
     with np.errstate(divide="ignore", invalid="ignore"):
-        err = np.where(zero, 0.0, diff / np.where(zero, 1.0, denom))
+        err = np.where(zero, np.where(excess > 0, np.inf, 0.0),
+                       excess / np.where(zero, 1.0, denom))
     err = np.where(np.isfinite(C), err, np.inf)
-    zero_bad = zero & ~(diff <= UNIT_ROUNDOFF[c_type] * np.abs(Cref))
-    err = np.where(zero_bad, np.inf, err)
     if err.size == 0:
         return GateResult(True, 0.0, tol, 0.0, (), 0)
     idx = int(np.argmax(np.where(np.isnan(err), np.inf, err)))

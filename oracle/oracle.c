@@ -17,7 +17,7 @@
  *   S(i,j) = sum_k a(i,k) b(k,j)                        double, k ascending
  *   D(i,j) = sa*sb * sum_k |a(i,k) b(k,j)|             double (denominator of the gate)
  *   t      = alpha*(sa*sb)*S + (beta != 0 ? beta*C_in(i,j) : 0) + (BIAS ? bias[j] : 0)
- *   Cref   = GELU ? 0.5*t*(1 + erf(t/sqrt(2))) : t      double, libm erf
+ *   Cref   = GELU ? 0.5*t*erfc(-t/sqrt(2)) : t          double, libm erfc
  *
  * Every product of two decoded inputs is exact in double (at most 24+24 significant bits), so
  * the only roundings are the k-ordered sums and the epilogue, each at 2^-53.
@@ -95,8 +95,10 @@ int oracle_decode(int t, const void* src, int64_t n, double* dst) {
   return 0;
 }
 
-/* GELU with the Gauss error function: x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)). */
-double oracle_gelu(double t) { return 0.5 * t * (1.0 + erf(t / sqrt(2.0))); }
+/* GELU with the Gauss error function: x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), evaluated as
+ * 0.5 x erfc(-x / sqrt 2) (the same function; erfc avoids the cancellation of 1 + erf for
+ * negative x). */
+double oracle_gelu(double t) { return 0.5 * t * erfc(-t / sqrt(2.0)); }
 
 typedef struct {
   int64_t M, N, K;

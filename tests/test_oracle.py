@@ -329,7 +329,21 @@ def test_gate_rejects_nan_and_planted_errors():
     bad = Cref.copy()
     bad[1, 1] = 1e-30          # zero denominator: only an exact zero passes
     assert not gate.check(bad, Cref, D, tol, "bf16").ok
-    assert gate.tolerance(1000, "f32") == pytest.approx(1000 * 2 ** -23 + 2 ** -24)
+    assert gate.tolerance(1000, "f32", gelu=False) == pytest.approx(1000 * 2 ** -23 + 5 * 2 ** -24)
+    # bias-dominated entry (tiny D): the final rounding is judged against |Cref|
+    Cref = np.array([0.1])
+    D = np.array([1e-6])
+    one_rounding = np.array([np.float32(0.1)], dtype=np.float64)
+    assert gate.check(one_rounding, Cref, D, gate.tolerance(1, "f32", gelu=False), "f32").ok
+    assert not gate.check(Cref * (1 + 2 ** -18), Cref, D, gate.tolerance(1, "f32", gelu=False),
+                          "f32").ok
+    # rounding into the subnormal range: within half a subnormal step passes, more fails
+    Cref = np.array([3e-7])
+    D = np.array([3e-7])
+    sub = 2.0 ** -24
+    assert gate.check(np.array([round(3e-7 / sub) * sub]), Cref, D, gate.tolerance(1, "f16"),
+                      "f16").ok
+    assert not gate.check(np.array([3e-7 + 2 * sub]), Cref, D, gate.tolerance(1, "f16"), "f16").ok
 
 
 def test_oracle_detects_planted_sign_error():

@@ -1,0 +1,348 @@
+#!/usr/bin/env python3
+"""Benchmark of the tiled GEMM on one MI355X.
+
+Headline: bf16 GEMM + bias + erf-GELU, fused into the GEMM epilogue, M = N = K = 4096
+(A ~ N(0,1), B ~ N(0,1/K), bias ~ N(0,0.1^2), seed 3).  One step = one fused GEMM call over
+that problem with every input already resident in HBM.  Throughput is 2*M*N*K per step
+(epilogue FLOPs are not counted).  Then the sweeps: fp32 256^3 and 1000^3 (NN and TN),
+fp16 n^3, bf16 fused versus unfused n^3 for n in {512, 1024, 2048, 4096}, and fp8-E4M3 versus
+bf16 at 4096^3.  Each cell: warm up for >= 200 ms, then R timed reps with one HIP event pair
+per rep on the stream the kernel runs on; median and a percentile-bootstrap 95% CI
+(10^4 resamples, seed 0), as "Rigel" (arXiv 2606.12765), section 3 reports its cells.
+
+Prints ONE JSON line.  Only --gpus 1 is supported: this build runs on a single GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s & % MFMA peak: bf16 GEMM+bias+GELU 4096³; fp32/fp16/fp8 sweeps"
+# MI355X published dense peaks (256 CUs at 2.4 GHz).
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2}
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_bf16_bias_gelu_4096.txt")
+
+
+def source_hash() -> str:
+    """Hash of the library sources: ties a stored counter measurement to the kernel it saw."""
+    h = hashlib.sha256()
+    for d in ("tiled_matrix_multiply_amd/csrc", "include"):
+        base = os.path.join(ROOT, d)
+        for f in sorted(os.listdir(base)):
+            with open(os.path.join(base, f), "rb") as fh:
+                h.update(f.encode())
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def bootstrap_ci(x: np.ndarray, n_boot: int = 10000, seed: int = 0):
+    """Percentile bootstrap 95% CI of the median."""
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, len(x), size=(n_boot, len(x)))
+    meds = np.median(x[idx], axis=1)
+    return float(np.percentile(meds, 2.5)), float(np.percentile(meds, 97.5))
+
+
+class Cell:
+    """Device-resident operands of one workload and the call that runs it."""
+
+    def __init__(self, g, p, unfused: bool = False):
+        import torch
+        import tiled_matrix_multiply_amd as tmm
+
+        def dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to("cuda:0")
+
+        self.p = p
+        self.unfused = unfused
+        self.A, self.B, self.C = dev(p.A), dev(p.B), dev(p.C)
+        self.bias = dev(p.bias) if p.bias is not None else None
+        self.stream = torch.cuda.current_stream()
+        s = self.stream.cuda_stream
+        h = g.handle
+        epi = 0 if unfused else p.epilogue
+        dt = tmm.DTYPE
+        args = (p.M, p.N, p.K, int(p.trans_a), int(p.trans_b), float(p.alpha), self.A.data_ptr(),
+                p.lda, float(p.scale_a), self.B.data_ptr(), p.ldb, float(p.scale_b),
+                float(p.beta), self.C.data_ptr(), p.ldc, dt[p.a_type], dt[p.b_type],
+                dt[p.c_type], epi, self.bias.data_ptr() if self.bias is not None else None)
+        self.kernel = tmm.KERNEL_NAME[tmm.gemm_select_kernel(
+            h, p.M, p.N, p.K, int(p.trans_a), int(p.trans_b), self.A.data_ptr(), p.lda,
+            self.B.data_ptr(), p.ldb, self.C.data_ptr(), p.ldc, dt[p.a_type], dt[p.b_type],
+            dt[p.c_type], epi, args[-1])]
+        run = tmm.library().gemm_run
+        bias_gelu = tmm.library().gemm_bias_gelu
+        post = (h, s, p.M, p.N, self.C.data_ptr(), p.ldc, dt[p.c_type], args[-1], p.epilogue)
+
+        def step():
+            st = run(h, s, *args)
+            if st != 0:
+                raise RuntimeError(f"gemm_run: {tmm.gemm_status_string(st)}")
+            if unfused:
+                st = bias_gelu(*post)
+                if st != 0:
+                    raise RuntimeError(f"gemm_bias_gelu: {tmm.gemm_status_string(st)}")
+        self.step = step
+
+    def time(self, reps: int, warmup_s: float = 0.2, warmup_min: int = 3):
+        """Per-rep durations (ms) from HIP event pairs on the kernel's stream."""
+        import torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n = 0
+        while n < warmup_min or time.perf_counter() - t0 < warmup_s:
+            self.step()
+            n += 1
+            if n % 16 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for s, e in ev:
+            s.record(self.stream)
+            self.step()
+            e.record(self.stream)
+        torch.cuda.synchronize()
+        return np.array([s.elapsed_time(e) for s, e in ev], dtype=np.float64)
+
+    def algorithmic_bytes(self) -> int:
+        p = self.p
+        import workloads as W
+        es, cs = W.ESIZE[p.a_type], W.ESIZE[p.c_type]
+        b = p.M * p.K * es + p.K * p.N * es + p.M * p.N * cs
+        if p.beta != 0:
+            b += p.M * p.N * cs
+        if p.bias is not None:
+            b += 4 * p.N
+        if self.unfused:
+            b += 2 * p.M * p.N * cs   # the second pass reads and writes C again
+        return b
+
+
+def summarize(name, cell: Cell, ms: np.ndarray, dtype: str) -> dict:
+    p = cell.p
+    med = float(np.median(ms))
+    lo, hi = bootstrap_ci(ms)
+    tf = p.flops / (med * 1e-3) / 1e12
+    row = {"cell": name, "kernel": cell.kernel, "M": p.M, "N": p.N, "K": p.K, "dtype": dtype,
+           "reps": int(len(ms)), "median_us": round(med * 1e3, 3),
+           "ci95_us": [round(hi_ * 1e3, 3) for hi_ in (lo, hi)],
+           "tflops": round(tf, 2),
+           "tflops_ci95": [round(p.flops / (hi * 1e-3) / 1e12, 2),
+                           round(p.flops / (lo * 1e-3) / 1e12, 2)],
+           "pct_peak": round(100 * tf / PEAK_TFLOPS[dtype], 2),
+           "gbs": round(cell.algorithmic_bytes() / (med * 1e-3) / 1e9, 1)}
+    print(f"[bench] {name:34s} {cell.kernel:8s} {row['median_us']:10.2f} us  "
+          f"{row['tflops']:8.1f} TFLOP/s  {row['pct_peak']:5.1f}% of {dtype} peak  "
+          f"{row['gbs']:8.1f} GB/s", file=sys.stderr, flush=True)
+    return row
+
+
+def read_traffic(src_hash: str):
+    """HBM bytes per launch from the committed counter summary, if it saw this source."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if "=" in line and not line.startswith("#"):
+                    k, v = line.split("=", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("source_hash") != src_hash:
+            return None
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(p, target_s: float) -> dict:
+    """The oracle, as it stands, on a bounded sample of the headline problem: the first rows
+    of the M x N result (all N columns, full K), timed with a monotonic clock."""
+    import oracle
+    oracle.lib()
+    t0 = time.perf_counter()
+    oracle.gemm_rows(p, 0, 8)
+    t_probe = time.perf_counter() - t0
+    rows = int(max(8, min(p.M, 8 * target_s / max(t_probe, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.gemm_rows(p, 0, rows)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * p.N * p.K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the {p.M}x{p.N}x{p.K} bf16+bias+GELU problem "
+                      f"(all {p.N} columns, K={p.K}, float64, plus the |a*b| denominator sums), "
+                      f"{dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+def provenance(src_hash: str) -> dict:
+    import torch
+    prop = torch.cuda.get_device_properties(0)
+    try:
+        hipcc = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True,
+                               text=True, timeout=30).stdout.splitlines()[0]
+    except Exception:
+        hipcc = "unknown"
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        commit = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT,
+                                capture_output=True, text=True, timeout=10).stdout.strip()
+    except Exception:
+        commit = ""
+    return {"gpu": prop.name, "gcn_arch": getattr(prop, "gcnArchName", ""),
+            "cus": prop.multi_processor_count, "hip": torch.version.hip, "hipcc": hipcc,
+            "torch": torch.__version__, "host_cpu": cpu,
+            "host_cores": len(os.sched_getaffinity(0)), "source_hash": src_hash,
+            "git_commit": commit or None, "python": platform.python_version()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300, help="timed steps (headline)")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed warmup steps (headline)")
+    ap.add_argument("--reps", type=int, default=300, help="timed reps per sweep cell")
+    ap.add_argument("--no-sweeps", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--headline-only-loop", type=int, default=0,
+                    help="run only N headline steps (for profiler passes) and exit")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: --gpus {args.gpus} (WORLD_SIZE={world}) requested, but this build is a "
+              f"single-GPU GEMM: there is no sharded path and no collective. Run --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_matrix_multiply_amd as tmm
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    g = tmm.Gemm(0)
+    src_hash = source_hash()
+
+    head_p = W.bf16_bias_gelu(4096)
+    head = Cell(g, head_p)
+    print(f"[bench] headline: bf16 GEMM+bias+GELU 4096^3 fused, kernel {head.kernel}",
+          file=sys.stderr, flush=True)
+
+    if args.headline_only_loop:
+        for _ in range(args.headline_only_loop):
+            head.step()
+        torch.cuda.synchronize()
+        print(f"[bench] ran {args.headline_only_loop} headline steps", file=sys.stderr)
+        return
+
+    # Headline: W untimed steps, then exactly K steps between two synchronisations, each
+    # bracketed by an event pair on the launch stream.
+    for _ in range(args.warmup):
+        head.step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(head.stream)
+        head.step()
+        e.record(head.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([s.elapsed_time(e) for s, e in ev])
+    ms_per_step = wall * 1e3 / args.steps
+    value = head_p.flops / (ms_per_step * 1e-3) / 1e12
+    head_row = summarize("bf16+bias+GELU fused 4096 (headline)", head, ms, "bf16")
+    mean_ms = float(np.mean(ms))
+    achieved = head_p.flops / (mean_ms * 1e-3) / 1e12
+
+    sweeps = []
+    if not args.no_sweeps:
+        R = args.reps
+
+        def cell(name, p, dtype, unfused=False):
+            c = Cell(g, p, unfused)
+            sweeps.append(summarize(name, c, c.time(R), dtype))
+            del c
+            torch.cuda.empty_cache()
+
+        cell("fp32 256", W.fp32_256(), "f32")
+        cell("fp32 1000 a=1.5 b=-0.5 NN", W.fp32_1000_ragged(False), "f32")
+        cell("fp32 1000 a=1.5 b=-0.5 TN", W.fp32_1000_ragged(True), "f32")
+        for n in (512, 1024, 2048, 4096):
+            cell(f"fp16 {n}", W.fp16_square(n), "f16")
+        for n in (512, 1024, 2048, 4096):
+            p = W.bf16_bias_gelu(n)
+            cell(f"bf16+bias+GELU fused {n}", p, "bf16")
+            cell(f"bf16 GEMM then bias+GELU {n}", p, "bf16", unfused=True)
+        cell("fp8 e4m3 4096 (scaled, bf16 out)", W.fp8_4096(4096), "e4m3")
+        cell("bf16 4096 (fp8 twin)", W.bf16_twin_of_fp8(4096), "bf16")
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] timing the oracle on the host (bounded sample) ...", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(head_p, args.cpu_seconds)
+
+    traffic = read_traffic(src_hash)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy draws: A~N(0,1), B~N(0,1/K), bias~N(0,0.01); bf16 RNE)",
+        "config": {"workload": "bf16 GEMM + bias + erf-GELU fused, M=N=K=4096, row-major NN, "
+                               "fp32 accumulate, bf16 out",
+                   "M": 4096, "N": 4096, "K": 4096, "kernel": head.kernel},
+        "pct_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
+        "median_tflops": head_row["tflops"],
+        "ci95_tflops": head_row["tflops_ci95"],
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS["bf16"], 4), "traffic": traffic,
+                     "kernel_mean_us": round(mean_ms * 1e3, 3),
+                     "flops_per_launch": head_p.flops},
+        "cpu_baseline": cpu,
+        "sweeps": sweeps,
+        "provenance": provenance(src_hash),
+    }
+    print(json.dumps(out), flush=True)
+    g.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,157 @@
+/*
+ * gemm.h -- C ABI of the tiled GEMM library for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * One operation:
+ *
+ *     C = epi( alpha * scale_a * scale_b * op(A) * op(B)  +  beta * C  [+ bias] )
+ *
+ * with op(X) = X or X^T chosen by a flag, fp32 accumulation, and an epilogue that may add a
+ * per-column bias and apply the erf form of GELU, x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)).
+ *
+ * Where it comes from:
+ *   - the BLAS form alpha*AB + beta*C computed in one fused store: "Case Study: The Tiled GEMM"
+ *     (its epilogue paragraph);
+ *   - bias / activation / scaling applied to every accumulator in registers before a single
+ *     store, and transposition expressed purely through strides: "Case Study: Steel's
+ *     BlockMMA" (its store_result and stride-constant paragraphs);
+ *   - operands described by a base pointer plus explicit strides, with the output tile shape
+ *     chosen by the library: "Rigel" (arXiv 2606.12765), section 2 (tensor_handle,
+ *     matmul2d_descriptor);
+ *   - the fused GEMM + bias + GELU versus the decomposed path, and fp8 E4M3 operands:
+ *     "Rigel", abstract and section 1 (contribution 7).
+ *
+ * Conventions shared by every entry point:
+ *   - Storage is row-major.  Element (r, c) of a stored matrix X with leading dimension ldX is
+ *     X[r * ldX + c].  A is stored M x K (lda >= K) or, with transA, K x M (lda >= M); B is
+ *     stored K x N (ldb >= N) or, with transB, N x K (ldb >= K); C is M x N (ldc >= N).
+ *     Leading dimensions and sizes are counted in elements.
+ *   - Supported (A, B, C) type tuples: (F32,F32,F32), (F16,F16,F16), (BF16,BF16,BF16) and
+ *     (E4M3,E4M3,BF16).  E4M3 is the OCP 8-bit float (bias 7, max 448, no infinities).
+ *     Any other tuple returns GEMM_ERR_UNSUPPORTED.
+ *   - Pointers A, B, C and bias are DEVICE pointers owned by the caller.  C is read (only when
+ *     beta != 0) and written.  Nothing is allocated and nothing is retained after a call.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream).  They
+ *     enqueue kernels and return; results are visible after the stream synchronises.  Device
+ *     faults surface at the caller's next synchronisation, not as a return value.
+ *   - Invalid arguments return a negative status and enqueue nothing.
+ *   - A handle is immutable after gemm_create and may be shared by threads.
+ */
+#ifndef TILED_GEMM_H
+#define TILED_GEMM_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define GEMM_API __attribute__((visibility("default")))
+#else
+#define GEMM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gemm_status {
+  GEMM_OK = 0,
+  GEMM_ERR_INVALID_HANDLE = -1, /* null or destroyed handle */
+  GEMM_ERR_INVALID_VALUE = -2,  /* negative size, null pointer, leading dimension too small,
+                                   bias flag without bias, unknown epilogue bits, trans not 0/1 */
+  GEMM_ERR_UNSUPPORTED = -3,    /* type tuple not supported, size beyond 2^31-1, or a forced
+                                   kernel that cannot serve this layout/alignment */
+  GEMM_ERR_ALIAS = -4,          /* C's byte range overlaps A, B or bias */
+  GEMM_ERR_DEVICE = -5,         /* no such device, device is not gfx950, or a HIP error at
+                                   gemm_create */
+  GEMM_ERR_LAUNCH = -6,         /* the kernel launch itself failed (hipGetLastError) */
+  GEMM_ERR_NO_MEMORY = -7       /* host allocation of the handle failed */
+} gemm_status_t;
+
+typedef enum gemm_dtype {
+  GEMM_F32 = 0,
+  GEMM_F16 = 1,
+  GEMM_BF16 = 2,
+  GEMM_E4M3 = 3
+} gemm_dtype_t;
+
+/* Epilogue bits.  BIAS adds bias[j] (fp32, length N, one value per output column, broadcast
+ * over rows, not scaled by alpha).  GELU applies x * Phi(x) after everything else.  Order:
+ * GELU(alpha*sa*sb*acc + beta*C + bias), rounded once to C's type (round to nearest even). */
+#define GEMM_EPI_NONE 0u
+#define GEMM_EPI_BIAS 1u
+#define GEMM_EPI_GELU 2u
+
+/* Kernel families, for gemm_run_kernel.  AUTO picks by type, layout, alignment and size. */
+typedef enum gemm_kernel {
+  GEMM_KERNEL_AUTO = 0,
+  GEMM_KERNEL_SIMT = 1,     /* LDS-tiled scalar FMA, 16x16 tile, one output per thread: the
+                               plain tiled kernel without matrix cores ("X3: Metal GEMM",
+                               section 2, translated to HIP).  Any alignment. */
+  GEMM_KERNEL_MFMA_64 = 2,  /* matrix-core kernel, 64x64 workgroup tile, 4 wavefronts */
+  GEMM_KERNEL_MFMA_128 = 3, /* matrix-core kernel, 128x128 workgroup tile, 4 wavefronts */
+  GEMM_KERNEL_MFMA_256 = 4  /* matrix-core kernel, 256x256 workgroup tile, 8 wavefronts */
+} gemm_kernel_t;
+
+typedef struct gemm_handle* gemm_handle_t;
+
+/* Create a handle bound to HIP device `device`.  Checks that the device is a gfx950 and
+ * records its compute-unit count for tile selection.  *out receives the handle (NULL on
+ * failure).  Errors: GEMM_ERR_INVALID_VALUE (out == NULL), GEMM_ERR_DEVICE (no such device,
+ * not gfx950, HIP error), GEMM_ERR_NO_MEMORY. */
+GEMM_API gemm_status_t gemm_create(gemm_handle_t* out, int device);
+
+/* Destroy a handle.  NULL is accepted and ignored.  Work already enqueued is unaffected. */
+GEMM_API gemm_status_t gemm_destroy(gemm_handle_t h);
+
+/* Check the arguments of gemm_run without touching any device.  Returns the status gemm_run
+ * would return for them before launching (GEMM_OK when they are valid).  M == 0 or N == 0 is a
+ * valid no-op; K == 0 is valid and yields C = epi(beta * C [+ bias]).  When K == 0, A and B are
+ * not read and may be NULL. */
+GEMM_API gemm_status_t gemm_check_args(int64_t M, int64_t N, int64_t K, int transA, int transB,
+                              const void* A, int64_t lda, const void* B, int64_t ldb,
+                              const void* C, int64_t ldc, gemm_dtype_t a_type,
+                              gemm_dtype_t b_type, gemm_dtype_t c_type, uint32_t epilogue,
+                              const float* bias);
+
+/* C = epi(alpha * scale_a * scale_b * op(A) op(B) + beta * C [+ bias]) on `stream`.
+ * scale_a / scale_b are the per-tensor dequantisation scales of E4M3 operands (pass 1.0f for
+ * other types; they multiply the product for every type).  beta == 0 means C is not read, so
+ * NaN in C does not propagate.  The kernel is chosen automatically (GEMM_KERNEL_AUTO). */
+GEMM_API gemm_status_t gemm_run(gemm_handle_t h, void* stream, int64_t M, int64_t N, int64_t K,
+                       int transA, int transB, float alpha, const void* A, int64_t lda,
+                       float scale_a, const void* B, int64_t ldb, float scale_b, float beta,
+                       void* C, int64_t ldc, gemm_dtype_t a_type, gemm_dtype_t b_type,
+                       gemm_dtype_t c_type, uint32_t epilogue, const float* bias);
+
+/* gemm_run with an explicit kernel family.  Matrix-core kernels need 16-byte-aligned A, B and
+ * C, lda * sizeof(A elem) and ldb * sizeof(B elem) multiples of 16 bytes, and ldc a multiple of
+ * 4; otherwise they return GEMM_ERR_UNSUPPORTED (AUTO then uses GEMM_KERNEL_SIMT). */
+GEMM_API gemm_status_t gemm_run_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* stream, int64_t M,
+                              int64_t N, int64_t K, int transA, int transB, float alpha,
+                              const void* A, int64_t lda, float scale_a, const void* B,
+                              int64_t ldb, float scale_b, float beta, void* C, int64_t ldc,
+                              gemm_dtype_t a_type, gemm_dtype_t b_type, gemm_dtype_t c_type,
+                              uint32_t epilogue, const float* bias);
+
+/* The kernel family gemm_run would use for these arguments (a gemm_kernel_t value), or a
+ * negative status when the arguments are invalid.  Touches no device. */
+GEMM_API int gemm_select_kernel(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int transA,
+                       int transB, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       const void* C, int64_t ldc, gemm_dtype_t a_type, gemm_dtype_t b_type,
+                       gemm_dtype_t c_type, uint32_t epilogue, const float* bias);
+
+/* The decomposed second pass: C = epi(C [+ bias]) in place, elementwise, for an M x N matrix of
+ * type c_type (F32, F16 or BF16) with leading dimension ldc.  With epilogue = BIAS|GELU after a
+ * gemm_run with epilogue NONE this is the unfused form of the fused epilogue ("Rigel",
+ * abstract: the decomposed path).  Same error conventions as gemm_run; an unsupported c_type
+ * returns GEMM_ERR_UNSUPPORTED. */
+GEMM_API gemm_status_t gemm_bias_gelu(gemm_handle_t h, void* stream, int64_t M, int64_t N, void* C,
+                             int64_t ldc, gemm_dtype_t c_type, const float* bias,
+                             uint32_t epilogue);
+
+/* A static, human-readable name for a status code (never NULL). */
+GEMM_API const char* gemm_status_string(gemm_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILED_GEMM_H */

@@ -1,0 +1,149 @@
+"""C ABI checks that need no GPU: every declared symbol is exported, argument validation and
+status codes behave as include/gemm.h states, and the binding has no fallback path."""
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm.h")
+
+tmm = pytest.importorskip("tiled_matrix_multiply_amd")
+
+F32, F16, BF16, E4M3 = tmm.GEMM_F32, tmm.GEMM_F16, tmm.GEMM_BF16, tmm.GEMM_E4M3
+BIAS, GELU = tmm.GEMM_EPI_BIAS, tmm.GEMM_EPI_GELU
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"GEMM_API\s+[\w\s\*]*?\b(gemm_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    syms = declared_symbols()
+    assert len(syms) == 8, syms
+    assert sorted(tmm.EXPORTS) == syms
+    nm = subprocess.run(["nm", "-D", "--defined-only", tmm.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = {line.split()[-1] for line in nm.splitlines() if " T " in line}
+    for s in syms:
+        assert s in exported, s
+        assert hasattr(tmm.library(), s)
+    # nothing but the C ABI is exported
+    assert {s for s in exported if not s.startswith("gemm_")} == set(), exported
+
+
+def test_status_strings():
+    for code in range(0, -8, -1):
+        s = tmm.gemm_status_string(code)
+        assert s.startswith("GEMM_")
+    assert tmm.gemm_status_string(-99) == "GEMM_ERR_UNKNOWN"
+
+
+# Fake, well-separated device addresses: gemm_check_args never dereferences them.
+PA, PB, PC, PBIAS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def chk(M=64, N=48, K=32, ta=0, tb=0, A=PA, lda=None, B=PB, ldb=None, C=PC, ldc=None, at=F32,
+        bt=None, ct=None, epi=0, bias=None):
+    bt = at if bt is None else bt
+    ct = (BF16 if at == E4M3 else at) if ct is None else ct
+    lda = (M if ta else K) if lda is None else lda
+    ldb = (K if tb else N) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return tmm.gemm_check_args(M, N, K, ta, tb, A, lda, B, ldb, C, ldc, at, bt, ct, epi, bias)
+
+
+def test_valid_arguments():
+    assert chk() == tmm.GEMM_OK
+    for at in (F32, F16, BF16, E4M3):
+        for ta in (0, 1):
+            for tb in (0, 1):
+                assert chk(at=at, ta=ta, tb=tb, epi=BIAS | GELU, bias=PBIAS) == tmm.GEMM_OK
+
+
+def test_invalid_values():
+    V = tmm.GEMM_ERR_INVALID_VALUE
+    assert chk(M=-1) == V and chk(N=-1) == V and chk(K=-1) == V
+    assert chk(ta=2) == V and chk(tb=-1) == V
+    assert chk(epi=4) == V
+    assert chk(C=None) == V
+    assert chk(A=None) == V and chk(B=None) == V
+    assert chk(lda=31) == V                 # lda < K
+    assert chk(ta=1, lda=63) == V           # A stored K x M: lda < M
+    assert chk(ldb=47) == V                 # ldb < N
+    assert chk(tb=1, ldb=31) == V           # B stored N x K: ldb < K
+    assert chk(ldc=47) == V
+    assert chk(epi=BIAS, bias=None) == V
+
+
+def test_unsupported_tuples_and_sizes():
+    U = tmm.GEMM_ERR_UNSUPPORTED
+    assert chk(at=F32, ct=BF16) == U
+    assert chk(at=E4M3, ct=E4M3) == U
+    assert chk(at=E4M3, ct=F32) == U
+    assert chk(at=BF16, bt=F16, ct=BF16) == U
+    assert chk(at=7) == U
+    assert chk(M=2 ** 31, lda=None) == U
+
+
+def test_degenerate_sizes():
+    OK = tmm.GEMM_OK
+    assert chk(M=0, A=None, B=None, C=None) == OK          # no-op
+    assert chk(N=0, A=None, B=None, C=None) == OK
+    assert chk(K=0, A=None, B=None, lda=0, ldb=48) == OK   # C = epi(beta*C)
+    assert chk(K=0, A=None, B=None, C=None) == tmm.GEMM_ERR_INVALID_VALUE
+
+
+def test_aliasing():
+    AL = tmm.GEMM_ERR_ALIAS
+    assert chk(C=PA) == AL
+    assert chk(C=PB + 4 * 100) == AL
+    assert chk(C=PA + 4 * (64 * 32 - 1)) == AL              # overlaps A's last element
+    assert chk(C=PA + 4 * (64 * 32)) == tmm.GEMM_OK          # just past A
+    assert chk(epi=BIAS, bias=PC + 8) == AL
+
+
+def test_null_handle_rejected_without_device():
+    H = tmm.GEMM_ERR_INVALID_HANDLE
+    assert tmm.gemm_run(None, None, 4, 4, 4, 0, 0, 1.0, PA, 4, 1.0, PB, 4, 1.0, 0.0, PC, 4, F32,
+                        F32, F32, 0, None) == H
+    assert tmm.gemm_run_kernel(None, 0, None, 4, 4, 4, 0, 0, 1.0, PA, 4, 1.0, PB, 4, 1.0, 0.0, PC,
+                               4, F32, F32, F32, 0, None) == H
+    assert tmm.gemm_select_kernel(None, 4, 4, 4, 0, 0, PA, 4, PB, 4, PC, 4, F32, F32, F32, 0,
+                                  None) == H
+    assert tmm.gemm_bias_gelu(None, None, 4, 4, PC, 4, F32, PBIAS, BIAS) == H
+    tmm.gemm_destroy(None)
+
+
+def test_create_without_gpu_reports_device_error():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(tmm.GemmError) as e:
+        tmm.gemm_create(0)
+    assert e.value.status == tmm.GEMM_ERR_DEVICE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    """No CPU fallback: importing the binding without libgemm.so raises ImportError."""
+    pkg = tmp_path / "tiled_matrix_multiply_amd"
+    pkg.mkdir()
+    (pkg / "__init__.py").write_text(open(os.path.join(ROOT, "tiled_matrix_multiply_amd",
+                                                       "__init__.py")).read())
+    code = "import tiled_matrix_multiply_amd"
+    res = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True,
+                         text=True)
+    assert res.returncode != 0 and "ImportError" in res.stderr and "libgemm.so" in res.stderr
+
+
+def test_product_path_never_touches_oracle():
+    """Neither the library sources nor the binding import, load or name the oracle."""
+    pkg = os.path.join(ROOT, "tiled_matrix_multiply_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text, os.path.join(dirpath, f)

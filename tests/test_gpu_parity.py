@@ -1,0 +1,297 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the float64 oracle.
+
+Bars: bit-exact where the arithmetic is exact (integer-valued inputs, identity/permutation
+operands, the fp8 format probe); otherwise the normalised-error gate
+max |C - Cref| / (sum_k |a b| + |beta C_in|) <= K * 2^-23 + u_out, checked on every entry at sizes
+the oracle finishes in seconds and on sampled entries at the full 2048/4096 sizes.
+"""
+import itertools
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from oracle import gate
+
+import gemm_harness as H
+
+pytestmark = pytest.mark.gpu
+
+KERNELS = {"simt": 1, "mfma64": 2, "mfma128": 3, "mfma256": 4}
+
+
+@pytest.fixture(scope="module")
+def g():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tiled_matrix_multiply_amd as tmm
+    h = tmm.Gemm(0)
+    yield h
+    h.close()
+
+
+def _report(name, res):
+    print(f"[parity] {name}: {res}", flush=True)
+
+
+# ------------------------------------------------------------------ fp8 format probe --
+
+@pytest.mark.parametrize("kernel", ["mfma64", "mfma128", "mfma256", "simt"])
+def test_fp8_is_ocp_e4m3(g, kernel):
+    """Bytes whose meaning differs between OCP E4M3 and the older FNUZ variant:
+    0x7E = 448 (FNUZ: 224), 0x01 = 2^-9 (FNUZ: 2^-10), 0x80 = -0 (FNUZ: NaN)."""
+    M, N, K = 32, 32, 64
+    A = np.zeros((M, K), np.uint8)
+    A[0, 0], A[1, 0], A[2, 0], A[3, 1], A[4, 5] = 0x7E, 0x01, 0x80, 0x08, 0xFE
+    B = np.zeros((K, N), np.uint8)
+    B[0, :] = 0x38     # 1.0
+    B[1, :] = 0x40     # 2.0
+    B[5, :] = 0xB8     # -1.0
+    p = W.Problem("fp8_probe", M, N, K, False, False, 1.0, 0.0, "e4m3", "e4m3", "bf16", 0, A, B,
+                  np.zeros((M, N), np.uint16), None)
+    raw, got = H.run(g, p, KERNELS[kernel])
+    Cref, _ = oracle.gemm(p)
+    assert got[0, 0] == 448.0 and got[1, 0] == 2.0 ** -9 and got[3, 0] == 2.0 ** -5
+    assert got[4, 0] == 448.0 and not np.isnan(got).any()
+    assert np.array_equal(got, Cref)
+
+
+# ------------------------------------------------------------- bit-exact integer runs --
+
+def _rne(x: np.ndarray, c_type: str) -> np.ndarray:
+    """Round exact values to the output format (the single final rounding)."""
+    return W.encode(x, c_type)
+
+
+@pytest.mark.parametrize("dtype,kernel,ta,tb",
+                         list(itertools.product(["f32", "f16", "bf16", "e4m3"], KERNELS,
+                                                [False, True], [False, True])))
+def test_integer_inputs_bit_exact(g, dtype, kernel, ta, tb):
+    """Integer inputs in [-4, 4]: every partial sum is an integer below 2^24, so any fp32
+    accumulation order is exact and the result must equal the exact value rounded once."""
+    M, N, K = 200, 264, 300
+    seed = zlib.crc32(f"{dtype}/{kernel}/{ta}/{tb}".encode()) & 0xFFFF
+    with_epi = (seed % 2) == 0
+    p = W.make_problem(M, N, K, a_type=dtype, trans_a=ta, trans_b=tb, seed=seed,
+                       dist_a=("int", (-4, 4)), dist_b=("int", (-4, 4)), fp8_scaled=False,
+                       alpha=2.0 if with_epi else 1.0, beta=-1.0 if with_epi else 0.0,
+                       dist_c=("int", (-8, 8)), epilogue=W.EPI_BIAS if with_epi else 0)
+    if p.bias is not None:
+        p.bias = np.round(p.bias * 30).astype(np.float32)   # small integers
+    # leading dimensions padded to 16-byte multiples so that every kernel family accepts them
+    got, kname, pad_ok = H.run_padded(g, p, kernel=KERNELS[kernel])
+    Cref, _ = oracle.gemm(p)
+    expect = oracle.decode(p.c_type, _rne(Cref, p.c_type))
+    bad = np.argwhere(got != expect)
+    assert pad_ok
+    assert bad.size == 0, f"{bad.shape[0]} mismatches, first at {bad[0]}: got {got[tuple(bad[0])]} want {expect[tuple(bad[0])]}"
+
+
+def test_identity_and_permutation_bit_exact(g):
+    rng = np.random.default_rng(3)
+    n = 320
+    for dtype in ["f32", "bf16", "e4m3", "f16"]:
+        b = rng.standard_normal((n, n))
+        P = np.zeros((n, n))
+        P[np.arange(n), rng.permutation(n)] = 1.0
+        p = W.Problem("perm", n, n, n, False, False, 1.0, 0.0, dtype, dtype, W.OUT_TYPE[dtype],
+                      0, W.encode(P, dtype, 1.0), W.encode(b, dtype, 1.0),
+                      np.zeros((n, n), W.STORAGE[W.OUT_TYPE[dtype]]), None)
+        raw, got = H.run(g, p)
+        Cref, _ = oracle.gemm(p)
+        # C = P B selects rows of B exactly; bf16/fp16/f32 outputs hold B's values exactly
+        # except fp8 inputs, whose values bf16 also holds exactly.
+        assert np.array_equal(got, Cref), dtype
+
+
+# ------------------------------------------------------------------- named workloads --
+
+def test_fp32_256(g):
+    p = W.fp32_256()
+    _, got = H.run(g, p)
+    res = H.gate_full(p, got)
+    _report("fp32 256^3", res)
+    assert res.ok
+
+
+@pytest.mark.parametrize("trans_a", [False, True])
+def test_fp32_1000_ragged(g, trans_a):
+    p = W.fp32_1000_ragged(trans_a)
+    _, got = H.run(g, p)
+    res = H.gate_full(p, got)
+    _report(f"fp32 1000^3 alpha=1.5 beta=-0.5 {'TN' if trans_a else 'NN'}", res)
+    assert res.ok
+
+
+def test_fp32_1000_nn_vs_tn_report(g):
+    """Same logical A stored two ways; reported, not gated (accumulation order may differ)."""
+    _, nn = H.run(g, W.fp32_1000_ragged(False))
+    _, tn = H.run(g, W.fp32_1000_ragged(True))
+    print(f"[parity] fp32 1000 NN vs TN bitwise equal fraction: {np.mean(nn == tn):.4f}")
+
+
+@pytest.mark.parametrize("n", [512, 1024, 2048, 4096])
+def test_fp16_square(g, n):
+    p = W.fp16_square(n)
+    _, got = H.run(g, p)
+    res = H.gate_full(p, got) if n <= 1024 else H.gate_sampled(p, got)
+    _report(f"fp16 {n}^3", res)
+    assert res.ok
+
+
+@pytest.mark.parametrize("n", [512, 1024, 2048, 4096])
+def test_bf16_bias_gelu_fused(g, n):
+    p = W.bf16_bias_gelu(n)
+    _, got = H.run(g, p)
+    res = H.gate_full(p, got) if n <= 1024 else H.gate_sampled(p, got)
+    _report(f"bf16+bias+GELU fused {n}^3", res)
+    assert res.ok
+
+
+@pytest.mark.parametrize("n", [512, 1024, 2048, 4096])
+def test_bf16_bias_gelu_unfused(g, n):
+    """GEMM without epilogue, then the separate bias+GELU pass; two roundings to bf16."""
+    import torch
+    import tiled_matrix_multiply_amd as tmm
+    p = W.bf16_bias_gelu(n)
+    d = H.Device(p)
+    H.run(g, p, dev=d, epilogue=0)
+    g.bias_gelu(d.C, d.bias, M=p.M, N=p.N, c_type="bf16")
+    torch.cuda.synchronize()
+    got = oracle.decode("bf16", H.from_device(d.C, "bf16"))
+    res = (H.gate_full(p, got, roundings=2) if n <= 1024
+           else H.gate_sampled(p, got, roundings=2))
+    _report(f"bf16 GEMM then bias+GELU (unfused) {n}^3", res)
+    assert res.ok
+
+
+@pytest.mark.parametrize("n", [512, 4096])
+def test_fp8_e4m3(g, n):
+    p = W.fp8_4096(n)
+    _, got = H.run(g, p)
+    res = H.gate_full(p, got) if n <= 1024 else H.gate_sampled(p, got)
+    _report(f"fp8 E4M3 {n}^3 (sa={p.scale_a:.4g}, sb={p.scale_b:.4g})", res)
+    assert res.ok
+
+
+def test_bf16_twin_4096(g):
+    p = W.bf16_twin_of_fp8(4096)
+    _, got = H.run(g, p)
+    res = H.gate_sampled(p, got)
+    _report("bf16 4096^3 (fp8 twin)", res)
+    assert res.ok
+
+
+def test_kernel_selection(g):
+    ptrs = dict(A=1 << 40, B=2 << 40, C=3 << 40)   # aligned, disjoint; never dereferenced
+    assert g.select_kernel(4096, 4096, 4096, a_type="bf16", **ptrs) == "mfma256"
+    assert g.select_kernel(2048, 2048, 2048, a_type="bf16", **ptrs) == "mfma128"
+    assert g.select_kernel(1024, 1024, 1024, a_type="f16", **ptrs) == "mfma64"
+    assert g.select_kernel(1000, 1000, 1000, a_type="f32", **ptrs) == "mfma64"
+    assert g.select_kernel(1000, 1000, 1000, a_type="f32", A=(1 << 40) + 4, B=2 << 40,
+                           C=3 << 40) == "simt"
+
+
+# ------------------------------------------------------------------------ edge cases --
+
+SHAPES = [(1, 1, 1), (31, 33, 17), (64, 64, 64), (65, 63, 129), (257, 255, 1), (300, 8, 4097),
+          (1000, 777, 333), (130, 1030, 40)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "e4m3"])
+@pytest.mark.parametrize("kernel", ["auto", "simt", "mfma64", "mfma128", "mfma256"])
+def test_edge_shapes(g, dtype, kernel):
+    """Ragged shapes with leading dimensions padded to 16-byte multiples (padding poisoned
+    with NaN): every kernel family must mask its loads and stores at every edge."""
+    kid = 0 if kernel == "auto" else KERNELS[kernel]
+    for i, (M, N, K) in enumerate(SHAPES):
+        if kernel == "simt" and M * N * K > 5e7:
+            continue
+        ta, tb = bool(i & 1), bool(i & 2)
+        p = W.make_problem(M, N, K, a_type=dtype, trans_a=ta, trans_b=tb, alpha=0.75,
+                           beta=0.5 if i % 3 == 0 else 0.0, epilogue=(i % 4), seed=40 + i,
+                           dist_a=("normal", 1.0), dist_b=("normal", 1.0))
+        got, kname, pad_ok = H.run_padded(g, p, kernel=kid)
+        res = H.gate_full(p, got)
+        tag = f"{dtype} {kernel}({kname}) {M}x{N}x{K} ta={ta} tb={tb}"
+        assert res.ok, f"{tag}: {res}"
+        assert pad_ok, f"{tag}: wrote outside the logical C"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "e4m3"])
+def test_edge_shapes_unpadded_auto(g, dtype):
+    """The same shapes stored densely: unaligned leading dimensions take the fallback."""
+    for i, (M, N, K) in enumerate(SHAPES):
+        ta, tb = bool(i & 1), bool(i & 2)
+        p = W.make_problem(M, N, K, a_type=dtype, trans_a=ta, trans_b=tb, alpha=1.25,
+                           beta=-0.5 if i % 2 else 0.0, epilogue=((i + 1) % 4), seed=60 + i,
+                           dist_a=("normal", 1.0), dist_b=("normal", 1.0))
+        _, got = H.run(g, p)
+        res = H.gate_full(p, got)
+        assert res.ok, f"{dtype} {M}x{N}x{K} ta={ta} tb={tb} aligned={H.mfma_aligned(p)}: {res}"
+
+
+def test_k_zero_is_beta_c_plus_bias(g):
+    for dtype in ["f32", "bf16", "e4m3"]:
+        p = W.make_problem(70, 90, 0, a_type=dtype, beta=-2.0, epilogue=W.EPI_BIAS | W.EPI_GELU,
+                           seed=9)
+        _, got = H.run(g, p)
+        res = H.gate_full(p, got)
+        assert res.ok, (dtype, res)
+
+
+def test_beta_zero_never_reads_c(g):
+    p = W.make_problem(128, 128, 64, a_type="f32", seed=2)
+    p.C = np.full((128, 128), np.nan, np.float32)
+    _, got = H.run(g, p)
+    assert np.isfinite(got).all()
+    assert H.gate_full(p, got).ok
+
+
+def test_m_zero_is_noop(g):
+    import tiled_matrix_multiply_amd as tmm
+    st = tmm.gemm_run(g.handle, None, 0, 5, 5, 0, 0, 1.0, None, 5, 1.0, None, 5, 1.0, 0.0, None,
+                      5, 0, 0, 0, 0, None)
+    assert st == tmm.GEMM_OK
+
+
+@pytest.mark.parametrize("pad", ["aligned", "odd"])
+def test_padded_leading_dimensions(g, pad):
+    """ld > logical width: aligned padding keeps the matrix-core path, odd padding (+1) forces
+    the fallback; both must give the oracle's result and leave the padding untouched."""
+    ld_fn = H.aligned_ld if pad == "aligned" else (lambda w: w + 1)
+    for dtype in ["f32", "bf16", "e4m3"]:
+        p = W.make_problem(150, 90, 170, a_type=dtype, beta=0.5, seed=11, trans_a=True,
+                           epilogue=W.EPI_BIAS)
+        got, kname, pad_ok = H.run_padded(g, p, ld_fn)
+        assert (kname == "simt") == (pad == "odd"), kname
+        res = H.gate_full(p, got)
+        assert res.ok and pad_ok, (dtype, pad, res, pad_ok)
+
+
+def test_unaligned_pointer_falls_back(g):
+    import torch
+    import tiled_matrix_multiply_amd as tmm
+    p = W.make_problem(96, 96, 96, a_type="f32", seed=12)
+    A = H.to_device(np.concatenate([np.zeros(1, np.float32), p.A.ravel()]))[1:]
+    B = H.to_device(p.B)
+    C = H.to_device(p.C)
+    assert g.select_kernel(96, 96, 96, a_type="f32", A=A, B=B, C=C) == "simt"
+    with pytest.raises(tmm.GemmError) as e:
+        tmm.run(g.handle, A, B, C, M=96, N=96, K=96, kernel=tmm.GEMM_KERNEL_MFMA_64)
+    assert e.value.status == tmm.GEMM_ERR_UNSUPPORTED
+    tmm.run(g.handle, A, B, C, M=96, N=96, K=96)
+    torch.cuda.synchronize()
+    assert H.gate_full(p, oracle.decode("f32", H.from_device(C, "f32"))).ok
+
+
+def test_alias_rejected_before_launch(g):
+    import tiled_matrix_multiply_amd as tmm
+    p = W.make_problem(64, 64, 64, a_type="f32", seed=13)
+    d = H.Device(p)
+    with pytest.raises(tmm.GemmError) as e:
+        tmm.run(g.handle, d.A, d.B, d.A, M=64, N=64, K=64)
+    assert e.value.status == tmm.GEMM_ERR_ALIAS

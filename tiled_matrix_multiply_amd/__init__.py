@@ -1,0 +1,243 @@
+"""Python binding of the tiled GEMM library for MI355X (gfx950).
+
+This module only marshals arguments into libgemm.so (the C ABI of include/gemm.h): every step
+of the computation runs in the library's HIP kernels.  The names mirror the C entry points
+(gemm_create, gemm_run, ...).  PyTorch is used only for device memory and the current HIP
+stream, and only inside the tensor helpers (`run`, `bias_gelu`).
+
+Importing this package loads libgemm.so and raises ImportError if it has not been built:
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgemm.so")
+
+# gemm_status_t
+GEMM_OK = 0
+GEMM_ERR_INVALID_HANDLE = -1
+GEMM_ERR_INVALID_VALUE = -2
+GEMM_ERR_UNSUPPORTED = -3
+GEMM_ERR_ALIAS = -4
+GEMM_ERR_DEVICE = -5
+GEMM_ERR_LAUNCH = -6
+GEMM_ERR_NO_MEMORY = -7
+
+# gemm_dtype_t
+GEMM_F32, GEMM_F16, GEMM_BF16, GEMM_E4M3 = 0, 1, 2, 3
+DTYPE = {"f32": GEMM_F32, "f16": GEMM_F16, "bf16": GEMM_BF16, "e4m3": GEMM_E4M3}
+
+# epilogue bits
+GEMM_EPI_NONE, GEMM_EPI_BIAS, GEMM_EPI_GELU = 0, 1, 2
+
+# gemm_kernel_t
+GEMM_KERNEL_AUTO = 0
+GEMM_KERNEL_SIMT = 1
+GEMM_KERNEL_MFMA_64 = 2
+GEMM_KERNEL_MFMA_128 = 3
+GEMM_KERNEL_MFMA_256 = 4
+KERNEL_NAME = {0: "auto", 1: "simt", 2: "mfma64", 3: "mfma128", 4: "mfma256"}
+
+# Every symbol include/gemm.h declares.
+EXPORTS = ("gemm_create", "gemm_destroy", "gemm_check_args", "gemm_run", "gemm_run_kernel",
+           "gemm_select_kernel", "gemm_bias_gelu", "gemm_status_string")
+
+# libgemm.so must resolve its libamdhip64.so.7 dependency to the HIP runtime instance that owns
+# the caller's device pointers and streams.  PyTorch ships its own runtime (soname
+# libamdhip64.so.7, but its libraries ask for plain "libamdhip64.so"): if libgemm.so were loaded
+# first, the system runtime would come in and torch would then load a second one beside it.
+# Loading torch first makes libgemm.so bind to torch's runtime.
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:
+    _torch = None
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as "
+                      f"g; g.build()' or python tiled_matrix_multiply_amd/build.py)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_f32 = ctypes.c_float
+_u32 = ctypes.c_uint32
+_vp = ctypes.c_void_p
+
+_lib.gemm_create.argtypes = [ctypes.POINTER(_vp), _int]
+_lib.gemm_create.restype = _int
+_lib.gemm_destroy.argtypes = [_vp]
+_lib.gemm_destroy.restype = _int
+_lib.gemm_check_args.argtypes = [_i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _i64, _vp, _i64,
+                                 _int, _int, _int, _u32, _vp]
+_lib.gemm_check_args.restype = _int
+_RUN = [_i64, _i64, _i64, _int, _int, _f32, _vp, _i64, _f32, _vp, _i64, _f32, _f32, _vp, _i64,
+        _int, _int, _int, _u32, _vp]
+_lib.gemm_run.argtypes = [_vp, _vp] + _RUN
+_lib.gemm_run.restype = _int
+_lib.gemm_run_kernel.argtypes = [_vp, _int, _vp] + _RUN
+_lib.gemm_run_kernel.restype = _int
+_lib.gemm_select_kernel.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _i64, _vp,
+                                    _i64, _int, _int, _int, _u32, _vp]
+_lib.gemm_select_kernel.restype = _int
+_lib.gemm_bias_gelu.argtypes = [_vp, _vp, _i64, _i64, _vp, _i64, _int, _vp, _u32]
+_lib.gemm_bias_gelu.restype = _int
+_lib.gemm_status_string.argtypes = [_int]
+_lib.gemm_status_string.restype = ctypes.c_char_p
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = status
+        super().__init__(f"{where}: {gemm_status_string(status)} ({status})")
+
+
+def library():
+    """The loaded ctypes library (for symbol checks)."""
+    return _lib
+
+
+# ----------------------------------------------------------------- C ABI, same names --
+
+def gemm_status_string(status: int) -> str:
+    return _lib.gemm_status_string(int(status)).decode()
+
+
+def gemm_create(device: int = 0) -> int:
+    """Create a handle for HIP device `device`; returns the opaque handle value."""
+    h = _vp()
+    st = _lib.gemm_create(ctypes.byref(h), int(device))
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_create")
+    return h.value
+
+
+def gemm_destroy(handle) -> None:
+    st = _lib.gemm_destroy(handle)
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_destroy")
+
+
+def gemm_check_args(M, N, K, transA, transB, A, lda, B, ldb, C, ldc, a_type, b_type, c_type,
+                    epilogue, bias) -> int:
+    """Pointers are integers (device addresses) or None.  Returns the status code."""
+    return _lib.gemm_check_args(M, N, K, transA, transB, A, lda, B, ldb, C, ldc, a_type, b_type,
+                                c_type, epilogue, bias)
+
+
+def gemm_run(handle, stream, M, N, K, transA, transB, alpha, A, lda, scale_a, B, ldb, scale_b,
+             beta, C, ldc, a_type, b_type, c_type, epilogue, bias) -> int:
+    """Raw entry point: returns the status code (no exception)."""
+    return _lib.gemm_run(handle, stream, M, N, K, transA, transB, alpha, A, lda, scale_a, B, ldb,
+                         scale_b, beta, C, ldc, a_type, b_type, c_type, epilogue, bias)
+
+
+def gemm_run_kernel(handle, kernel, stream, M, N, K, transA, transB, alpha, A, lda, scale_a, B,
+                    ldb, scale_b, beta, C, ldc, a_type, b_type, c_type, epilogue, bias) -> int:
+    return _lib.gemm_run_kernel(handle, kernel, stream, M, N, K, transA, transB, alpha, A, lda,
+                                scale_a, B, ldb, scale_b, beta, C, ldc, a_type, b_type, c_type,
+                                epilogue, bias)
+
+
+def gemm_select_kernel(handle, M, N, K, transA, transB, A, lda, B, ldb, C, ldc, a_type, b_type,
+                       c_type, epilogue, bias) -> int:
+    return _lib.gemm_select_kernel(handle, M, N, K, transA, transB, A, lda, B, ldb, C, ldc,
+                                   a_type, b_type, c_type, epilogue, bias)
+
+
+def gemm_bias_gelu(handle, stream, M, N, C, ldc, c_type, bias, epilogue) -> int:
+    return _lib.gemm_bias_gelu(handle, stream, M, N, C, ldc, c_type, bias, epilogue)
+
+
+# ----------------------------------------------------------------- tensor helpers --
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    """Device address of a tensor; an int is taken as an address already."""
+    if t is None or isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def run(handle, A, B, C, *, M, N, K, trans_a=False, trans_b=False, alpha=1.0, beta=0.0,
+        a_type="f32", c_type=None, epilogue=GEMM_EPI_NONE, bias=None, scale_a=1.0,
+        scale_b=1.0, lda=None, ldb=None, ldc=None, kernel=GEMM_KERNEL_AUTO, stream=None):
+    """GEMM on device tensors holding storage words (A, B, C contiguous row-major unless ld*
+    is given).  Raises GemmError on a negative status.  Asynchronous on `stream` (default:
+    torch's current stream)."""
+    c_type = c_type or ("bf16" if a_type == "e4m3" else a_type)
+    lda = lda if lda is not None else (M if trans_a else K)
+    ldb = ldb if ldb is not None else (K if trans_b else N)
+    ldc = ldc if ldc is not None else N
+    st = gemm_run_kernel(handle, kernel, _stream(stream), M, N, K, int(trans_a), int(trans_b),
+                         float(alpha), _ptr(A), lda, float(scale_a), _ptr(B), ldb,
+                         float(scale_b), float(beta), _ptr(C), ldc, DTYPE[a_type], DTYPE[a_type],
+                         DTYPE[c_type], int(epilogue), _ptr(bias))
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_run")
+
+
+def bias_gelu(handle, C, bias, *, M, N, c_type, epilogue=GEMM_EPI_BIAS | GEMM_EPI_GELU,
+              ldc=None, stream=None):
+    """The unfused epilogue pass C = epi(C + bias) in place."""
+    st = gemm_bias_gelu(handle, _stream(stream), M, N, _ptr(C), ldc if ldc is not None else N,
+                        DTYPE[c_type], _ptr(bias), int(epilogue))
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_bias_gelu")
+
+
+def select_kernel(handle, M, N, K, *, trans_a=False, trans_b=False, a_type="f32", A=None,
+                  B=None, C=None, epilogue=GEMM_EPI_NONE, bias=None, lda=None, ldb=None,
+                  ldc=None) -> str:
+    """Name of the kernel family gemm_run picks for these arguments."""
+    c_type = "bf16" if a_type == "e4m3" else a_type
+    k = gemm_select_kernel(handle, M, N, K, int(trans_a), int(trans_b), _ptr(A),
+                           lda if lda is not None else (M if trans_a else K), _ptr(B),
+                           ldb if ldb is not None else (K if trans_b else N), _ptr(C),
+                           ldc if ldc is not None else N, DTYPE[a_type], DTYPE[a_type],
+                           DTYPE[c_type], int(epilogue), _ptr(bias))
+    if k < 0:
+        raise GemmError(k, "gemm_select_kernel")
+    return KERNEL_NAME[k]
+
+
+class Gemm:
+    """Owns one handle (gemm_create / gemm_destroy)."""
+
+    def __init__(self, device: int = 0):
+        self.handle = gemm_create(device)
+
+    def close(self):
+        if self.handle:
+            gemm_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def run(self, A, B, C, **kw):
+        run(self.handle, A, B, C, **kw)
+
+    def bias_gelu(self, C, bias, **kw):
+        bias_gelu(self.handle, C, bias, **kw)
+
+    def select_kernel(self, M, N, K, **kw) -> str:
+        return select_kernel(self.handle, M, N, K, **kw)

@@ -1,0 +1,10 @@
+// Matrix-core GEMM instantiations for f16 inputs (all tile families and operand layouts).
+#include "mfma.hpp"
+
+namespace tgemm {
+
+hipError_t launch_mfma_f16(const GemmParams& p, int tile, bool a_mn, bool b_mn, hipStream_t s) {
+  return launch_mfma_dtype<F16>(p, tile, a_mn, b_mn, s);
+}
+
+}  // namespace tgemm

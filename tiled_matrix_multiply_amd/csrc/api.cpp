@@ -24,6 +24,7 @@ namespace {
 
 constexpr uint32_t kMagic = 0x47454d4du;  // "GEMM"
 constexpr int64_t kMaxDim = 0x7fffffff;
+constexpr int64_t kMaxRowBytes = int64_t(1) << 23;
 
 struct Args {
   int64_t M, N, K;
@@ -104,6 +105,8 @@ bool mfma_aligned(const Args& a) {
   if (a.K > 0) {
     if (!al16(a.A) || !al16(a.B)) return false;
     if ((a.lda * esize(a.at)) % 16 != 0 || (a.ldb * esize(a.bt)) % 16 != 0) return false;
+    // per-lane 32-bit buffer offsets span up to 256 rows of a staged tile
+    if (a.lda * esize(a.at) > kMaxRowBytes || a.ldb * esize(a.bt) > kMaxRowBytes) return false;
   }
   return al16(a.C) && (a.ldc % 4 == 0);
 }

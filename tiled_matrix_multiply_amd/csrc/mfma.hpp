@@ -2,24 +2,32 @@
 //
 // Structure (each piece restated from the pages, rebuilt for CDNA4):
 //  * One workgroup per BM x BN output tile; the grid counts workgroups ("X3: Metal GEMM",
-//    section 6 and its first pitfall: the dispatch unit must be the tile, not the thread).
+//    section 6 and its first pitfall: the dispatch unit is the tile, not the thread).
 //  * Cooperative global -> LDS staging of a BM x BK slice of op(A) and a BK x BN slice of
-//    op(B), zero outside the matrix ("X3", sections 2 and 4), with 16-byte vector loads per
-//    thread (the vectorised loader of "X3", section 7).
+//    op(B) per K step ("X3", sections 2 and 4), 16 contiguous bytes per lane (the vectorised
+//    loader of "X3", section 7).  Here the copy goes straight from global memory into LDS
+//    (buffer loads with the LDS-destination bit), so staging costs no registers.
 //  * A register-blocked accumulator grid per wavefront: each wave keeps FM x FN 32x32 fp32
 //    accumulator tiles for the whole kernel and marches K in MFMA-sized steps ("Case Study:
 //    Steel's BlockMMA", the TM x TN fragment grid and its K-march; "X3", section 4 on why more
 //    accumulators per wave means more reuse).
-//  * Transposition handled by layout, never by branching in the inner loop ("Steel's
-//    BlockMMA", stride constants): both operands are staged K-contiguous in LDS; an operand
-//    whose storage is contiguous along M or N is transposed in registers while staging.
+//  * Transposition by layout, never by branching in the inner loop ("Steel's BlockMMA",
+//    stride constants).  Each operand is copied into LDS in its storage order; an operand stored
+//    contiguous along K is read with 16-byte LDS loads, one stored contiguous along M or N with
+//    the CDNA4 transposing LDS loads (ds_read_b64_tr_b16 / _tr_b8), which hand each lane K-runs
+//    of one column.
 //  * The epilogue applies alpha, beta*C, bias and GELU to the accumulators in registers and
 //    stores once ("Steel's BlockMMA", store_result; "Case Study: The Tiled GEMM", fused
 //    alpha*AB + beta*C), with an unmasked store for interior tiles and a masked store at the
 //    edges ("X3", section 5: store_result versus store_result_safe).
-// What differs from the pages' Metal kernels: MFMA 32x32 tiles instead of 8x8 simdgroup
-// fragments, a double-buffered K loop with a single barrier per step instead of two
-// barriers, an XOR-swizzled LDS layout instead of padding, and an XCD-aware tile order.
+// Zero fill at the edges ("X3", sections 2 and 4): each operand's buffer descriptor spans
+// exactly the bytes the matrix occupies, so loads past its end read zero without touching
+// memory.  Rows past M (or columns past N) that still fall inside the matrix feed only output
+// rows (columns) that are never stored.  The one case that needs care is K: in the last K
+// tile, chunks that reach past K are rewritten in LDS with zeros beyond K.
+// What differs from the pages' Metal kernels: 32x32 MFMA tiles instead of 8x8 simdgroup
+// fragments, a double-buffered K loop with a single barrier per step instead of two, an
+// XOR-swizzled LDS layout instead of padding, and an XCD-aware tile order.
 #pragma once
 
 #include "common.hpp"
@@ -30,31 +38,51 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-// ------------------------------------------------------------------------- LDS layout --
-// Each operand tile row (one m of op(A), or one n of op(B)) holds 128 bytes of K as eight
-// 16-byte chunks.  Chunk c of row r sits at byte r*128 + 16*lds_swizzle(r, c).  The XOR with
-// (r ^ r/8) keeps both access patterns free of bank conflicts: 8 consecutive rows read at the
-// same logical chunk (fragment reads), and rows 8 apart written at the same chunk (the
-// transposing stager).
-constexpr int ROW_BYTES = 128;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int lds_swizzle(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+// Buffer descriptor word 3 for raw (unformatted, unswizzled) buffers on gfx9-family parts.
+constexpr int BUFFER_FLAGS = 0x00020000;
+
+// Raw buffer descriptor over [base, base + bytes): reads past the end return zero.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, BUFFER_FLAGS};
+}
+
+// 16 bytes per lane from the buffer at byte offset voffset straight into LDS at
+// lds_base + 16 * lane (lds_base is wave-uniform).  Written as inline assembly so that the
+// compiler does not treat the in-flight LDS writes as aliasing every LDS read that follows:
+// the kernel itself waits (vmcnt 0) and barriers before any wave reads the stage written.
+// m0 holds the LDS base for the instruction and is restored afterwards.
+__device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, uint32_t lds_base, uint32_t voffset) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voffset), "s"(rsrc)
+      : "memory");
+}
 
 // ------------------------------------------------------------------------- MFMA ops --
-// Each op consumes, per lane, CPL 16-byte chunks of the first operand (32 rows of D) and of
-// the second operand (32 columns of D) for one "k-group" of KG_CHUNKS chunks per row.  Lanes
-// 0-31 supply the first CPL chunks of the group for rows/columns 0-31, lanes 32-63 the next CPL
-// chunks.  Any fixed assignment of k to (lane half, byte) is correct as long as both operands
-// use the same one, which the symmetric operand layouts of these instructions guarantee.
-// Result layout of every 32x32 op: lane l holds column l%32 of D; register r holds row
+// Each op consumes, per lane, CPL 16-byte "chunks" of the first operand (32 rows of D) and of
+// the second operand (32 columns of D) for one k-group.  Lanes 0-31 hold the first half of the
+// group's K range for rows/columns 0-31, lanes 32-63 the second half; inside a lane, K runs in
+// order through the chunk.  Both operands use the same assignment, which is all a dot product
+// needs.  Result layout of every 32x32 op: lane l holds column l%32 of D; register r holds row
 // 8*(r/4) + 4*(l/32) + r%4.
 template <int DT> struct MmaOp;
 
 template <> struct MmaOp<BF16> {
-  static constexpr int KG_CHUNKS = 2, CPL = 1;
+  static constexpr int KG = 16, CPL = 1;  // K per k-group, chunks per lane
   __device__ static __forceinline__ f32x16 run(const u32x4* x, const u32x4* y, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[0]),
                                                    __builtin_bit_cast(bf16x8, y[0]), c, 0, 0, 0);
@@ -62,16 +90,16 @@ template <> struct MmaOp<BF16> {
 };
 
 template <> struct MmaOp<F16> {
-  static constexpr int KG_CHUNKS = 2, CPL = 1;
+  static constexpr int KG = 16, CPL = 1;
   __device__ static __forceinline__ f32x16 run(const u32x4* x, const u32x4* y, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x[0]),
                                                   __builtin_bit_cast(f16x8, y[0]), c, 0, 0, 0);
   }
 };
 
-// fp32: the 32x32x2 op takes one value per lane; a 16-byte chunk feeds four ops.
+// fp32: the 32x32x2 op takes one value per lane; one 4-value chunk feeds four ops.
 template <> struct MmaOp<F32> {
-  static constexpr int KG_CHUNKS = 2, CPL = 1;
+  static constexpr int KG = 8, CPL = 1;
   __device__ static __forceinline__ f32x16 run(const u32x4* x, const u32x4* y, f32x16 c) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -84,121 +112,13 @@ template <> struct MmaOp<F32> {
 // fp8 E4M3 (OCP): the 32x32x64 f8f6f4 op, format code 0 (E4M3) for both operands, unit block
 // scales (E8M0 exponent 127 = 2^0); the per-tensor scales are folded into alpha instead.
 template <> struct MmaOp<E4M3> {
-  static constexpr int KG_CHUNKS = 4, CPL = 2;
+  static constexpr int KG = 64, CPL = 2;
   __device__ static __forceinline__ f32x16 run(const u32x4* x, const u32x4* y, f32x16 c) {
     const i32x8 xa = {(int)x[0][0], (int)x[0][1], (int)x[0][2], (int)x[0][3],
                       (int)x[1][0], (int)x[1][1], (int)x[1][2], (int)x[1][3]};
     const i32x8 ya = {(int)y[0][0], (int)y[0][1], (int)y[0][2], (int)y[0][3],
                       (int)y[1][0], (int)y[1][1], (int)y[1][2], (int)y[1][3]};
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa, ya, c, 0, 0, 0, 127, 0, 127);
-  }
-};
-
-// ----------------------------------------------------------------------------- staging --
-
-// Load the first `n` elements (n < 16/ES) of a 16-byte chunk, zero the rest.
-template <int ES>
-__device__ __forceinline__ u32x4 load_partial(const uint8_t* src, int n) {
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-  for (int e = 0; e < n; ++e) {
-    uint32_t v;
-    if constexpr (ES == 4) v = reinterpret_cast<const uint32_t*>(src)[e];
-    else if constexpr (ES == 2) v = reinterpret_cast<const uint16_t*>(src)[e];
-    else v = src[e];
-    const int bit = e * ES * 8;
-    w[bit >> 5] |= v << (bit & 31);
-  }
-  return u32x4{w[0], w[1], w[2], w[3]};
-}
-
-// Global -> register -> LDS staging of one operand tile (ROWS rows of 128 bytes of K) by NTH
-// threads.  K-contiguous storage (row r at X + r*ld): each thread moves LOADS whole chunks.
-// MN-contiguous storage (k-row k at X + k*ld): each thread loads KR k-rows of one 16-byte
-// run along M/N and transposes them into CE row pieces of KR elements.
-template <int ES, int ROWS, int NTH, bool MN>
-struct Stage {
-  static constexpr int CE = 16 / ES;               // elements per 16-byte chunk
-  static constexpr int LOADS = ROWS * 8 / NTH;     // 16-byte loads per thread per tile
-  static constexpr int KR = MN ? (LOADS < CE ? LOADS : CE) : 1;
-  static constexpr int UNITS = LOADS / KR;
-  static constexpr int MNC = ROWS / CE;            // 16-byte runs along M/N per k-row
-  static_assert(ROWS * 8 % NTH == 0 && LOADS % KR == 0, "staging split");
-
-  __device__ static __forceinline__ void load(u32x4 (&r)[LOADS], const uint8_t* X, int64_t ld,
-                                              int row0, int rows, int k0, int K, int t) {
-    if constexpr (!MN) {
-#pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        const int e = t + u * NTH, row = e >> 3, c = e & 7;
-        const int grow = row0 + row, gk = k0 + c * CE;
-        const uint8_t* src = X + ((int64_t)grow * ld + gk) * ES;
-        if (grow < rows && gk + CE <= K) r[u] = *reinterpret_cast<const u32x4*>(src);
-        else if (grow < rows && gk < K) r[u] = load_partial<ES>(src, K - gk);
-        else r[u] = u32x4{0u, 0u, 0u, 0u};
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < UNITS; ++u) {
-        const int e = t + u * NTH, mc = e % MNC, kb = e / MNC;
-        const int gmn = row0 + mc * CE;
-#pragma unroll
-        for (int q = 0; q < KR; ++q) {
-          const int gk = k0 + kb * KR + q;
-          const uint8_t* src = X + ((int64_t)gk * ld + gmn) * ES;
-          u32x4 v = u32x4{0u, 0u, 0u, 0u};
-          if (gk < K && gmn + CE <= rows) v = *reinterpret_cast<const u32x4*>(src);
-          else if (gk < K && gmn < rows) v = load_partial<ES>(src, rows - gmn);
-          r[u * KR + q] = v;
-        }
-      }
-    }
-  }
-
-  // Dword w of the piece for M/N position j: the elements of k-rows w*(4/ES) .. at column j.
-  __device__ static __forceinline__ uint32_t piece_dword(const u32x4* r, int j, int w) {
-    if constexpr (ES == 4) {
-      return r[w][j];
-    } else if constexpr (ES == 2) {
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      return __builtin_amdgcn_perm(r[2 * w + 1][j >> 1], r[2 * w][j >> 1], sel);
-    } else {
-      const int b = j & 3, d = j >> 2;
-      const uint32_t sel = (uint32_t)b | ((uint32_t)(4 + b) << 8) | 0x0c0c0000u;
-      const uint32_t lo = __builtin_amdgcn_perm(r[4 * w + 1][d], r[4 * w][d], sel);
-      const uint32_t hi = __builtin_amdgcn_perm(r[4 * w + 3][d], r[4 * w + 2][d], sel);
-      return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-    }
-  }
-
-  __device__ static __forceinline__ void store(const u32x4 (&r)[LOADS], uint8_t* lds, int t) {
-    if constexpr (!MN) {
-#pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        const int e = t + u * NTH, row = e >> 3, c = e & 7;
-        *reinterpret_cast<u32x4*>(lds + row * ROW_BYTES + lds_swizzle(row, c) * 16) = r[u];
-      }
-    } else {
-      constexpr int PIECE = KR * ES;  // bytes per row piece: 4, 8 or 16
-#pragma unroll
-      for (int u = 0; u < UNITS; ++u) {
-        const int e = t + u * NTH, mc = e % MNC, kb = e / MNC;
-        const int kbyte = kb * PIECE, c = kbyte >> 4, off = kbyte & 15;
-        const u32x4* src = &r[u * KR];
-#pragma unroll
-        for (int j = 0; j < CE; ++j) {
-          const int row = mc * CE + j;
-          uint8_t* dst = lds + row * ROW_BYTES + lds_swizzle(row, c) * 16 + off;
-          if constexpr (PIECE == 16) {
-            *reinterpret_cast<u32x4*>(dst) = u32x4{piece_dword(src, j, 0), piece_dword(src, j, 1),
-                                                   piece_dword(src, j, 2), piece_dword(src, j, 3)};
-          } else if constexpr (PIECE == 8) {
-            *reinterpret_cast<u32x2*>(dst) = u32x2{piece_dword(src, j, 0), piece_dword(src, j, 1)};
-          } else {
-            *reinterpret_cast<uint32_t*>(dst) = piece_dword(src, j, 0);
-          }
-        }
-      }
-    }
   }
 };
 
@@ -213,27 +133,98 @@ struct MfmaCfg {
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 accumulators per wave
   static constexpr int ES = DTypeInfo<DT_>::bytes;
-  static constexpr int BKE = ROW_BYTES / ES;           // K elements per staged tile
+  static constexpr int BKE = 128 / ES;                 // K elements per staged tile (128 bytes)
   static constexpr bool A_MN = A_MN_, B_MN = B_MN_;    // operand stored contiguous along M/N
-  static constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
-  static constexpr int NTH = NT / 2;                   // stager threads per operand
-  using SA = Stage<ES, BM, NTH, A_MN_>;
-  using SB = Stage<ES, BN, NTH, B_MN_>;
-  static_assert(SA::LOADS == SB::LOADS, "both operands share the prefetch registers");
-  static constexpr int LOADS = SA::LOADS;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is a whole number of 32x32 tiles");
+};
+
+// One operand's staged tile.  LDS holds it in storage order:
+//  * K-contiguous (A not transposed, B transposed): BX rows of 128 bytes (one row per m or n),
+//    eight 16-byte chunks per row, chunk c of row r at position c ^ kswz(r);
+//  * M/N-contiguous (A transposed, B not transposed): BKE rows of BX*ES bytes (one row per k),
+//    chunk c of row k at position c ^ mswz(k).
+// The XOR patterns keep the fragment reads free of bank conflicts: eight consecutive rows at
+// one chunk (16-byte reads), or 4 (16-bit) / 8 (8-bit) consecutive k-rows at the same columns
+// (transposing reads).
+template <class C, bool IS_A>
+struct Operand {
+  static constexpr bool MN = IS_A ? C::A_MN : C::B_MN;
+  static constexpr int BX = IS_A ? C::BM : C::BN;   // tile extent along M (A) or N (B)
+  static constexpr int ES = C::ES, CE = 16 / ES;    // elements per chunk
+  static constexpr int RB = MN ? BX * ES : 128;     // LDS row bytes
+  static constexpr int CPR = RB / 16;               // chunks per LDS row
+  static constexpr int WLOADS = BX / 8;             // 1 KB wave-loads per tile (BX*128 bytes)
+  static constexpr int PER_WAVE = WLOADS / C::NW;
+  static constexpr int LDS_OFF = IS_A ? 0 : C::A_BYTES;
+  static_assert(WLOADS % C::NW == 0, "every wave issues the same number of loads");
+  static_assert(!MN || (RB <= 1024 && 1024 % RB == 0), "whole k-rows per wave-load");
+
+  __device__ static __forceinline__ int kswz(int r) { return (r ^ (r >> 3)) & 7; }
+  __device__ static __forceinline__ int mswz(int k) {
+    if constexpr (ES == 4) return 0;  // 32 lanes read one k-row: never conflicts
+    else if constexpr (ES == 2) return (k & 3) << (CPR >= 16 ? 2 : 1);
+    else if constexpr (CPR >= 16) return (k & 7) << 1;
+    else if constexpr (CPR == 8) return k & 7;
+    else return (k >> 1) & 3;
+  }
+
+  // The chunk this lane copies in wave-load u: its row in the tile and its logical chunk.
+  __device__ static __forceinline__ void chunk_of(int u, int lane, int& row, int& c) {
+    if constexpr (!MN) {
+      row = 8 * u + (lane >> 3);
+      c = (lane & 7) ^ kswz(row);
+    } else {
+      constexpr int RPW = 1024 / RB;  // k-rows per wave-load
+      row = RPW * u + lane / CPR;
+      c = (lane % CPR) ^ mswz(row);
+    }
+  }
 };
 
 // Group of tile rows walked together so that concurrently running tiles share A panels.
 constexpr int TILE_GROUP_M = 4;
 
+// Byte extent of a stored rows x cols matrix from element (r0, c0) to its last element,
+// rounded down to whole 16-byte chunks (so that no 16-byte load straddles the end: a chunk is
+// either entirely inside the matrix or reads as zero; the last-K-tile fix-up restores the
+// valid part of a chunk cut off here), clamped to what a buffer descriptor holds, and 0 when
+// (r0, c0) is past the end.
+__device__ __forceinline__ uint32_t extent_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t r0,
+                                                 int64_t c0, int es) {
+  const int64_t e = (((rows - 1 - r0) * ld + cols - c0) * es) & ~int64_t(15);
+  return e <= 0 ? 0u : (e >= 0xfffffff0LL ? 0xfffffff0u : (uint32_t)e);
+}
+
+template <int ES>
+__device__ __forceinline__ u32x4 load_partial(const uint8_t* src, int n) {
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (int e = 0; e < n; ++e) {
+    uint32_t v;
+    if constexpr (ES == 4) v = reinterpret_cast<const uint32_t*>(src)[e];
+    else if constexpr (ES == 2) v = reinterpret_cast<const uint16_t*>(src)[e];
+    else v = src[e];
+    const int bit = e * ES * 8;
+    w[bit >> 5] |= v << (bit & 31);
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// Flags computed on the host: which operands need the last-K-tile fix-up.
+enum : uint32_t { FIX_A = 1u << 8, FIX_B = 1u << 9 };
+
 template <class C>
 __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE_BYTES];
   using Op = MmaOp<C::DT>;
-  constexpr int G = 8 / Op::KG_CHUNKS;  // k-groups per staged tile
+  using OA = Operand<C, true>;
+  using OB = Operand<C, false>;
+  constexpr int ES = C::ES;
+  constexpr int G = C::BKE / Op::KG;  // k-groups per staged tile
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index, in a scalar register
 
   // Tile order.  Workgroups are dealt to the 8 XCDs round-robin by id; renumber so each XCD
   // receives a contiguous range, then walk tiles in groups of TILE_GROUP_M tile rows so the
@@ -249,22 +240,157 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int wm = wave / C::WN, wn = wave % C::WN;
 
-  // The first half of the threads stages op(A), the second half op(B) (wave-uniform split).
-  const bool stages_a = tid < C::NTH;
-  const int st = stages_a ? tid : tid - C::NTH;
   const uint8_t* Ag = reinterpret_cast<const uint8_t*>(p.A);
   const uint8_t* Bg = reinterpret_cast<const uint8_t*>(p.B);
 
-  u32x4 pre[C::LOADS];
-  auto gload = [&](int kt) {
+  // Per-lane byte offsets of the chunks this lane copies (loop invariant).
+  uint32_t voA[OA::PER_WAVE], voB[OB::PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < OA::PER_WAVE; ++i) {
+    int r, c;
+    OA::chunk_of(wave + C::NW * i, lane, r, c);
+    voA[i] = (uint32_t)((int64_t)r * p.lda * ES + c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < OB::PER_WAVE; ++i) {
+    int r, c;
+    OB::chunk_of(wave + C::NW * i, lane, r, c);
+    voB[i] = (uint32_t)((int64_t)r * p.ldb * ES + c * 16);
+  }
+
+  // Issue the direct copies of K tile kt into LDS stage buf.
+  auto issue = [&](int kt, int buf) {
     const int k0 = kt * C::BKE;
-    if (stages_a) C::SA::load(pre, Ag, p.lda, m0, p.M, k0, p.K, st);
-    else C::SB::load(pre, Bg, p.ldb, n0, p.N, k0, p.K, st);
+    uint8_t* sA = smem + buf * C::STAGE_BYTES + OA::LDS_OFF;
+    uint8_t* sB = smem + buf * C::STAGE_BYTES + OB::LDS_OFF;
+    const uint8_t* baseA;
+    uint32_t extA;
+    if constexpr (!OA::MN) {  // A stored M x K
+      baseA = Ag + ((int64_t)m0 * p.lda + k0) * ES;
+      extA = extent_bytes(p.M, p.K, p.lda, m0, k0, ES);
+    } else {                  // A stored K x M
+      baseA = Ag + ((int64_t)k0 * p.lda + m0) * ES;
+      extA = extent_bytes(p.K, p.M, p.lda, k0, m0, ES);
+    }
+    const uint8_t* baseB;
+    uint32_t extB;
+    if constexpr (OB::MN) {   // B stored K x N
+      baseB = Bg + ((int64_t)k0 * p.ldb + n0) * ES;
+      extB = extent_bytes(p.K, p.N, p.ldb, k0, n0, ES);
+    } else {                  // B stored N x K
+      baseB = Bg + ((int64_t)n0 * p.ldb + k0) * ES;
+      extB = extent_bytes(p.N, p.K, p.ldb, n0, k0, ES);
+    }
+    const i32x4 ra = make_rsrc(baseA, extA);
+    const i32x4 rb = make_rsrc(baseB, extB);
+    const uint32_t la = (uint32_t)reinterpret_cast<uintptr_t>(sA) + wave_u * 1024;
+    const uint32_t lb = (uint32_t)reinterpret_cast<uintptr_t>(sB) + wave_u * 1024;
+#pragma unroll
+    for (int i = 0; i < OA::PER_WAVE; ++i) buffer_load_lds16(ra, la + C::NW * i * 1024, voA[i]);
+#pragma unroll
+    for (int i = 0; i < OB::PER_WAVE; ++i) buffer_load_lds16(rb, lb + C::NW * i * 1024, voB[i]);
   };
-  auto lstore = [&](int buf) {
-    uint8_t* base = smem + buf * C::STAGE_BYTES;
-    if (stages_a) C::SA::store(pre, base, st);
-    else C::SB::store(pre, base + C::BM * ROW_BYTES, st);
+
+  // Last K tile: rewrite every chunk that reaches past K (K-contiguous operand) or past the
+  // matrix edge in the final k-row (M/N-contiguous operand) with its valid elements and zeros.
+  // Runs after the tile's copies have landed (vmcnt 0) and before the barrier.
+  auto fixup = [&](int kt, int buf) {
+    const int k0 = kt * C::BKE;
+    if (p.epi & FIX_A) {
+#pragma unroll
+      for (int i = 0; i < OA::PER_WAVE; ++i) {
+        const int u = wave + C::NW * i;
+        int r, c;
+        OA::chunk_of(u, lane, r, c);
+        uint8_t* dst = smem + buf * C::STAGE_BYTES + OA::LDS_OFF + u * 1024 + lane * 16;
+        if constexpr (!OA::MN) {
+          const int gm = m0 + r, gk = k0 + c * OA::CE;
+          if (gk + OA::CE > p.K) {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (gm < p.M && gk < p.K) v = load_partial<ES>(Ag + ((int64_t)gm * p.lda + gk) * ES, p.K - gk);
+            *reinterpret_cast<u32x4*>(dst) = v;
+          }
+        } else {
+          const int gk = k0 + r, gm = m0 + c * OA::CE;
+          if (gk == p.K - 1 && gm < p.M && gm + OA::CE > p.M)
+            *reinterpret_cast<u32x4*>(dst) = load_partial<ES>(Ag + ((int64_t)gk * p.lda + gm) * ES, p.M - gm);
+        }
+      }
+    }
+    if (p.epi & FIX_B) {
+#pragma unroll
+      for (int i = 0; i < OB::PER_WAVE; ++i) {
+        const int u = wave + C::NW * i;
+        int r, c;
+        OB::chunk_of(u, lane, r, c);
+        uint8_t* dst = smem + buf * C::STAGE_BYTES + OB::LDS_OFF + u * 1024 + lane * 16;
+        if constexpr (!OB::MN) {
+          const int gn = n0 + r, gk = k0 + c * OB::CE;
+          if (gk + OB::CE > p.K) {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (gn < p.N && gk < p.K) v = load_partial<ES>(Bg + ((int64_t)gn * p.ldb + gk) * ES, p.K - gk);
+            *reinterpret_cast<u32x4*>(dst) = v;
+          }
+        } else {
+          const int gk = k0 + r, gn = n0 + c * OB::CE;
+          if (gk == p.K - 1 && gn < p.N && gn + OB::CE > p.N)
+            *reinterpret_cast<u32x4*>(dst) = load_partial<ES>(Bg + ((int64_t)gk * p.ldb + gn) * ES, p.N - gn);
+        }
+      }
+    }
+  };
+
+  // Fragment reads.  K-contiguous: one or two 16-byte reads per lane.  M/N-contiguous:
+  // transposing reads, each giving a lane 4 (16-bit) or 8 (8-bit) consecutive k of its column;
+  // fp32 reads one value per k-row.
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  auto read_frag = [&](const uint8_t* s, auto opnd, int wbase, int f, int g, u32x4* out) {
+    using O = decltype(opnd);
+    if constexpr (!O::MN) {
+      const int row = wbase + f * 32 + lrow;
+#pragma unroll
+      for (int x = 0; x < Op::CPL; ++x) {
+        const int c = (g * Op::KG * ES) / 16 + lhalf * Op::CPL + x;
+        out[x] = *reinterpret_cast<const u32x4*>(s + row * 128 + ((c ^ O::kswz(row)) << 4));
+      }
+    } else if constexpr (ES == 2) {
+      const int q = lane >> 4, sl = lane & 15;
+      const int n = wbase + f * 32 + 16 * (q & 1) + 4 * (sl & 3);
+      uint32_t w[4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int k = g * 16 + 8 * (q >> 1) + 4 * t + (sl >> 2);
+        const uint8_t* a = s + k * O::RB + (((n >> 3) ^ O::mswz(k)) << 4) + ((n & 7) << 1);
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a);
+        const u32x2 d = __builtin_bit_cast(u32x2, v);
+        w[2 * t] = d[0];
+        w[2 * t + 1] = d[1];
+      }
+      out[0] = u32x4{w[0], w[1], w[2], w[3]};
+    } else if constexpr (ES == 1) {
+      const int q = lane >> 4, sl = lane & 15;
+      const int n = wbase + f * 32 + 16 * (q & 1) + 8 * (sl & 1);
+      uint32_t w[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int k = g * 64 + 32 * (q >> 1) + 8 * t + (sl >> 1);
+        const uint8_t* a = s + k * O::RB + (((n >> 4) ^ O::mswz(k)) << 4) + (n & 15);
+        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)a);
+        w[2 * t] = (uint32_t)v[0];
+        w[2 * t + 1] = (uint32_t)v[1];
+      }
+      out[0] = u32x4{w[0], w[1], w[2], w[3]};
+      out[1] = u32x4{w[4], w[5], w[6], w[7]};
+    } else {
+      const int n = wbase + f * 32 + lrow;
+      uint32_t w[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int k = g * 8 + 4 * lhalf + t;
+        w[t] = *reinterpret_cast<const uint32_t*>(s + k * O::RB + (((n >> 2) ^ O::mswz(k)) << 4) + ((n & 3) << 2));
+      }
+      out[0] = u32x4{w[0], w[1], w[2], w[3]};
+    }
   };
 
   f32x16 acc[C::FM][C::FN];
@@ -275,60 +401,61 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int lrow = lane & 31, lhalf = lane >> 5;
   auto compute = [&](int buf) {
-    const uint8_t* As = smem + buf * C::STAGE_BYTES;
-    const uint8_t* Bs = As + C::BM * ROW_BYTES;
+    const uint8_t* sA = smem + buf * C::STAGE_BYTES + OA::LDS_OFF;
+    const uint8_t* sB = smem + buf * C::STAGE_BYTES + OB::LDS_OFF;
+    u32x4 af[2][C::FM][Op::CPL], bf[2][C::FN][Op::CPL];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) read_frag(sA, OA{}, wm * C::WTM, i, 0, af[0][i]);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) read_frag(sB, OB{}, wn * C::WTN, j, 0, bf[0][j]);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      u32x4 af[C::FM][Op::CPL], bf[C::FN][Op::CPL];
+      const int cur = g & 1;
+      if (g + 1 < G) {
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        const int row = wm * C::WTM + i * 32 + lrow;
+        for (int i = 0; i < C::FM; ++i) read_frag(sA, OA{}, wm * C::WTM, i, g + 1, af[cur ^ 1][i]);
 #pragma unroll
-        for (int x = 0; x < Op::CPL; ++x) {
-          const int c = g * Op::KG_CHUNKS + lhalf * Op::CPL + x;
-          af[i][x] = *reinterpret_cast<const u32x4*>(As + row * ROW_BYTES + lds_swizzle(row, c) * 16);
-        }
+        for (int j = 0; j < C::FN; ++j) read_frag(sB, OB{}, wn * C::WTN, j, g + 1, bf[cur ^ 1][j]);
       }
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int row = wn * C::WTN + j * 32 + lrow;
-#pragma unroll
-        for (int x = 0; x < Op::CPL; ++x) {
-          const int c = g * Op::KG_CHUNKS + lhalf * Op::CPL + x;
-          bf[j][x] = *reinterpret_cast<const u32x4*>(Bs + row * ROW_BYTES + lds_swizzle(row, c) * 16);
-        }
-      }
-      // D = op(B)^T-fragment x op(A)^T-fragment: rows of D are n, columns are m, so each lane
-      // ends up holding 4 consecutive n of one m (vector stores along the C row).
+      // D = op(B)-fragment x op(A)-fragment: rows of D are n, columns are m, so each lane ends
+      // up holding 4 consecutive n of one m (vector stores along the C row).
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) acc[i][j] = Op::run(bf[j], af[i], acc[i][j]);
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = Op::run(bf[cur][j], af[cur][i], acc[i][j]);
     }
   };
 
-  // Double-buffered K loop: tile kt+1 travels global -> registers while tile kt is multiplied
-  // from LDS; one barrier per step separates "stage kt+1 written" from "stage kt+1 read" and
-  // "stage kt read" from "stage kt overwritten two steps later".
+  // Double-buffered K loop: the copies of tile kt+1 fly while tile kt is multiplied from
+  // LDS; one barrier per step separates "stage written" from "stage read" and "stage read"
+  // from "stage overwritten two steps later".
   const int KT = (p.K + C::BKE - 1) / C::BKE;
+  const bool need_fix = (p.epi & (FIX_A | FIX_B)) != 0;
   if (KT > 0) {
-    gload(0);
-    lstore(0);
+    issue(0, 0);
+    if (KT == 1 && need_fix) {
+      __builtin_amdgcn_s_waitcnt(0);
+      fixup(0, 0);
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) gload(kt + 1);
+    if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
     compute(kt & 1);
-    if (kt + 1 < KT) lstore((kt + 1) & 1);
+    if (kt + 2 == KT && need_fix) {
+      __builtin_amdgcn_s_waitcnt(0);
+      fixup(kt + 1, (kt + 1) & 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
   // Epilogue in registers, then one store per element.
   const bool full = (m0 + C::BM <= p.M) && (n0 + C::BN <= p.N);
   const float alpha = p.alpha, beta = p.beta;
-  const uint32_t epi = p.epi;
+  const uint32_t epi = p.epi & (EPI_BIAS | EPI_GELU);
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
     const int m = m0 + wm * C::WTM + i * 32 + lrow;
@@ -386,16 +513,20 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
 }
 
 template <class C>
-hipError_t launch_mfma_cfg(const GemmParams& p, hipStream_t s) {
+hipError_t launch_mfma_cfg(GemmParams p, hipStream_t s) {
   const int64_t T = (int64_t)p.tiles_m * p.tiles_n;
+  // Last-K-tile fix-ups: a K-contiguous operand whose K is not a whole number of tiles, or an
+  // M/N-contiguous operand whose row length is not a whole number of 16-byte chunks.
+  constexpr int CE = 16 / C::ES;
+  const bool fix_a = C::A_MN ? (p.M % CE != 0) : (p.K % C::BKE != 0);
+  const bool fix_b = C::B_MN ? (p.N % CE != 0) : (p.K % C::BKE != 0);
+  p.epi |= (fix_a ? FIX_A : 0u) | (fix_b ? FIX_B : 0u);
   hipLaunchKernelGGL((gemm_mfma_kernel<C>), dim3((unsigned)T), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
 // Tile families: 0 -> 64x64 (2x2 waves of 32x32), 1 -> 128x128 (2x2 waves of 64x64),
 // 2 -> 256x256 (2x4 waves of 128x64).
-constexpr int TILE_SIZE[3] = {64, 128, 256};
-
 template <int DT, int TILE, int WM, int WN>
 hipError_t launch_mfma_layout(const GemmParams& p, bool a_mn, bool b_mn, hipStream_t s) {
   if (!a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, false>>(p, s);

@@ -230,6 +230,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--headline-only-loop", type=int, default=0,
                     help="run only N headline steps (for profiler passes) and exit")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="with --headline-only-loop: also run a plain device copy of this many "
+                         "bytes three times (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -259,29 +262,37 @@ def main():
             head.step()
         torch.cuda.synchronize()
         print(f"[bench] ran {args.headline_only_loop} headline steps", file=sys.stderr)
+        if args.copy_bytes:
+            src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            print(f"[bench] copied {args.copy_bytes} bytes 3 times", file=sys.stderr)
         return
 
-    # Headline: W untimed steps, then exactly K steps between two synchronisations, each
-    # bracketed by an event pair on the launch stream.
+    # Headline: W untimed steps, then exactly K back-to-back steps between two
+    # synchronisations, with one HIP event pair around them on the launch stream (the
+    # average launch duration for the roofline).  A second pass times each step with its own
+    # event pair for the median and its bootstrap CI.
     for _ in range(args.warmup):
         head.step()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for s, e in ev:
-        s.record(head.stream)
+    e0.record(head.stream)
+    for _ in range(args.steps):
         head.step()
-        e.record(head.stream)
+    e1.record(head.stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = np.array([s.elapsed_time(e) for s, e in ev])
     ms_per_step = wall * 1e3 / args.steps
     value = head_p.flops / (ms_per_step * 1e-3) / 1e12
-    head_row = summarize("bf16+bias+GELU fused 4096 (headline)", head, ms, "bf16")
-    mean_ms = float(np.mean(ms))
+    mean_ms = e0.elapsed_time(e1) / args.steps
     achieved = head_p.flops / (mean_ms * 1e-3) / 1e12
+    ms = head.time(args.steps, warmup_s=0.05)
+    head_row = summarize("bf16+bias+GELU fused 4096 (headline)", head, ms, "bf16")
 
     sweeps = []
     if not args.no_sweeps:

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void bias_gelu_vec_kernel(void* C, int64_t ldc
     for (int e = 0; e < 8; ++e) {
       float x = v[e];
       if (epi & EPI_BIAS) x += bias[n + e];
-      if (epi & EPI_GELU) x = gelu_erf(x);
+      if (epi & EPI_GELU) x = gelu_out<CT>(x);
       v[e] = x;
     }
     if constexpr (CT == F32) {
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void bias_gelu_scalar_kernel(void* C, int64_t 
     const int64_t idx = (int64_t)m * ldc + n;
     float x = load_as_float<CT>(C, idx);
     if (epi & EPI_BIAS) x += bias[n];
-    if (epi & EPI_GELU) x = gelu_erf(x);
+    if (epi & EPI_GELU) x = gelu_out<CT>(x);
     store_from_float<CT>(C, idx, x);
   }
 }

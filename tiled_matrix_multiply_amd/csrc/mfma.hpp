@@ -42,6 +42,7 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -82,29 +83,31 @@ __device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, uint32_t lds_base,
 template <int DT> struct MmaOp;
 
 template <> struct MmaOp<BF16> {
-  static constexpr int KG = 16, CPL = 1;  // K per k-group, chunks per lane
-  __device__ static __forceinline__ f32x16 run(const u32x4* x, const u32x4* y, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[0]),
-                                                   __builtin_bit_cast(bf16x8, y[0]), c, 0, 0, 0);
+  static constexpr int KG = 16, CPL = 1;  // K per k-group, 16-byte chunks per lane
+  using Frag = u32x4;
+  __device__ static __forceinline__ f32x16 run(const Frag& x, const Frag& y, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x),
+                                                   __builtin_bit_cast(bf16x8, y), c, 0, 0, 0);
   }
 };
 
 template <> struct MmaOp<F16> {
   static constexpr int KG = 16, CPL = 1;
-  __device__ static __forceinline__ f32x16 run(const u32x4* x, const u32x4* y, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x[0]),
-                                                  __builtin_bit_cast(f16x8, y[0]), c, 0, 0, 0);
+  using Frag = u32x4;
+  __device__ static __forceinline__ f32x16 run(const Frag& x, const Frag& y, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x),
+                                                  __builtin_bit_cast(f16x8, y), c, 0, 0, 0);
   }
 };
 
 // fp32: the 32x32x2 op takes one value per lane; one 4-value chunk feeds four ops.
 template <> struct MmaOp<F32> {
   static constexpr int KG = 8, CPL = 1;
-  __device__ static __forceinline__ f32x16 run(const u32x4* x, const u32x4* y, f32x16 c) {
+  using Frag = u32x4;
+  __device__ static __forceinline__ f32x16 run(const Frag& x, const Frag& y, f32x16 c) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(x[0][s]), __uint_as_float(y[0][s]),
-                                               c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(x[s]), __uint_as_float(y[s]), c, 0, 0, 0);
     return c;
   }
 };
@@ -113,12 +116,11 @@ template <> struct MmaOp<F32> {
 // scales (E8M0 exponent 127 = 2^0); the per-tensor scales are folded into alpha instead.
 template <> struct MmaOp<E4M3> {
   static constexpr int KG = 64, CPL = 2;
-  __device__ static __forceinline__ f32x16 run(const u32x4* x, const u32x4* y, f32x16 c) {
-    const i32x8 xa = {(int)x[0][0], (int)x[0][1], (int)x[0][2], (int)x[0][3],
-                      (int)x[1][0], (int)x[1][1], (int)x[1][2], (int)x[1][3]};
-    const i32x8 ya = {(int)y[0][0], (int)y[0][1], (int)y[0][2], (int)y[0][3],
-                      (int)y[1][0], (int)y[1][1], (int)y[1][2], (int)y[1][3]};
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa, ya, c, 0, 0, 0, 127, 0, 127);
+  using Frag = u32x8;
+  __device__ static __forceinline__ f32x16 run(const Frag& x, const Frag& y, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, x),
+                                                           __builtin_bit_cast(i32x8, y), c, 0, 0,
+                                                           0, 127, 0, 127);
   }
 };
 
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   constexpr int ES = C::ES;
   constexpr int G = C::BKE / Op::KG;  // k-groups per staged tile
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lane_id = lane;
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index, in a scalar register
 
   // Tile order.  Workgroups are dealt to the 8 XCDs round-robin by id; renumber so each XCD
@@ -295,6 +297,10 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   // matrix edge in the final k-row (M/N-contiguous operand) with its valid elements and zeros.
   // Runs after the tile's copies have landed (vmcnt 0) and before the barrier.
   auto fixup = [&](int kt, int buf) {
+    // An opaque copy of the lane index keeps the compiler from hoisting this rarely run code's
+    // address arithmetic out of the K loop, where it would hold registers for every iteration.
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
     const int k0 = kt * C::BKE;
     if (p.epi & FIX_A) {
 #pragma unroll
@@ -344,54 +350,97 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   // transposing reads, each giving a lane 4 (16-bit) or 8 (8-bit) consecutive k of its column;
   // fp32 reads one value per k-row.
   const int lrow = lane & 31, lhalf = lane >> 5;
-  auto read_frag = [&](const uint8_t* s, auto opnd, int wbase, int f, int g, u32x4* out) {
+  using Frag = typename Op::Frag;
+  // Per-lane LDS byte offsets of the fragment reads, computed once and kept opaque so that the
+  // compiler holds exactly these few registers instead of materialising one address per
+  // (fragment, k-group, chunk).
+  //  * K-contiguous tile: row = wbase + 32 f + lrow and chunk c = KGC g + CPL lhalf + x sit at
+  //    byte row*128 + 16 (c ^ kswz(row)), and kswz(row) = s_lane ^ 4 ((wbase/32 + f) & 1) with
+  //    s_lane = (lrow & 7) ^ (lrow >> 3).  So the offset is
+  //      (wbase + 32 f) * 128 + (kbase[par] ^ 16 (KGC g + x)),  par = (wbase/32 + f) & 1,
+  //    kbase[par] = lrow*128 + 16 ((CPL lhalf) ^ s_lane ^ 4 par).
+  //  * M/N-contiguous tile: the swizzle depends only on k % 4 (16-bit) or k % 8 (8-bit), which is
+  //    fixed per lane, so each fragment f has one base and every k-group / k-row step is a
+  //    plain offset.
+  constexpr int KGC = Op::KG * ES / 16;  // chunks per k-group
+  const int s_lane = (lrow & 7) ^ (lrow >> 3);
+  auto kbase = [&](int par) {
+    int v = lrow * 128 + 16 * ((Op::CPL * lhalf) ^ s_lane ^ (4 * par));
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+  auto mbase = [&](auto opnd, int wbase, int f) {
     using O = decltype(opnd);
-    if constexpr (!O::MN) {
-      const int row = wbase + f * 32 + lrow;
-#pragma unroll
-      for (int x = 0; x < Op::CPL; ++x) {
-        const int c = (g * Op::KG * ES) / 16 + lhalf * Op::CPL + x;
-        out[x] = *reinterpret_cast<const u32x4*>(s + row * 128 + ((c ^ O::kswz(row)) << 4));
-      }
-    } else if constexpr (ES == 2) {
+    int v;
+    if constexpr (ES == 2) {
       const int q = lane >> 4, sl = lane & 15;
       const int n = wbase + f * 32 + 16 * (q & 1) + 4 * (sl & 3);
-      uint32_t w[4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int k = g * 16 + 8 * (q >> 1) + 4 * t + (sl >> 2);
-        const uint8_t* a = s + k * O::RB + (((n >> 3) ^ O::mswz(k)) << 4) + ((n & 7) << 1);
-        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a);
-        const u32x2 d = __builtin_bit_cast(u32x2, v);
-        w[2 * t] = d[0];
-        w[2 * t + 1] = d[1];
-      }
-      out[0] = u32x4{w[0], w[1], w[2], w[3]};
+      const int k = 8 * (q >> 1) + (sl >> 2);
+      v = k * O::RB + (((n >> 3) ^ O::mswz(k)) << 4) + ((n & 7) << 1);
     } else if constexpr (ES == 1) {
       const int q = lane >> 4, sl = lane & 15;
       const int n = wbase + f * 32 + 16 * (q & 1) + 8 * (sl & 1);
-      uint32_t w[8];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int k = g * 64 + 32 * (q >> 1) + 8 * t + (sl >> 1);
-        const uint8_t* a = s + k * O::RB + (((n >> 4) ^ O::mswz(k)) << 4) + (n & 15);
-        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)a);
-        w[2 * t] = (uint32_t)v[0];
-        w[2 * t + 1] = (uint32_t)v[1];
-      }
-      out[0] = u32x4{w[0], w[1], w[2], w[3]};
-      out[1] = u32x4{w[4], w[5], w[6], w[7]};
+      const int k = 32 * (q >> 1) + (sl >> 1);
+      v = k * O::RB + (((n >> 4) ^ O::mswz(k)) << 4) + (n & 15);
     } else {
       const int n = wbase + f * 32 + lrow;
-      uint32_t w[4];
+      v = 4 * lhalf * O::RB + n * 4;
+    }
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+  // Fragment f of an operand for k-group g, from LDS stage bytes `stage` (uniform).
+  auto read_frag = [&](uint32_t stage, auto opnd, int wbase, int f, int g, const int* kb,
+                       const int* mb, Frag& out) {
+    using O = decltype(opnd);
+    const uint8_t* s = smem + stage + O::LDS_OFF;
+    if constexpr (!O::MN) {
+      const int par = ((wbase >> 5) + f) & 1;
+#pragma unroll
+      for (int x = 0; x < Op::CPL; ++x) {
+        const int off = (wbase + f * 32) * 128 + (kb[par] ^ (16 * (KGC * g + x)));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(s + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[4 * x + e] = v[e];
+      }
+    } else if constexpr (ES == 2) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint8_t* a = s + mb[f] + (g * 16 + 4 * t) * O::RB;
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a);
+        const u32x2 d = __builtin_bit_cast(u32x2, v);
+        out[2 * t] = d[0];
+        out[2 * t + 1] = d[1];
+      }
+    } else if constexpr (ES == 1) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int k = g * 8 + 4 * lhalf + t;
-        w[t] = *reinterpret_cast<const uint32_t*>(s + k * O::RB + (((n >> 2) ^ O::mswz(k)) << 4) + ((n & 3) << 2));
+        const uint8_t* a = s + mb[f] + (g * 64 + 8 * t) * O::RB;
+        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)a);
+        out[2 * t] = (uint32_t)v[0];
+        out[2 * t + 1] = (uint32_t)v[1];
       }
-      out[0] = u32x4{w[0], w[1], w[2], w[3]};
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        out[t] = *reinterpret_cast<const uint32_t*>(s + mb[f] + (g * 8 + t) * O::RB);
     }
   };
+  int kbA[2] = {0, 0}, kbB[2] = {0, 0}, mbA[C::FM], mbB[C::FN];
+  if constexpr (!OA::MN) {
+    kbA[0] = kbase(0);
+    kbA[1] = kbase(1);
+  } else {
+#pragma unroll
+    for (int f = 0; f < C::FM; ++f) mbA[f] = mbase(OA{}, wm * C::WTM, f);
+  }
+  if constexpr (!OB::MN) {
+    kbB[0] = kbase(0);
+    kbB[1] = kbase(1);
+  } else {
+#pragma unroll
+    for (int f = 0; f < C::FN; ++f) mbB[f] = mbase(OB{}, wn * C::WTN, f);
+  }
 
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -401,37 +450,67 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto compute = [&](int buf) {
-    const uint8_t* sA = smem + buf * C::STAGE_BYTES + OA::LDS_OFF;
-    const uint8_t* sB = smem + buf * C::STAGE_BYTES + OB::LDS_OFF;
-    u32x4 af[2][C::FM][Op::CPL], bf[2][C::FN][Op::CPL];
+  // Fragment schedules.  A tile is multiplied in G k-groups; in each, every wave issues the
+  // FM x FN multiplies of its accumulator grid.
+  //  * 16- and 32-bit inputs (GROUPED): all fragments of k-group g+1 are read while k-group g
+  //    is multiplied (two register sets, set g & 1).
+  //  * 8-bit inputs (streamed): the 64-cycle multiplies and twice-as-large fragments favour
+  //    fewer registers: the tile is walked in S = G * FM steps, step s = g * FM + i issuing the
+  //    FN multiplies of row i; the A fragment of step s+1 (slot (s+1) & 1) is read during step
+  //    s, and one set of B fragments is read at the start of each k-group.
+  // G, FM and S are even, so the register-set parities carry over from tile to tile.
+  constexpr bool GROUPED = Op::CPL == 1;
+  constexpr int AS = GROUPED ? C::FM : 1;   // A fragments per register set
+  constexpr int BS = GROUPED ? 2 : 1;       // B register sets
+  Frag af[2][AS], bf[BS][C::FN];
+  auto load_a = [&](int buf, int g, int i, Frag& dst) {
+    read_frag(buf * C::STAGE_BYTES, OA{}, wm * C::WTM, i, g, kbA, mbA, dst);
+  };
+  auto load_b = [&](int buf, int g, int set) {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) read_frag(sA, OA{}, wm * C::WTM, i, 0, af[0][i]);
+    for (int j = 0; j < C::FN; ++j)
+      read_frag(buf * C::STAGE_BYTES, OB{}, wn * C::WTN, j, g, kbB, mbB, bf[set][j]);
+  };
+  auto load_group = [&](int buf, int g, int set) {
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) read_frag(sB, OB{}, wn * C::WTN, j, 0, bf[0][j]);
+    for (int i = 0; i < C::FM; ++i) load_a(buf, g, i, af[set][i]);
+    load_b(buf, g, set);
+  };
+  // D = op(B)-fragment x op(A)-fragment: rows of D are n, columns are m, so each lane ends up
+  // holding 4 consecutive n of one m (vector stores along the C row).  With the 256 x 256 tile
+  // (128 accumulator registers, held in VGPRs) an empty asm after each multiply pins it in
+  // place: the multiplies touch no memory, so the compiler would otherwise sink them past the
+  // barrier and read every fragment of the tile up front, which costs the registers these
+  // schedules are built to save.  Smaller grids keep their accumulators in AccVGPRs, which a
+  // VGPR operand constraint would force out and back on every step, so they are not pinned.
+  constexpr bool PIN = C::FM * C::FN >= 8;
+  auto mma = [&](int i, const Frag& a, int bset) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int cur = g & 1;
-      if (g + 1 < G) {
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) read_frag(sA, OA{}, wm * C::WTM, i, g + 1, af[cur ^ 1][i]);
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) read_frag(sB, OB{}, wn * C::WTN, j, g + 1, bf[cur ^ 1][j]);
-      }
-      // D = op(B)-fragment x op(A)-fragment: rows of D are n, columns are m, so each lane ends
-      // up holding 4 consecutive n of one m (vector stores along the C row).
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) acc[i][j] = Op::run(bf[cur][j], af[cur][i], acc[i][j]);
+    for (int j = 0; j < C::FN; ++j) {
+      acc[i][j] = Op::run(bf[bset][j], a, acc[i][j]);
+      if constexpr (PIN) asm volatile("" : "+v"(acc[i][j]));
     }
   };
+  auto mma_group = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) mma(i, af[set][i], set);
+  };
+  constexpr int S = G * C::FM;
+  static_assert(G % 2 == 0 && S % 2 == 0, "register-set parities carry across tiles");
 
-  // Double-buffered K loop: the copies of tile kt+1 fly while tile kt is multiplied from
-  // LDS; one barrier per step separates "stage written" from "stage read" and "stage read"
-  // from "stage overwritten two steps later".
+  // Double-buffered K loop with one barrier per K tile.  The copies of tile kt+1 fly while tile
+  // kt is multiplied from LDS.  The barrier sits before the tile's last multiplies: by then every
+  // wave holds their fragments and has finished reading the stage, so right after the barrier
+  // the stage is refilled (tile kt+2) and the first fragments of tile kt+1 are read while the
+  // last multiplies of tile kt keep the matrix cores busy.
   const int KT = (p.K + C::BKE - 1) / C::BKE;
   const bool need_fix = (p.epi & (FIX_A | FIX_B)) != 0;
+  auto tile_boundary = [&](int kt) {
+    __builtin_amdgcn_s_waitcnt(0);  // tile kt+1 has landed (issued one tile earlier)
+    if (kt + 2 == KT && need_fix) fixup(kt + 1, (kt + 1) & 1);
+    __syncthreads();
+    if (kt + 2 < KT) issue(kt + 2, kt & 1);
+  };
   if (KT > 0) {
     issue(0, 0);
     if (KT == 1 && need_fix) {
@@ -441,15 +520,43 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
-    compute(kt & 1);
-    if (kt + 2 == KT && need_fix) {
-      __builtin_amdgcn_s_waitcnt(0);
-      fixup(kt + 1, (kt + 1) & 1);
+  if (KT > 1) issue(1, 1);
+  if constexpr (GROUPED) {
+    if (KT > 0) load_group(0, 0, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int buf = kt & 1;
+#pragma unroll
+      for (int g = 0; g + 1 < G; ++g) {
+        load_group(buf, g + 1, (g + 1) & 1);
+        mma_group(g & 1);
+      }
+      tile_boundary(kt);
+      if (kt + 1 < KT) load_group(buf ^ 1, 0, 0);
+      mma_group((G - 1) & 1);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  } else {
+    if (KT > 0) {
+      load_b(0, 0, 0);
+      load_a(0, 0, 0, af[0][0]);
+    }
+    for (int kt = 0; kt < KT; ++kt) {
+      const int buf = kt & 1;
+#pragma unroll
+      for (int st = 0; st < S; ++st) {
+        const int g = st / C::FM, i = st % C::FM;
+        if (i == 0 && g > 0) load_b(buf, g, 0);
+        if (st + 1 < S) {
+          load_a(buf, (st + 1) / C::FM, (st + 1) % C::FM, af[(st + 1) & 1][0]);
+          mma(i, af[st & 1][0], 0);
+        } else {
+          tile_boundary(kt);
+          if (kt + 1 < KT) load_a(buf ^ 1, 0, 0, af[0][0]);
+          mma(i, af[st & 1][0], 0);
+          // the single B set is still read by the last step: refill it only afterwards
+          if (kt + 1 < KT) load_b(buf ^ 1, 0, 0);
+        }
+      }
+    }
   }
 
   // Epilogue in registers, then one store per element.
@@ -486,7 +593,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
             for (int e = 0; e < 4; ++e) bj[e] = p.bias[n + e];
           }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = epilogue_value(acc[i][j][rg * 4 + e], alpha, beta, cin[e], bj[e], epi);
+          for (int e = 0; e < 4; ++e) v[e] = epilogue_value<C::CT>(acc[i][j][rg * 4 + e], alpha, beta, cin[e], bj[e], epi);
           if constexpr (C::CT == F32) {
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + idx) = float4{v[0], v[1], v[2], v[3]};
           } else {
@@ -503,7 +610,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
               const float cin = beta != 0.0f ? load_as_float<C::CT>(p.C, idx + e) : 0.0f;
               const float bj = (epi & EPI_BIAS) ? p.bias[n + e] : 0.0f;
               store_from_float<C::CT>(p.C, idx + e,
-                                      epilogue_value(acc[i][j][rg * 4 + e], alpha, beta, cin, bj, epi));
+                                      epilogue_value<C::CT>(acc[i][j][rg * 4 + e], alpha, beta, cin, bj, epi));
             }
           }
         }

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(TS * TS) void gemm_simt_kernel(GemmParams p, int tr
     const int64_t idx = (int64_t)row * p.ldc + col;
     const float cin = p.beta != 0.0f ? load_as_float<CT>(p.C, idx) : 0.0f;
     const float bj = (p.epi & EPI_BIAS) ? p.bias[col] : 0.0f;
-    store_from_float<CT>(p.C, idx, epilogue_value(acc, p.alpha, p.beta, cin, bj, p.epi));
+    store_from_float<CT>(p.C, idx, epilogue_value<CT>(acc, p.alpha, p.beta, cin, bj, p.epi));
   }
 }
 

@@ -223,7 +223,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300, help="timed steps (headline)")
-    ap.add_argument("--warmup", type=int, default=20, help="untimed warmup steps (headline)")
+    ap.add_argument("--warmup", type=int, default=2000,
+                    help="untimed warmup steps (headline; the default runs ~0.25 s so clocks settle)")
     ap.add_argument("--reps", type=int, default=300, help="timed reps per sweep cell")
     ap.add_argument("--no-sweeps", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")

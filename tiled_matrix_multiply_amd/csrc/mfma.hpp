@@ -527,6 +527,11 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
       const int buf = kt & 1;
 #pragma unroll
       for (int g = 0; g + 1 < G; ++g) {
+        // Ask the scheduler to interleave this k-group's multiplies with the next group's LDS
+        // reads (LLVM's MFMA / DS-read interleaving strategy 1).  At 4096^3 this is 4% faster
+        // while the clock holds (constant operands) and neutral on random operands, where the
+        // chip runs near 2.1 GHz.
+        __builtin_amdgcn_iglp_opt(1);
         load_group(buf, g + 1, (g + 1) & 1);
         mma_group(g & 1);
       }

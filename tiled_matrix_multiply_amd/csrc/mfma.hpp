@@ -30,6 +30,8 @@
 // XOR-swizzled LDS layout instead of padding, and an XCD-aware tile order.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace tgemm {
@@ -564,51 +566,88 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
     }
   }
 
-  // Epilogue in registers, then one store per element.
+  // Epilogue in registers.  Lane (lrow, lhalf) of accumulator (i, j) holds rows
+  // m = m0 + wm*WTM + 32 i + lrow and, in register group rg, the 4 consecutive columns
+  // n = n0 + wn*WTN + 32 j + 8 rg + 4 lhalf (+0..3).
   const bool full = (m0 + C::BM <= p.M) && (n0 + C::BN <= p.N);
   const float alpha = p.alpha, beta = p.beta;
   const uint32_t epi = p.epi & (EPI_BIAS | EPI_GELU);
+  const int mw = m0 + wm * C::WTM + lrow;
+  const int nw = n0 + wn * C::WTN + lhalf * 4;
+  if (full) {
+    // Interior tile: no masks.  The bias values of the lane's columns are fetched in one batch
+    // (a single wait), each row's C values (beta != 0) likewise, and the element loop is
+    // specialised on (beta != 0, GELU) so that it carries no branches: this loop runs on the
+    // vector ALUs after the last multiply, so every instruction in it is paid in full.
+    float bj[C::FN][4][4];
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int m = m0 + wm * C::WTM + i * 32 + lrow;
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
+    for (int j = 0; j < C::FN; ++j)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const int n = n0 + wn * C::WTN + j * 32 + rg * 8 + lhalf * 4;
-        const int64_t idx = (int64_t)m * p.ldc + n;
-        float v[4];
-        if (full) {
-          float cin[4] = {0.f, 0.f, 0.f, 0.f}, bj[4] = {0.f, 0.f, 0.f, 0.f};
-          if (beta != 0.0f) {
-            if constexpr (C::CT == F32) {
-              const float4 c4 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.C) + idx);
-              cin[0] = c4.x; cin[1] = c4.y; cin[2] = c4.z; cin[3] = c4.w;
-            } else {
-              const u32x2 c2 = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(p.C) + idx);
+        // four scalar loads (the bias need only be 4-byte aligned); they merge into one
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const uint32_t h = (c2[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-                cin[e] = (C::CT == F16) ? f16_bits_to_float(h) : bf16_bits_to_float(h);
+        for (int e = 0; e < 4; ++e) bj[j][rg][e] = (epi & EPI_BIAS) ? p.bias[nw + 32 * j + 8 * rg + e] : 0.0f;
+      }
+    auto store_tile = [&](auto has_beta, auto has_gelu) {
+      constexpr bool HB = decltype(has_beta)::value, HG = decltype(has_gelu)::value;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) {
+        const int64_t row = (int64_t)(mw + 32 * i) * p.ldc;
+        float cin[C::FN][4][4];
+        if constexpr (HB) {
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+              const int64_t idx = row + nw + 32 * j + 8 * rg;
+              if constexpr (C::CT == F32) {
+                const float4 c4 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.C) + idx);
+                cin[j][rg][0] = c4.x; cin[j][rg][1] = c4.y; cin[j][rg][2] = c4.z; cin[j][rg][3] = c4.w;
+              } else {
+                const u32x2 c2 = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(p.C) + idx);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const uint32_t h = (c2[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+                  cin[j][rg][e] = (C::CT == F16) ? f16_bits_to_float(h) : bf16_bits_to_float(h);
+                }
               }
             }
-          }
-          if (epi & EPI_BIAS) {
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) bj[e] = p.bias[n + e];
-          }
+        for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = epilogue_value<C::CT>(acc[i][j][rg * 4 + e], alpha, beta, cin[e], bj[e], epi);
-          if constexpr (C::CT == F32) {
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + idx) = float4{v[0], v[1], v[2], v[3]};
-          } else {
-            uint32_t h[4];
+          for (int rg = 0; rg < 4; ++rg) {
+            float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = (C::CT == F16) ? float_to_f16_bits(v[e]) : float_to_bf16_bits(v[e]);
-            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.C) + idx) =
-                u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+            for (int e = 0; e < 4; ++e) {
+              float x = fmaf(alpha, acc[i][j][rg * 4 + e], bj[j][rg][e]);
+              if constexpr (HB) x = fmaf(beta, cin[j][rg][e], x);
+              if constexpr (HG) x = gelu_out<C::CT>(x);
+              v[e] = x;
+            }
+            store4<C::CT>(p.C, row + nw + 32 * j + 8 * rg, v);
           }
-        } else if (m < p.M) {
+      }
+    };
+    if (beta != 0.0f) {
+      if (epi & EPI_GELU) store_tile(std::true_type{}, std::true_type{});
+      else store_tile(std::true_type{}, std::false_type{});
+    } else {
+      if (epi & EPI_GELU) store_tile(std::false_type{}, std::true_type{});
+      else store_tile(std::false_type{}, std::false_type{});
+    }
+  } else {
+    // Edge tile: per-element masks on both axes.
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      const int m = mw + 32 * i;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int n = nw + 32 * j + 8 * rg;
+          const int64_t idx = (int64_t)m * p.ldc + n;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             if (n + e < p.N) {
@@ -619,7 +658,6 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
             }
           }
         }
-      }
     }
   }
 }

@@ -58,6 +58,29 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, BUFFER_FLAGS};
 }
 
+// Wait until at most N of this wave's vector-memory loads are outstanding (gfx9 s_waitcnt
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Wait until at most n * NL loads are outstanding, for 0 <= n <= MAXN (n is uniform; the count
+// must be an immediate, so each possible n has its own wait).
+template <int NL, int MAXN>
+__device__ __forceinline__ void wait_tiles(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) {
+      wait_vmcnt<MAXN * NL>();
+      return;
+    }
+    wait_tiles<NL, MAXN - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 // 16 bytes per lane from the buffer at byte offset voffset straight into LDS at
 // lds_base + 16 * lane (lds_base is wave-uniform).  Written as inline assembly so that the
 // compiler does not treat the in-flight LDS writes as aliasing every LDS read that follows:
@@ -128,7 +151,14 @@ template <> struct MmaOp<E4M3> {
 
 // ----------------------------------------------------------------------- configuration --
 
-template <int DT_, int TILE_, int WM_, int WN_, bool A_MN_, bool B_MN_>
+// LDS stages (K tiles resident or in flight per operand) by tile size, from a sweep over
+// n = 512 .. 2048 (fp16, random operands): the 128 x 128 tile gains 12% at 2048 from a third
+// stage (its four waves cannot hide one copy's latency); the 64 x 64 tile loses from any more
+// (fewer workgroups fit a compute unit); the 256 x 256 tile fills 128 of the 160 KB with two.
+template <int TILE>
+constexpr int default_stages() { return TILE == 128 ? 3 : 2; }
+
+template <int DT_, int TILE_, int WM_, int WN_, bool A_MN_, bool B_MN_, int S_ = default_stages<TILE_>()>
 struct MfmaCfg {
   static constexpr int DT = DT_;
   static constexpr int CT = (DT_ == E4M3) ? BF16 : DT_;
@@ -139,8 +169,10 @@ struct MfmaCfg {
   static constexpr int ES = DTypeInfo<DT_>::bytes;
   static constexpr int BKE = 128 / ES;                 // K elements per staged tile (128 bytes)
   static constexpr bool A_MN = A_MN_, B_MN = B_MN_;    // operand stored contiguous along M/N
-  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;  // one staged K tile
+  static constexpr int S = S_;  // LDS buffers per operand: K tiles kt .. kt+S-1 are resident or in flight
+  static constexpr int LDS_BYTES = S * (A_BYTES + B_BYTES);
+  static_assert(S >= 2 && LDS_BYTES <= 160 * 1024, "LDS holds at most 160 KB");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is a whole number of 32x32 tiles");
 };
 
@@ -161,7 +193,8 @@ struct Operand {
   static constexpr int CPR = RB / 16;               // chunks per LDS row
   static constexpr int WLOADS = BX / 8;             // 1 KB wave-loads per tile (BX*128 bytes)
   static constexpr int PER_WAVE = WLOADS / C::NW;
-  static constexpr int LDS_OFF = IS_A ? 0 : C::A_BYTES;
+  static constexpr int LDS_OFF = IS_A ? 0 : C::S * C::A_BYTES;  // first buffer of the operand
+  static constexpr int BUF_BYTES = IS_A ? C::A_BYTES : C::B_BYTES;
   static_assert(WLOADS % C::NW == 0, "every wave issues the same number of loads");
   static_assert(!MN || (RB <= 1024 && 1024 % RB == 0), "whole k-rows per wave-load");
 
@@ -220,7 +253,7 @@ enum : uint32_t { FIX_A = 1u << 8, FIX_B = 1u << 9 };
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
   using Op = MmaOp<C::DT>;
   using OA = Operand<C, true>;
   using OB = Operand<C, false>;
@@ -262,43 +295,44 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
     voB[i] = (uint32_t)((int64_t)r * p.ldb * ES + c * 16);
   }
 
-  // Issue the direct copies of K tile kt into LDS stage buf.
-  auto issue = [&](int kt, int buf) {
+  // Issue the direct copies of K tile kt of A (into A buffer buf) or of B (into B buffer buf).
+  auto issue_a = [&](int kt, int buf) {
     const int k0 = kt * C::BKE;
-    uint8_t* sA = smem + buf * C::STAGE_BYTES + OA::LDS_OFF;
-    uint8_t* sB = smem + buf * C::STAGE_BYTES + OB::LDS_OFF;
-    const uint8_t* baseA;
-    uint32_t extA;
+    const uint8_t* base;
+    uint32_t ext;
     if constexpr (!OA::MN) {  // A stored M x K
-      baseA = Ag + ((int64_t)m0 * p.lda + k0) * ES;
-      extA = extent_bytes(p.M, p.K, p.lda, m0, k0, ES);
+      base = Ag + ((int64_t)m0 * p.lda + k0) * ES;
+      ext = extent_bytes(p.M, p.K, p.lda, m0, k0, ES);
     } else {                  // A stored K x M
-      baseA = Ag + ((int64_t)k0 * p.lda + m0) * ES;
-      extA = extent_bytes(p.K, p.M, p.lda, k0, m0, ES);
+      base = Ag + ((int64_t)k0 * p.lda + m0) * ES;
+      ext = extent_bytes(p.K, p.M, p.lda, k0, m0, ES);
     }
-    const uint8_t* baseB;
-    uint32_t extB;
+    const i32x4 r = make_rsrc(base, ext);
+    const uint32_t l = (uint32_t)reinterpret_cast<uintptr_t>(smem + OA::LDS_OFF + buf * C::A_BYTES) + wave_u * 1024;
+#pragma unroll
+    for (int i = 0; i < OA::PER_WAVE; ++i) buffer_load_lds16(r, l + C::NW * i * 1024, voA[i]);
+  };
+  auto issue_b = [&](int kt, int buf) {
+    const int k0 = kt * C::BKE;
+    const uint8_t* base;
+    uint32_t ext;
     if constexpr (OB::MN) {   // B stored K x N
-      baseB = Bg + ((int64_t)k0 * p.ldb + n0) * ES;
-      extB = extent_bytes(p.K, p.N, p.ldb, k0, n0, ES);
+      base = Bg + ((int64_t)k0 * p.ldb + n0) * ES;
+      ext = extent_bytes(p.K, p.N, p.ldb, k0, n0, ES);
     } else {                  // B stored N x K
-      baseB = Bg + ((int64_t)n0 * p.ldb + k0) * ES;
-      extB = extent_bytes(p.N, p.K, p.ldb, n0, k0, ES);
+      base = Bg + ((int64_t)n0 * p.ldb + k0) * ES;
+      ext = extent_bytes(p.N, p.K, p.ldb, n0, k0, ES);
     }
-    const i32x4 ra = make_rsrc(baseA, extA);
-    const i32x4 rb = make_rsrc(baseB, extB);
-    const uint32_t la = (uint32_t)reinterpret_cast<uintptr_t>(sA) + wave_u * 1024;
-    const uint32_t lb = (uint32_t)reinterpret_cast<uintptr_t>(sB) + wave_u * 1024;
+    const i32x4 r = make_rsrc(base, ext);
+    const uint32_t l = (uint32_t)reinterpret_cast<uintptr_t>(smem + OB::LDS_OFF + buf * C::B_BYTES) + wave_u * 1024;
 #pragma unroll
-    for (int i = 0; i < OA::PER_WAVE; ++i) buffer_load_lds16(ra, la + C::NW * i * 1024, voA[i]);
-#pragma unroll
-    for (int i = 0; i < OB::PER_WAVE; ++i) buffer_load_lds16(rb, lb + C::NW * i * 1024, voB[i]);
+    for (int i = 0; i < OB::PER_WAVE; ++i) buffer_load_lds16(r, l + C::NW * i * 1024, voB[i]);
   };
 
   // Last K tile: rewrite every chunk that reaches past K (K-contiguous operand) or past the
   // matrix edge in the final k-row (M/N-contiguous operand) with its valid elements and zeros.
-  // Runs after the tile's copies have landed (vmcnt 0) and before the barrier.
-  auto fixup = [&](int kt, int buf) {
+  // Runs after the tile's copies have landed and before the barrier.
+  auto fixup = [&](int kt, int abuf, int bbuf) {
     // An opaque copy of the lane index keeps the compiler from hoisting this rarely run code's
     // address arithmetic out of the K loop, where it would hold registers for every iteration.
     int lane = lane_id;
@@ -310,7 +344,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
         const int u = wave + C::NW * i;
         int r, c;
         OA::chunk_of(u, lane, r, c);
-        uint8_t* dst = smem + buf * C::STAGE_BYTES + OA::LDS_OFF + u * 1024 + lane * 16;
+        uint8_t* dst = smem + OA::LDS_OFF + abuf * C::A_BYTES + u * 1024 + lane * 16;
         if constexpr (!OA::MN) {
           const int gm = m0 + r, gk = k0 + c * OA::CE;
           if (gk + OA::CE > p.K) {
@@ -331,7 +365,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
         const int u = wave + C::NW * i;
         int r, c;
         OB::chunk_of(u, lane, r, c);
-        uint8_t* dst = smem + buf * C::STAGE_BYTES + OB::LDS_OFF + u * 1024 + lane * 16;
+        uint8_t* dst = smem + OB::LDS_OFF + bbuf * C::B_BYTES + u * 1024 + lane * 16;
         if constexpr (!OB::MN) {
           const int gn = n0 + r, gk = k0 + c * OB::CE;
           if (gk + OB::CE > p.K) {
@@ -391,11 +425,12 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
     asm volatile("" : "+v"(v));
     return v;
   };
-  // Fragment f of an operand for k-group g, from LDS stage bytes `stage` (uniform).
-  auto read_frag = [&](uint32_t stage, auto opnd, int wbase, int f, int g, const int* kb,
+  // Fragment f of an operand for k-group g, from the operand buffer at byte offset `boff`
+  // (uniform) past the operand's first buffer.
+  auto read_frag = [&](uint32_t boff, auto opnd, int wbase, int f, int g, const int* kb,
                        const int* mb, Frag& out) {
     using O = decltype(opnd);
-    const uint8_t* s = smem + stage + O::LDS_OFF;
+    const uint8_t* s = smem + O::LDS_OFF + boff;
     if constexpr (!O::MN) {
       const int par = ((wbase >> 5) + f) & 1;
 #pragma unroll
@@ -465,18 +500,18 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   constexpr int AS = GROUPED ? C::FM : 1;   // A fragments per register set
   constexpr int BS = GROUPED ? 2 : 1;       // B register sets
   Frag af[2][AS], bf[BS][C::FN];
-  auto load_a = [&](int buf, int g, int i, Frag& dst) {
-    read_frag(buf * C::STAGE_BYTES, OA{}, wm * C::WTM, i, g, kbA, mbA, dst);
+  auto load_a = [&](uint32_t aoff, int g, int i, Frag& dst) {
+    read_frag(aoff, OA{}, wm * C::WTM, i, g, kbA, mbA, dst);
   };
-  auto load_b = [&](int buf, int g, int set) {
+  auto load_b = [&](uint32_t boff, int g, int set) {
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
-      read_frag(buf * C::STAGE_BYTES, OB{}, wn * C::WTN, j, g, kbB, mbB, bf[set][j]);
+      read_frag(boff, OB{}, wn * C::WTN, j, g, kbB, mbB, bf[set][j]);
   };
-  auto load_group = [&](int buf, int g, int set) {
+  auto load_group = [&](uint32_t aoff, uint32_t boff, int g, int set) {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) load_a(buf, g, i, af[set][i]);
-    load_b(buf, g, set);
+    for (int i = 0; i < C::FM; ++i) load_a(aoff, g, i, af[set][i]);
+    load_b(boff, g, set);
   };
   // D = op(B)-fragment x op(A)-fragment: rows of D are n, columns are m, so each lane ends up
   // holding 4 consecutive n of one m (vector stores along the C row).  With the 256 x 256 tile
@@ -500,33 +535,41 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   constexpr int S = G * C::FM;
   static_assert(G % 2 == 0 && S % 2 == 0, "register-set parities carry across tiles");
 
-  // Double-buffered K loop with one barrier per K tile.  The copies of tile kt+1 fly while tile
-  // kt is multiplied from LDS.  The barrier sits before the tile's last multiplies: by then every
-  // wave holds their fragments and has finished reading the stage, so right after the barrier
-  // the stage is refilled (tile kt+2) and the first fragments of tile kt+1 are read while the
-  // last multiplies of tile kt keep the matrix cores busy.
+  // Multi-buffered K loop with one barrier per K tile.  While tile kt is multiplied, the copies
+  // of tiles kt+1 .. kt+S-1 are in flight.  The barrier sits before the tile's last multiplies:
+  // by then every wave holds their fragments and has finished reading tile kt's buffers, so
+  // right after the barrier those buffers are refilled (tile kt+S) and the first fragments of
+  // tile kt+1 are read while the last multiplies of tile kt keep the matrix cores busy.  A wave's
+  // copies land in the order they were issued, so "tile kt+1 has landed" is a bound on the
+  // number of its copies still outstanding (vmcnt): those of the tiles issued after it.
   const int KT = (p.K + C::BKE - 1) / C::BKE;
   const bool need_fix = (p.epi & (FIX_A | FIX_B)) != 0;
-  auto tile_boundary = [&](int kt) {
-    __builtin_amdgcn_s_waitcnt(0);  // tile kt+1 has landed (issued one tile earlier)
-    if (kt + 2 == KT && need_fix) fixup(kt + 1, (kt + 1) & 1);
-    __syncthreads();
-    if (kt + 2 < KT) issue(kt + 2, kt & 1);
+  constexpr int NL = OA::PER_WAVE + OB::PER_WAVE;  // copies per wave per K tile
+  auto issue = [&](int kt, int buf) {
+    issue_b(kt, buf);
+    issue_a(kt, buf);
   };
-  if (KT > 0) {
-    issue(0, 0);
-    if (KT == 1 && need_fix) {
-      __builtin_amdgcn_s_waitcnt(0);
-      fixup(0, 0);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
+  static_assert((C::S - 1) * NL < 64, "outstanding-copy counts fit the 6-bit vmcnt");
+  auto tile_boundary = [&](int kt, int abuf, int anext) {
+    // tiles kt+2 .. min(kt+S-1, KT-1) may stay in flight
+    wait_tiles<NL, C::S - 1>(min(C::S - 2, KT - 2 - kt));
+    if (kt + 2 == KT && need_fix) fixup(kt + 1, anext, anext);
+    __syncthreads();
+    if (kt + C::S < KT) issue(kt + C::S, abuf);  // into the buffers tile kt has released
+  };
+  // Prologue: copies of tiles 0 .. S-1, then wait for tile 0.
+#pragma unroll
+  for (int t = 0; t < C::S; ++t)
+    if (t < KT) issue(t, t);
+  wait_tiles<NL, C::S - 1>(min(C::S - 1, KT - 1));
+  if (KT == 1 && need_fix) fixup(0, 0, 0);
   __syncthreads();
-  if (KT > 1) issue(1, 1);
+  int abuf = 0;  // buffer of tile kt (kt % S)
   if constexpr (GROUPED) {
-    if (KT > 0) load_group(0, 0, 0);
+    if (KT > 0) load_group(0, 0, 0, 0);
     for (int kt = 0; kt < KT; ++kt) {
-      const int buf = kt & 1;
+      const uint32_t aoff = abuf * C::A_BYTES, boff = abuf * C::B_BYTES;
+      const int anext = abuf + 1 == C::S ? 0 : abuf + 1;
 #pragma unroll
       for (int g = 0; g + 1 < G; ++g) {
         // Ask the scheduler to interleave this k-group's multiplies with the next group's LDS
@@ -534,12 +577,13 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
         // while the clock holds (constant operands) and neutral on random operands, where the
         // chip runs near 2.1 GHz.
         __builtin_amdgcn_iglp_opt(1);
-        load_group(buf, g + 1, (g + 1) & 1);
+        load_group(aoff, boff, g + 1, (g + 1) & 1);
         mma_group(g & 1);
       }
-      tile_boundary(kt);
-      if (kt + 1 < KT) load_group(buf ^ 1, 0, 0);
+      tile_boundary(kt, abuf, anext);
+      if (kt + 1 < KT) load_group(anext * C::A_BYTES, anext * C::B_BYTES, 0, 0);
       mma_group((G - 1) & 1);
+      abuf = anext;
     }
   } else {
     if (KT > 0) {
@@ -547,22 +591,24 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
       load_a(0, 0, 0, af[0][0]);
     }
     for (int kt = 0; kt < KT; ++kt) {
-      const int buf = kt & 1;
+      const uint32_t aoff = abuf * C::A_BYTES, boff = abuf * C::B_BYTES;
+      const int anext = abuf + 1 == C::S ? 0 : abuf + 1;
 #pragma unroll
       for (int st = 0; st < S; ++st) {
         const int g = st / C::FM, i = st % C::FM;
-        if (i == 0 && g > 0) load_b(buf, g, 0);
+        if (i == 0 && g > 0) load_b(boff, g, 0);
         if (st + 1 < S) {
-          load_a(buf, (st + 1) / C::FM, (st + 1) % C::FM, af[(st + 1) & 1][0]);
+          load_a(aoff, (st + 1) / C::FM, (st + 1) % C::FM, af[(st + 1) & 1][0]);
           mma(i, af[st & 1][0], 0);
         } else {
-          tile_boundary(kt);
-          if (kt + 1 < KT) load_a(buf ^ 1, 0, 0, af[0][0]);
+          tile_boundary(kt, abuf, anext);
+          if (kt + 1 < KT) load_a(anext * C::A_BYTES, 0, 0, af[0][0]);
           mma(i, af[st & 1][0], 0);
           // the single B set is still read by the last step: refill it only afterwards
-          if (kt + 1 < KT) load_b(buf ^ 1, 0, 0);
+          if (kt + 1 < KT) load_b(anext * C::B_BYTES, 0, 0);
         }
       }
+      abuf = anext;
     }
   }
 

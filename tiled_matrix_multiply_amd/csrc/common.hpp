@@ -73,29 +73,27 @@ __device__ __forceinline__ void store_from_float(void* base, int64_t idx, float 
   else reinterpret_cast<uint16_t*>(base)[idx] = (uint16_t)float_to_bf16_bits(v);
 }
 
-// Four consecutive outputs at element idx (16-byte aligned for fp32, 8-byte for 16-bit types),
-// rounded to nearest even; bf16 pairs go through the packed conversion.
+// Four consecutive outputs, rounded to nearest even, written to LDS at dst (16-byte aligned for
+// fp32, 8-byte for 16-bit types).
 template <int CT>
-__device__ __forceinline__ void store4(void* base, int64_t idx, const float* v) {
+__device__ __forceinline__ void stage4(uint8_t* dst, const float* v) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
   if constexpr (CT == F32) {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx) = float4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<float4*>(dst) = float4{v[0], v[1], v[2], v[3]};
   } else if constexpr (CT == BF16) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t lo = __builtin_convertvector((f32x2_t{v[0], v[1]}), bf16x2_t);
     const bf16x2_t hi = __builtin_convertvector((f32x2_t{v[2], v[3]}), bf16x2_t);
-    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-    *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(base) + idx) =
-        u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
   } else {
-    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     uint32_t h[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) h[e] = float_to_f16_bits(v[e]);
-    *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(base) + idx) =
-        u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
   }
 }
+
 
 // ------------------------------------------------------------------------------ epilogue --
 

@@ -634,11 +634,25 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) bj[j][rg][e] = (epi & EPI_BIAS) ? p.bias[nw + 32 * j + 8 * rg + e] : 0.0f;
       }
+    // Output staging.  In the accumulator layout one store instruction would write 32 rows x
+    // 16 bytes, 32 partial cache lines that L2 merges one request at a time.  Instead each wave
+    // writes one row of accumulator tiles (32 x WTN outputs) into a private LDS region in that
+    // layout, reads it back as whole 16-byte granules along the rows and stores full lines.
+    // The K loop's buffers are free here: every wave has passed the last tile's barrier, after
+    // which LDS is not read, and no copy is in flight.  Granule g of staged row r sits at
+    // position g ^ (r % GPR), which keeps the row-wise read-back free of bank conflicts.
+    constexpr int OES = C::CT == F32 ? 4 : 2;           // output element bytes
+    constexpr int ROWB = C::WTN * OES, GPR = ROWB / 16;  // staged row bytes, granules per row
+    constexpr int CHUNK = 32 * ROWB;                      // one wave's region
+    static_assert(C::NW * CHUNK <= C::LDS_BYTES, "output staging fits the K loop's LDS");
+    uint8_t* const ostage = smem + wave_u * CHUNK;
+    const int m_w0 = m0 + wm * C::WTM, n_w0 = n0 + wn * C::WTN;
+    typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
     auto store_tile = [&](auto has_beta, auto has_gelu) {
       constexpr bool HB = decltype(has_beta)::value, HG = decltype(has_gelu)::value;
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
-        const int64_t row = (int64_t)(mw + 32 * i) * p.ldc;
+        const int64_t row = (int64_t)(mw + 32 * i) * p.ldc;  // this lane's row (beta != 0 loads)
         float cin[C::FN][4][4];
         if constexpr (HB) {
 #pragma unroll
@@ -671,8 +685,18 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
               if constexpr (HG) x = gelu_out<C::CT>(x);
               v[e] = x;
             }
-            store4<C::CT>(p.C, row + nw + 32 * j + 8 * rg, v);
+            const int gb = (32 * j + 8 * rg + 4 * lhalf) * OES;  // byte offset in the row
+            stage4<C::CT>(ostage + lrow * ROWB + 16 * ((gb >> 4) ^ (lrow % GPR)) + (gb & 15), v);
           }
+        // read back whole granules: linear granule L = 64 q + lane is row L / GPR, granule L % GPR
+#pragma unroll
+        for (int q = 0; q < GPR / 2; ++q) {
+          const int L = 64 * q + lane, r = L / GPR, g = L % GPR;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(ostage + r * ROWB + 16 * (g ^ (r % GPR)));
+          uint8_t* dst = reinterpret_cast<uint8_t*>(p.C) +
+                         ((int64_t)(m_w0 + 32 * i + r) * p.ldc + n_w0 + g * (16 / OES)) * OES;
+          *reinterpret_cast<u32x4_a4*>(dst) = val;
+        }
       }
     };
     if (beta != 0.0f) {

@@ -26,8 +26,10 @@
 // rows (columns) that are never stored.  The one case that needs care is K: in the last K
 // tile, chunks that reach past K are rewritten in LDS with zeros beyond K.
 // What differs from the pages' Metal kernels: 32x32 MFMA tiles instead of 8x8 simdgroup
-// fragments, a double-buffered K loop with a single barrier per step instead of two, an
-// XOR-swizzled LDS layout instead of padding, and an XCD-aware tile order.
+// fragments, a multi-buffered K loop (2 or 3 LDS stages) with a single barrier per step
+// instead of two, an XOR-swizzled LDS layout instead of padding, an XCD-aware tile order, and
+// interior-tile stores staged per wave through LDS (the pages' Cs buffer) so that every store
+// instruction writes whole cache lines.
 #pragma once
 
 #include <type_traits>

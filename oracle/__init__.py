@@ -9,7 +9,8 @@ the passages of the pages it follows.
 Parity pins (tests/test_oracle.py): exact brute force with fractions.Fraction on every shape in
 {1..4}^3, identity and permutation matrices, rank-1 closed forms, alpha/beta linearity,
 A*B == (B^T A^T)^T, an exhaustive OCP E4M3 table, bf16 ties-to-even, closed-form GELU values, and
-a numpy float64 matmul cross-check.
+a numpy float64 matmul cross-check, exhaustive OCP E5M2 / E2M1 / E8M0 tables, and exact
+block-scaled (MX) brute force.
 """
 from __future__ import annotations
 
@@ -22,7 +23,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
-TYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
+TYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3, "e5m2": 4, "e2m1": 5}
 EPI_BIAS = 1
 EPI_GELU = 2
 
@@ -54,6 +55,13 @@ def lib():
         L.oracle_gemm_rows.restype = _int
         L.oracle_gemm_points.argtypes = _PROBLEM + [_i64, _vp, _vp, _vp, _vp]
         L.oracle_gemm_points.restype = _int
+        _MX = [_vp, _i64, _vp, _i64]
+        L.oracle_decode_e8m0.argtypes = [_vp, _i64, _vp]
+        L.oracle_decode_e8m0.restype = _int
+        L.oracle_gemm_mx.argtypes = _PROBLEM + _MX + [_vp, _vp]
+        L.oracle_gemm_mx.restype = _int
+        L.oracle_gemm_mx_points.argtypes = _PROBLEM + _MX + [_i64, _vp, _vp, _vp, _vp]
+        L.oracle_gemm_mx_points.restype = _int
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = _int
         _lib = L
@@ -65,13 +73,23 @@ def _ptr(a: Optional[np.ndarray]):
 
 
 def decode(dtype: str, stored: np.ndarray) -> np.ndarray:
-    """Decode stored words/bytes of `dtype` to float64 with the oracle's own decoders."""
+    """Decode stored words/bytes of `dtype` to float64 with the oracle's own decoders (E2M1:
+    two elements per byte along the last axis, low nibble first)."""
     a = np.ascontiguousarray(stored)
-    n = a.size
-    out = np.empty(a.shape, dtype=np.float64)
+    n = a.size * (2 if dtype == "e2m1" else 1)
+    shape = a.shape[:-1] + (a.shape[-1] * 2,) if dtype == "e2m1" else a.shape
+    out = np.empty(shape, dtype=np.float64)
     rc = lib().oracle_decode(TYPE_CODE[dtype], _ptr(a), n, _ptr(out))
     if rc != 0:
         raise ValueError(f"oracle_decode({dtype}) failed: {rc}")
+    return out
+
+
+def decode_e8m0(stored: np.ndarray) -> np.ndarray:
+    """Decode E8M0 block-scale bytes to float64 (2^(e-127), NaN for 255)."""
+    a = np.ascontiguousarray(stored, dtype=np.uint8)
+    out = np.empty(a.shape, dtype=np.float64)
+    lib().oracle_decode_e8m0(_ptr(a), a.size, _ptr(out))
     return out
 
 
@@ -98,6 +116,13 @@ def _problem_args(p):
                        p.epilogue, bias)
 
 
+def _mx_args(p):
+    """(keep, args) for the block scales of an MX problem (fields sa_blk, sb_blk)."""
+    sa = np.ascontiguousarray(p.sa_blk, dtype=np.uint8)
+    sb = np.ascontiguousarray(p.sb_blk, dtype=np.uint8)
+    return (sa, sb), (_ptr(sa), sa.shape[1], _ptr(sb), sb.shape[1])
+
+
 def gemm(p) -> Tuple[np.ndarray, np.ndarray]:
     """Full reference (Cref, D), each M x N float64, for a problem with the fields of
     workloads.Problem (M, N, K, trans_a, trans_b, alpha, beta, a_type, b_type, c_type,
@@ -105,7 +130,12 @@ def gemm(p) -> Tuple[np.ndarray, np.ndarray]:
     keep, args = _problem_args(p)
     Cref = np.empty((p.M, p.N), dtype=np.float64)
     D = np.empty((p.M, p.N), dtype=np.float64)
-    rc = lib().oracle_gemm(*args, _ptr(Cref), _ptr(D))
+    if getattr(p, "sa_blk", None) is not None:
+        keep2, mx = _mx_args(p)
+        rc = lib().oracle_gemm_mx(*args, *mx, _ptr(Cref), _ptr(D))
+        del keep2
+    else:
+        rc = lib().oracle_gemm(*args, _ptr(Cref), _ptr(D))
     del keep
     if rc != 0:
         raise ValueError(f"oracle_gemm failed: {rc}")
@@ -149,7 +179,13 @@ def gemm_points(p, rows: np.ndarray, cols: np.ndarray) -> Tuple[np.ndarray, np.n
     c = np.ascontiguousarray(cols, dtype=np.int64)
     Cref = np.empty(r.size, dtype=np.float64)
     D = np.empty(r.size, dtype=np.float64)
-    rc = lib().oracle_gemm_points(*args, r.size, _ptr(r), _ptr(c), _ptr(Cref), _ptr(D))
+    if getattr(p, "sa_blk", None) is not None:
+        keep2, mx = _mx_args(p)
+        rc = lib().oracle_gemm_mx_points(*args, *mx, r.size, _ptr(r), _ptr(c), _ptr(Cref),
+                                         _ptr(D))
+        del keep2
+    else:
+        rc = lib().oracle_gemm_points(*args, r.size, _ptr(r), _ptr(c), _ptr(Cref), _ptr(D))
     del keep
     if rc != 0:
         raise ValueError(f"oracle_gemm_points failed: {rc}")

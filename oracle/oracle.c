@@ -19,8 +19,15 @@
  *   t      = alpha*(sa*sb)*S + (beta != 0 ? beta*C_in(i,j) : 0) + (BIAS ? bias[j] : 0)
  *   Cref   = GELU ? 0.5*t*erfc(-t/sqrt(2)) : t          double, libm erfc
  *
- * Every product of two decoded inputs is exact in double (at most 24+24 significant bits), so
- * the only roundings are the k-ordered sums and the epilogue, each at 2^-53.
+ * Block-scaled (OCP microscaling, "MX") inputs: each run of 32 consecutive k of a row of op(A)
+ * and of a column of op(B) shares one E8M0 scale 2^(e - 127) (e = 255 is NaN), so
+ *   a(i,k) = dec(A ...) * 2^(sa[i*ldsa + k/32] - 127),  b(k,j) = dec(B ...) * 2^(sb[j*ldsb + k/32] - 127)
+ * with the per-tensor scales then 1.  This is the plain reading of the MX formats that
+ * "Rigel" (arXiv 2606.12765) lists next to fp8 (section 4, the block-scaled MXFP4 rows).
+ *
+ * Every product of two decoded inputs is exact in double (at most 24+24 significant bits; a
+ * power-of-two block scale only moves the exponent, and 2^(+-127) products stay inside the
+ * double range), so the only roundings are the k-ordered sums and the epilogue, each at 2^-53.
  * Build: gcc -O3 -fopenmp -ffp-contract=off (no fast-math: no reassociation, no FMA).
  */
 #include <math.h>
@@ -29,15 +36,18 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_E4M3 = 3 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_E4M3 = 3, OR_E5M2 = 4, OR_E2M1 = 5 };
 enum { OR_EPI_BIAS = 1u, OR_EPI_GELU = 2u };
 
-static int esize_of(int t) {
+/* Storage bits per element (E2M1 packs two elements per byte). */
+static int ebits_of(int t) {
   switch (t) {
-    case OR_F32: return 4;
-    case OR_F16: return 2;
-    case OR_BF16: return 2;
-    case OR_E4M3: return 1;
+    case OR_F32: return 32;
+    case OR_F16: return 16;
+    case OR_BF16: return 16;
+    case OR_E4M3: return 8;
+    case OR_E5M2: return 8;
+    case OR_E2M1: return 4;
     default: return 0;
   }
 }
@@ -71,6 +81,28 @@ static double dec_e4m3(uint8_t q) {
   return s ? -v : v;
 }
 
+/* OCP 8-bit E5M2: 1 sign, 5 exponent (bias 15), 2 mantissa bits, IEEE-style: exponent 31 is
+ * infinity (mantissa 0) or NaN, largest finite 57344, subnormals m * 2^-16. */
+static double dec_e5m2(uint8_t q) {
+  int s = q >> 7, e = (q >> 2) & 31, m = q & 3;
+  double v;
+  if (e == 31) v = m ? NAN : INFINITY;
+  else if (e == 0) v = ldexp((double)m, -16);
+  else v = ldexp((double)(4 + m), e - 17);
+  return s ? -v : v;
+}
+
+/* OCP 4-bit E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit, no infinities or NaN:
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (exponent 0 is the subnormal m * 2^-1). */
+static double dec_e2m1(uint8_t q) {
+  int s = (q >> 3) & 1, e = (q >> 1) & 3, m = q & 1;
+  double v = (e == 0) ? 0.5 * m : ldexp((double)(2 + m), e - 2);
+  return s ? -v : v;
+}
+
+/* OCP E8M0 block scale: 2^(e - 127); e = 255 is NaN. */
+static double dec_e8m0(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
 static double dec_f32(const void* p) {
   float f;
   memcpy(&f, p, 4);
@@ -83,13 +115,23 @@ static double dec_one(int t, const uint8_t* base, int64_t idx) {
     case OR_F16: { uint16_t h; memcpy(&h, base + 2 * idx, 2); return dec_f16(h); }
     case OR_BF16: { uint16_t h; memcpy(&h, base + 2 * idx, 2); return dec_bf16(h); }
     case OR_E4M3: return dec_e4m3(base[idx]);
+    case OR_E5M2: return dec_e5m2(base[idx]);
+    /* element idx sits in byte idx/2: the low nibble for even idx, the high one for odd */
+    case OR_E2M1: return dec_e2m1((uint8_t)((base[idx >> 1] >> (4 * (idx & 1))) & 15));
     default: return NAN;
   }
 }
 
+/* Decode n E8M0 scale bytes to doubles. */
+int oracle_decode_e8m0(const void* src, int64_t n, double* dst) {
+  const uint8_t* p = (const uint8_t*)src;
+  for (int64_t i = 0; i < n; ++i) dst[i] = dec_e8m0(p[i]);
+  return 0;
+}
+
 /* Decode n consecutive stored values of type t into doubles. Returns 0, or -1 on bad type. */
 int oracle_decode(int t, const void* src, int64_t n, double* dst) {
-  if (esize_of(t) == 0) return -1;
+  if (ebits_of(t) == 0) return -1;
   const uint8_t* p = (const uint8_t*)src;
   for (int64_t i = 0; i < n; ++i) dst[i] = dec_one(t, p, i);
   return 0;
@@ -109,15 +151,31 @@ typedef struct {
   int at, bt, ct;
   unsigned epi;
   const float* bias;
+  const uint8_t *sa_blk, *sb_blk; /* E8M0 block scales, or NULL */
+  int64_t ldsa, ldsb;
 } problem_t;
 
 static int check(const problem_t* p) {
   if (p->M < 0 || p->N < 0 || p->K < 0) return -1;
-  if (!esize_of(p->at) || !esize_of(p->bt) || !esize_of(p->ct)) return -1;
+  if (!ebits_of(p->at) || !ebits_of(p->bt) || !ebits_of(p->ct) || p->ct == OR_E2M1) return -1;
+  if ((p->sa_blk != NULL) != (p->sb_blk != NULL)) return -1;
+  if (p->sa_blk && (p->K % 32 != 0 || p->ldsa < p->K / 32 || p->ldsb < p->K / 32)) return -1;
   if (p->K > 0 && (!p->A || !p->B)) return -1;
   if (p->beta != 0.0 && !p->Cin) return -1;
   if ((p->epi & OR_EPI_BIAS) && !p->bias) return -1;
   return 0;
+}
+
+/* op(A)[i][k] and op(B)[k][j], decoded exactly, block scale applied. */
+static double opA(const problem_t* p, int64_t i, int64_t k) {
+  double a = dec_one(p->at, p->A, p->transA ? k * p->lda + i : i * p->lda + k);
+  if (p->sa_blk) a *= dec_e8m0(p->sa_blk[i * p->ldsa + k / 32]);
+  return a;
+}
+static double opB(const problem_t* p, int64_t k, int64_t j) {
+  double b = dec_one(p->bt, p->B, p->transB ? j * p->ldb + k : k * p->ldb + j);
+  if (p->sb_blk) b *= dec_e8m0(p->sb_blk[j * p->ldsb + k / 32]);
+  return b;
 }
 
 /* op(B) as a K x N row-major double matrix. */
@@ -128,7 +186,7 @@ static double* decode_opB(const problem_t* p) {
 #pragma omp parallel for schedule(static)
   for (int64_t k = 0; k < p->K; ++k)
     for (int64_t j = 0; j < p->N; ++j)
-      b[k * p->N + j] = dec_one(p->bt, p->B, p->transB ? j * p->ldb + k : k * p->ldb + j);
+      b[k * p->N + j] = opB(p, k, j);
   return b;
 }
 
@@ -161,7 +219,7 @@ static int run_rows(const problem_t* p, int64_t row0, int64_t nrows, double* Cre
         const int64_t i = row0 + r;
         for (int64_t j = 0; j < p->N; ++j) { s[j] = 0.0; d[j] = 0.0; }
         for (int64_t k = 0; k < p->K; ++k) {
-          const double a = dec_one(p->at, p->A, p->transA ? k * p->lda + i : i * p->lda + k);
+          const double a = opA(p, i, k);
           const double* brow = b + k * p->N;
           for (int64_t j = 0; j < p->N; ++j) {
             const double prod = a * brow[j];
@@ -191,7 +249,14 @@ static int run_rows(const problem_t* p, int64_t row0, int64_t nrows, double* Cre
 #define FILL_PROBLEM(p)                                                                     \
   problem_t p = {M, N, K, transA, transB, alpha, scale_a, scale_b, beta,                    \
                  (const uint8_t*)A, (const uint8_t*)B, (const uint8_t*)Cin, lda, ldb, ldc,  \
-                 a_type, b_type, c_type, epilogue, bias}
+                 a_type, b_type, c_type, epilogue, bias, NULL, NULL, 0, 0}
+
+#define MX_ARGS const void *sa_blk, int64_t ldsa, const void *sb_blk, int64_t ldsb
+#define FILL_MX(p)                          \
+  p.sa_blk = (const uint8_t*)sa_blk;        \
+  p.sb_blk = (const uint8_t*)sb_blk;        \
+  p.ldsa = ldsa;                            \
+  p.ldsb = ldsb
 
 /* Full M x N result: Cref and D are caller-owned M*N double arrays.  Returns 0 on success. */
 int oracle_gemm(PROBLEM_ARGS, double* Cref, double* D) {
@@ -206,27 +271,45 @@ int oracle_gemm_rows(PROBLEM_ARGS, int64_t row0, int64_t nrows, double* Cref, do
 }
 
 /* Selected entries (rows[t], cols[t]), t < npts, each computed on its own with k ascending. */
-int oracle_gemm_points(PROBLEM_ARGS, int64_t npts, const int64_t* rows, const int64_t* cols,
-                       double* Cref, double* D) {
-  FILL_PROBLEM(p);
-  if (check(&p)) return -1;
+static int run_points(const problem_t* p, int64_t npts, const int64_t* rows, const int64_t* cols,
+                      double* Cref, double* D) {
+  if (check(p)) return -1;
   for (int64_t t = 0; t < npts; ++t)
-    if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N) return -1;
+    if (rows[t] < 0 || rows[t] >= p->M || cols[t] < 0 || cols[t] >= p->N) return -1;
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t t = 0; t < npts; ++t) {
     const int64_t i = rows[t], j = cols[t];
     double s = 0.0, d = 0.0;
-    for (int64_t k = 0; k < K; ++k) {
-      const double a = dec_one(p.at, p.A, transA ? k * lda + i : i * lda + k);
-      const double b = dec_one(p.bt, p.B, transB ? j * ldb + k : k * ldb + j);
-      const double prod = a * b;
+    for (int64_t k = 0; k < p->K; ++k) {
+      const double prod = opA(p, i, k) * opB(p, k, j);
       s += prod;
       d += fabs(prod);
     }
-    Cref[t] = apply_epilogue(&p, i, j, s);
-    D[t] = (p.sa * p.sb) * d;
+    Cref[t] = apply_epilogue(p, i, j, s);
+    D[t] = (p->sa * p->sb) * d;
   }
   return 0;
+}
+
+int oracle_gemm_points(PROBLEM_ARGS, int64_t npts, const int64_t* rows, const int64_t* cols,
+                       double* Cref, double* D) {
+  FILL_PROBLEM(p);
+  return run_points(&p, npts, rows, cols, Cref, D);
+}
+
+/* Block-scaled variants: the same with E8M0 scales sa_blk (row i of op(A), block k/32 at
+ * sa_blk[i*ldsa + k/32]) and sb_blk (column j of op(B) at sb_blk[j*ldsb + k/32]); K % 32 == 0. */
+int oracle_gemm_mx(PROBLEM_ARGS, MX_ARGS, double* Cref, double* D) {
+  FILL_PROBLEM(p);
+  FILL_MX(p);
+  return run_rows(&p, 0, M, Cref, D);
+}
+
+int oracle_gemm_mx_points(PROBLEM_ARGS, MX_ARGS, int64_t npts, const int64_t* rows,
+                          const int64_t* cols, double* Cref, double* D) {
+  FILL_PROBLEM(p);
+  FILL_MX(p);
+  return run_points(&p, npts, rows, cols, Cref, D);
 }
 
 /* Number of OpenMP threads a parallel region of the oracle uses. */

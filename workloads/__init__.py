@@ -15,6 +15,9 @@ are fixed here):
   * bf16 n^3 + bias + erf-GELU, A ~ N(0,1), B ~ N(0,1/K), bias ~ N(0, 0.1^2) fp32, seed 3.
   * fp8-E4M3 4096^3 with per-tensor scales (max|x| -> 448) and its bf16 twin, A,B ~ N(0,1),
     seed 4, bf16 output.
+  * fp8-E5M2 4096^3 (per-tensor scale max|x| -> 57344), and the OCP microscaling (MX) formats
+    MXFP8 (E4M3 elements) and MXFP4 (E2M1 elements) at 4096^3: one E8M0 scale per 32
+    consecutive k of each row of op(A) and each column of op(B), A,B ~ N(0,1), seed 5.
 Draw order is always: logical A (M x K, row-major), then logical B (K x N), then C_in (M x N),
 then bias (N).  A transposed operand is the same logical matrix stored as its transpose.
 """
@@ -27,17 +30,21 @@ from typing import Optional
 
 import numpy as np
 
-DTYPES = ("f32", "f16", "bf16", "e4m3")
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
-ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
-STORAGE = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8}
+DTYPES = ("f32", "f16", "bf16", "e4m3", "e5m2", "e2m1")
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3, "e5m2": 4, "e2m1": 5}
+ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1, "e2m1": 0.5}
+STORAGE = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8,
+           "e5m2": np.uint8, "e2m1": np.uint8}
+FP8 = ("e4m3", "e5m2")
+MX_BLOCK = 32  # elements per E8M0 block scale (OCP microscaling)
 
 EPI_NONE = 0
 EPI_BIAS = 1
 EPI_GELU = 2
 
 # Output type for each supported input type.
-OUT_TYPE = {"f32": "f32", "f16": "f16", "bf16": "bf16", "e4m3": "bf16"}
+OUT_TYPE = {"f32": "f32", "f16": "f16", "bf16": "bf16", "e4m3": "bf16", "e5m2": "bf16",
+            "e2m1": "bf16"}
 
 
 # --------------------------------------------------------------------------------------------
@@ -104,8 +111,99 @@ def e4m3_scale(x: np.ndarray) -> np.float32:
     return np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
 
 
+def _nearest_code(y: np.ndarray, mags: np.ndarray, sign_shift: int) -> np.ndarray:
+    """Nearest code among increasing non-negative magnitudes `mags` (code = index), ties to
+    the even code, saturating at the largest; the sign goes to bit `sign_shift`."""
+    mag = np.minimum(np.abs(y), mags[-1])
+    top = mags.size - 1
+    hi = np.clip(np.searchsorted(mags, mag, side="left"), 0, top)
+    lo = np.clip(hi - 1, 0, top)
+    d_hi = mags[hi] - mag
+    d_lo = mag - mags[lo]
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & ((lo & 1) == 0))
+    code = np.where(pick_lo, lo, hi).astype(np.uint8)
+    return code | (np.signbit(y).astype(np.uint8) << sign_shift)
+
+
+def _e5m2_magnitudes() -> np.ndarray:
+    """Magnitudes of the 124 finite non-negative OCP E5M2 codes 0x00..0x7B, increasing."""
+    vals = np.empty(124, dtype=np.float64)
+    for code in range(124):
+        e, m = code >> 2, code & 3
+        vals[code] = m * 2.0 ** -16 if e == 0 else (4 + m) * 2.0 ** (e - 17)
+    return vals
+
+
+_E5M2_MAG = _e5m2_magnitudes()
+E5M2_MAX = 57344.0
+
+
+def to_e5m2_bits(y: np.ndarray) -> np.ndarray:
+    """float64 -> OCP E5M2 bytes: nearest code, ties to even, saturating at +-57344; NaN -> 0x7F."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    code = _nearest_code(y, _E5M2_MAG, 7)
+    code[np.isnan(y)] = 0x7F
+    return code
+
+
+# OCP E2M1 magnitudes for codes 0..7 (exponent bias 1, one mantissa bit; no inf or NaN).
+_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+E2M1_MAX = 6.0
+
+
+def to_e2m1_codes(y: np.ndarray) -> np.ndarray:
+    """float64 -> OCP E2M1 4-bit codes (one per uint8): nearest, ties to even, saturating at
+    +-6.  NaN has no code; it must not occur."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    if np.isnan(y).any():
+        raise ValueError("E2M1 has no NaN")
+    return _nearest_code(y, _E2M1_MAG, 3)
+
+
+def pack_e2m1(codes: np.ndarray) -> np.ndarray:
+    """Pack 4-bit codes two per byte along the last axis: element 2i in the low nibble of
+    byte i, element 2i+1 in the high nibble.  The last axis must be even."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    if c.shape[-1] % 2:
+        raise ValueError("E2M1 rows must hold an even number of elements")
+    return np.ascontiguousarray((c[..., 0::2] & 15) | ((c[..., 1::2] & 15) << 4))
+
+
+# Largest binade of each MX element format (2^emax <= max finite < 2^(emax+1)).
+MX_EMAX = {"e4m3": 8, "e5m2": 15, "e2m1": 2}
+
+
+def mx_quantize(x: np.ndarray, elem: str):
+    """OCP microscaling quantisation of a rows x K float64 matrix (K a multiple of 32): every
+    run of 32 consecutive values in a row shares the E8M0 scale 2^X with
+    X = floor(log2(max|v|)) - emax(elem) (X clamped to [-127, 127]; an all-zero block takes
+    X = 0); the elements are v / 2^X rounded to `elem`, saturating.
+    Returns (element storage, rows x K (x K/2 packed for e2m1), uint8 scales rows x K/32)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    rows, K = x.shape
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    blk = x.reshape(rows, K // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(blk), axis=2)
+    X = np.zeros_like(amax, dtype=np.int64)
+    nz = amax > 0
+    X[nz] = np.floor(np.log2(amax[nz])).astype(np.int64) - MX_EMAX[elem]
+    X = np.clip(X, -127, 127)
+    scaled = (blk / np.ldexp(1.0, X)[..., None]).reshape(rows, K)
+    if elem == "e4m3":
+        q = to_e4m3_bits(scaled)
+    elif elem == "e5m2":
+        q = to_e5m2_bits(scaled)
+    elif elem == "e2m1":
+        q = pack_e2m1(to_e2m1_codes(scaled))
+    else:
+        raise ValueError(f"no MX element format {elem!r}")
+    return q, (X + 127).astype(np.uint8)
+
+
 def encode(x: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
-    """Encode float64 values to the storage of `dtype` (E4M3 encodes x / scale)."""
+    """Encode float64 values to the storage of `dtype` (fp8 types encode x / scale; E2M1 packs
+    two codes per byte along the last axis)."""
     if dtype == "f32":
         return to_f32(x)
     if dtype == "f16":
@@ -114,7 +212,18 @@ def encode(x: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
         return to_bf16_bits(x)
     if dtype == "e4m3":
         return to_e4m3_bits(np.asarray(x, dtype=np.float64) / float(scale))
+    if dtype == "e5m2":
+        return to_e5m2_bits(np.asarray(x, dtype=np.float64) / float(scale))
+    if dtype == "e2m1":
+        return pack_e2m1(to_e2m1_codes(np.asarray(x, dtype=np.float64) / float(scale)))
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def fp8_scale(x: np.ndarray, dtype: str) -> np.float32:
+    """Per-tensor dequantisation scale: fp32(max|x| / max finite of `dtype`), 1 if all zero."""
+    top = {"e4m3": E4M3_MAX, "e5m2": E5M2_MAX, "e2m1": E2M1_MAX}[dtype]
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    return np.float32(amax / top) if amax > 0 else np.float32(1.0)
 
 
 # --------------------------------------------------------------------------------------------
@@ -148,6 +257,22 @@ class Problem:
     scale_a: float = 1.0
     scale_b: float = 1.0
     recipe: dict = dataclasses.field(default_factory=dict)
+    # OCP MX block scales (E8M0 bytes): sa_blk[i, k // 32] for row i of op(A), sb_blk[j, k // 32]
+    # for column j of op(B); None for per-tensor scaling.
+    sa_blk: Optional[np.ndarray] = None
+    sb_blk: Optional[np.ndarray] = None
+
+    @property
+    def mx(self) -> bool:
+        return self.sa_blk is not None
+
+    @property
+    def ldsa(self) -> int:
+        return self.sa_blk.shape[1] if self.sa_blk is not None else 0
+
+    @property
+    def ldsb(self) -> int:
+        return self.sb_blk.shape[1] if self.sb_blk is not None else 0
 
     @property
     def lda(self) -> int:
@@ -184,14 +309,17 @@ def _draw(rng: np.random.Generator, shape, dist) -> np.ndarray:
 
 
 def make_problem(M: int, N: int, K: int, *, a_type: str = "f32", c_type: Optional[str] = None,
-                 trans_a: bool = False, trans_b: bool = False, alpha: float = 1.0,
-                 beta: float = 0.0, epilogue: int = EPI_NONE, seed: int = 0,
+                 b_type: Optional[str] = None, trans_a: bool = False, trans_b: bool = False,
+                 alpha: float = 1.0, beta: float = 0.0, epilogue: int = EPI_NONE, seed: int = 0,
                  dist_a=("uniform", (-1.0, 1.0)), dist_b=("uniform", (-1.0, 1.0)),
                  dist_c=("uniform", (-1.0, 1.0)), bias_std: float = 0.1,
-                 fp8_scaled: bool = True, name: str = "") -> Problem:
+                 fp8_scaled: bool = True, mx: bool = False, name: str = "") -> Problem:
     """Draw a seeded problem.  `dist_*` is ("uniform", (lo, hi)), ("normal", std) or
-    ("int", (lo, hi)).  For E4M3 inputs each operand gets its own per-tensor scale when
-    `fp8_scaled`, else scale 1 (the draws must then already be E4M3 values)."""
+    ("int", (lo, hi)).  For fp8 inputs each operand gets its own per-tensor scale when
+    `fp8_scaled`, else scale 1 (the draws must then already be representable).  With `mx`
+    (8-bit or E2M1 inputs) the operands are quantised in OCP MX blocks of 32 along K instead,
+    and the per-tensor scales are 1.  `b_type` defaults to `a_type`."""
+    b_type = b_type or a_type
     c_type = c_type or OUT_TYPE[a_type]
     rng = np.random.default_rng(seed)
     a = _draw(rng, (M, K), dist_a)
@@ -200,23 +328,39 @@ def make_problem(M: int, N: int, K: int, *, a_type: str = "f32", c_type: Optiona
     bias = (rng.normal(0.0, bias_std, size=N).astype(np.float32)
             if epilogue & EPI_BIAS else None)
     sa = sb = np.float32(1.0)
-    if a_type == "e4m3" and fp8_scaled:
-        sa, sb = e4m3_scale(a), e4m3_scale(b)
-    a_st = np.ascontiguousarray(a.T if trans_a else a)
-    b_st = np.ascontiguousarray(b.T if trans_b else b)
-    A = encode(a_st, a_type, float(sa))
-    B = encode(b_st, a_type, float(sb))
+    sa_blk = sb_blk = None
+    if mx:
+        # quantise op(A) by rows and op(B) by columns (rows of B^T), then store as asked
+        qa, sa_blk = mx_quantize(a, a_type)
+        qb, sb_blk = mx_quantize(b.T, b_type)
+        if a_type == "e2m1" or b_type == "e2m1":
+            if trans_a or not trans_b:
+                raise ValueError("packed E2M1 operands are stored K-contiguous (A M x K, B N x K)")
+            A, B = qa, qb
+        else:
+            A = np.ascontiguousarray(qa.T if trans_a else qa)
+            B = np.ascontiguousarray(qb if trans_b else qb.T)
+    else:
+        if a_type in FP8 and fp8_scaled:
+            sa = fp8_scale(a, a_type)
+        if b_type in FP8 and fp8_scaled:
+            sb = fp8_scale(b, b_type)
+        a_st = np.ascontiguousarray(a.T if trans_a else a)
+        b_st = np.ascontiguousarray(b.T if trans_b else b)
+        A = encode(a_st, a_type, float(sa))
+        B = encode(b_st, b_type, float(sb))
     C = (encode(c_in, c_type) if c_in is not None
          else np.zeros((M, N), dtype=STORAGE[c_type]))
     recipe = dict(name=name, M=M, N=N, K=K, a_type=a_type, c_type=c_type, trans_a=trans_a,
                   trans_b=trans_b, alpha=alpha, beta=beta, epilogue=epilogue, seed=seed,
                   dist_a=list(map(str, dist_a)), dist_b=list(map(str, dist_b)),
                   dist_c=list(map(str, dist_c)), bias_std=bias_std, fp8_scaled=fp8_scaled,
-                  rng="numpy.default_rng(PCG64)", order="A,B,C_in,bias")
+                  b_type=b_type, mx=mx, rng="numpy.default_rng(PCG64)", order="A,B,C_in,bias")
     return Problem(name=name or f"{a_type}_{M}x{N}x{K}", M=M, N=N, K=K, trans_a=trans_a,
                    trans_b=trans_b, alpha=float(alpha), beta=float(beta), a_type=a_type,
-                   b_type=a_type, c_type=c_type, epilogue=epilogue, A=A, B=B, C=C, bias=bias,
-                   scale_a=float(sa), scale_b=float(sb), recipe=recipe)
+                   b_type=b_type, c_type=c_type, epilogue=epilogue, A=A, B=B, C=C, bias=bias,
+                   scale_a=float(sa), scale_b=float(sb), recipe=recipe, sa_blk=sa_blk,
+                   sb_blk=sb_blk)
 
 
 # The named workloads.
@@ -260,3 +404,24 @@ def bf16_twin_of_fp8(n: int = 4096) -> Problem:
     """The same float64 draws as fp8_4096, rounded to bf16 instead, bf16 out, no epilogue."""
     return make_problem(n, n, n, a_type="bf16", c_type="bf16", seed=4, dist_a=("normal", 1.0),
                         dist_b=("normal", 1.0), name=f"bf16_{n}")
+
+
+def e5m2_4096(n: int = 4096) -> Problem:
+    """fp8-E5M2 C = (sa*sb)*A*B, n^3, A,B ~ N(0,1), per-tensor scale max|x| -> 57344, bf16 out."""
+    return make_problem(n, n, n, a_type="e5m2", c_type="bf16", seed=5, dist_a=("normal", 1.0),
+                        dist_b=("normal", 1.0), name=f"e5m2_{n}")
+
+
+def mxfp8_4096(n: int = 4096) -> Problem:
+    """MXFP8 (E4M3 elements, E8M0 scale per 32 k) C = A*B, n^3, row-major A and B,
+    A,B ~ N(0,1), bf16 out, seed 5."""
+    return make_problem(n, n, n, a_type="e4m3", c_type="bf16", seed=5, mx=True,
+                        dist_a=("normal", 1.0), dist_b=("normal", 1.0), name=f"mxfp8_{n}")
+
+
+def mxfp4_4096(n: int = 4096) -> Problem:
+    """MXFP4 (E2M1 elements packed two per byte, E8M0 scale per 32 k) C = A*B, n^3, A stored
+    M x K and B stored N x K (both K-contiguous, as packed operands are), A,B ~ N(0,1), bf16
+    out, seed 5."""
+    return make_problem(n, n, n, a_type="e2m1", c_type="bf16", trans_b=True, seed=5, mx=True,
+                        dist_a=("normal", 1.0), dist_b=("normal", 1.0), name=f"mxfp4_{n}")

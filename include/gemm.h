@@ -18,16 +18,21 @@
  *     chosen by the library: "Rigel" (arXiv 2606.12765), section 2 (tensor_handle,
  *     matmul2d_descriptor);
  *   - the fused GEMM + bias + GELU versus the decomposed path, and fp8 E4M3 operands:
- *     "Rigel", abstract and section 1 (contribution 7).
+ *     "Rigel", abstract and section 1 (contribution 7);
+ *   - the other low-precision formats it lists beside fp8, block-scaled MXFP4 among them:
+ *     "Rigel", section 4 (the format rows of its results).
  *
  * Conventions shared by every entry point:
  *   - Storage is row-major.  Element (r, c) of a stored matrix X with leading dimension ldX is
  *     X[r * ldX + c].  A is stored M x K (lda >= K) or, with transA, K x M (lda >= M); B is
  *     stored K x N (ldb >= N) or, with transB, N x K (ldb >= K); C is M x N (ldc >= N).
  *     Leading dimensions and sizes are counted in elements.
- *   - Supported (A, B, C) type tuples: (F32,F32,F32), (F16,F16,F16), (BF16,BF16,BF16) and
- *     (E4M3,E4M3,BF16).  E4M3 is the OCP 8-bit float (bias 7, max 448, no infinities).
- *     Any other tuple returns GEMM_ERR_UNSUPPORTED.
+ *   - Supported (A, B, C) type tuples: (F32,F32,F32), (F16,F16,F16), (BF16,BF16,BF16),
+ *     (X,Y,BF16) for X, Y in {E4M3, E5M2}, and (E2M1,E2M1,BF16).  E4M3 and E5M2 are the OCP
+ *     8-bit floats (E4M3: bias 7, max 448, no infinities; E5M2: bias 15, max 57344, IEEE-style
+ *     infinities and NaN).  E2M1 is the OCP 4-bit float (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4,
+ *     6), stored two per byte along each stored row: element c of a row sits in byte c / 2,
+ *     in the low nibble when c is even.  Any other tuple returns GEMM_ERR_UNSUPPORTED.
  *   - Pointers A, B, C and bias are DEVICE pointers owned by the caller.  C is read (only when
  *     beta != 0) and written.  Nothing is allocated and nothing is retained after a call.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream).  They
@@ -69,7 +74,9 @@ typedef enum gemm_dtype {
   GEMM_F32 = 0,
   GEMM_F16 = 1,
   GEMM_BF16 = 2,
-  GEMM_E4M3 = 3
+  GEMM_E4M3 = 3,
+  GEMM_E5M2 = 4,
+  GEMM_E2M1 = 5
 } gemm_dtype_t;
 
 /* Epilogue bits.  BIAS adds bias[j] (fp32, length N, one value per output column, broadcast
@@ -112,8 +119,8 @@ GEMM_API gemm_status_t gemm_check_args(int64_t M, int64_t N, int64_t K, int tran
                               const float* bias);
 
 /* C = epi(alpha * scale_a * scale_b * op(A) op(B) + beta * C [+ bias]) on `stream`.
- * scale_a / scale_b are the per-tensor dequantisation scales of E4M3 operands (pass 1.0f for
- * other types; they multiply the product for every type).  beta == 0 means C is not read, so
+ * scale_a / scale_b are the per-tensor dequantisation scales of 8- and 4-bit operands (pass
+ * 1.0f for other types; they multiply the product for every type).  beta == 0 means C is not read, so
  * NaN in C does not propagate.  The kernel is chosen automatically (GEMM_KERNEL_AUTO). */
 GEMM_API gemm_status_t gemm_run(gemm_handle_t h, void* stream, int64_t M, int64_t N, int64_t K,
                        int transA, int transB, float alpha, const void* A, int64_t lda,
@@ -123,13 +130,58 @@ GEMM_API gemm_status_t gemm_run(gemm_handle_t h, void* stream, int64_t M, int64_
 
 /* gemm_run with an explicit kernel family.  Matrix-core kernels need 16-byte-aligned A, B and
  * C, lda * sizeof(A elem) and ldb * sizeof(B elem) multiples of 16 bytes, and ldc a multiple of
- * 4; otherwise they return GEMM_ERR_UNSUPPORTED (AUTO then uses GEMM_KERNEL_SIMT). */
+ * 4; E2M1 operands also need A stored M x K, B stored N x K and K even.  Otherwise they return
+ * GEMM_ERR_UNSUPPORTED (AUTO then uses GEMM_KERNEL_SIMT). */
 GEMM_API gemm_status_t gemm_run_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* stream, int64_t M,
                               int64_t N, int64_t K, int transA, int transB, float alpha,
                               const void* A, int64_t lda, float scale_a, const void* B,
                               int64_t ldb, float scale_b, float beta, void* C, int64_t ldc,
                               gemm_dtype_t a_type, gemm_dtype_t b_type, gemm_dtype_t c_type,
                               uint32_t epilogue, const float* bias);
+
+/* Block-scaled GEMM in the OCP microscaling (MX) formats: every run of 32 consecutive k of a
+ * row of op(A) and of a column of op(B) shares one E8M0 scale byte e, worth 2^(e - 127)
+ * (e = 255 is NaN):
+ *
+ *     op(A)[i][k] = A-element * 2^(sa[i * ldsa + k / 32] - 127),  0 <= i < M, 0 <= k < K
+ *     op(B)[k][j] = B-element * 2^(sb[j * ldsb + k / 32] - 127),  0 <= j < N
+ *     C = epi(alpha * op(A) op(B) + beta * C [+ bias])
+ *
+ * sa (M rows of ldsa >= K/32 bytes) and sb (N rows of ldsb >= K/32 bytes) are DEVICE pointers
+ * owned by the caller; bytes past K/32 in a row are never used.  Types: A and B in
+ * {E4M3, E5M2} (MXFP8, either mix) or both E2M1 (MXFP4); C is BF16.  K must be a multiple of
+ * 32.  Errors as gemm_run, plus GEMM_ERR_INVALID_VALUE for K % 32 != 0, a NULL scale array
+ * when K > 0, or ldsa / ldsb < K / 32, and GEMM_ERR_ALIAS when C overlaps a scale array.
+ * Matrix-core kernels additionally need 16-byte-aligned sa and sb, ldsa and ldsb multiples of
+ * 16, and fewer than 2^32 scale bytes per array; E2M1 operands need A stored M x K and B
+ * stored N x K with lda, ldb multiples of 32.  Other arguments take GEMM_KERNEL_SIMT. */
+GEMM_API gemm_status_t gemm_run_mx(gemm_handle_t h, void* stream, int64_t M, int64_t N,
+                                   int64_t K, int transA, int transB, float alpha,
+                                   const void* A, int64_t lda, const uint8_t* sa, int64_t ldsa,
+                                   const void* B, int64_t ldb, const uint8_t* sb, int64_t ldsb,
+                                   float beta, void* C, int64_t ldc, gemm_dtype_t a_type,
+                                   gemm_dtype_t b_type, gemm_dtype_t c_type, uint32_t epilogue,
+                                   const float* bias);
+
+/* Check the arguments of gemm_run_mx without touching any device (as gemm_check_args). */
+GEMM_API gemm_status_t gemm_check_args_mx(int64_t M, int64_t N, int64_t K, int transA,
+                                          int transB, const void* A, int64_t lda,
+                                          const uint8_t* sa, int64_t ldsa, const void* B,
+                                          int64_t ldb, const uint8_t* sb, int64_t ldsb,
+                                          const void* C, int64_t ldc, gemm_dtype_t a_type,
+                                          gemm_dtype_t b_type, gemm_dtype_t c_type,
+                                          uint32_t epilogue, const float* bias);
+
+/* gemm_run_mx with an explicit kernel family (as gemm_run_kernel). */
+GEMM_API gemm_status_t gemm_run_mx_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* stream,
+                                          int64_t M, int64_t N, int64_t K, int transA,
+                                          int transB, float alpha, const void* A, int64_t lda,
+                                          const uint8_t* sa, int64_t ldsa, const void* B,
+                                          int64_t ldb, const uint8_t* sb, int64_t ldsb,
+                                          float beta, void* C, int64_t ldc,
+                                          gemm_dtype_t a_type, gemm_dtype_t b_type,
+                                          gemm_dtype_t c_type, uint32_t epilogue,
+                                          const float* bias);
 
 /* The kernel family gemm_run would use for these arguments (a gemm_kernel_t value), or a
  * negative status when the arguments are invalid.  Touches no device. */

@@ -34,6 +34,8 @@ class Device:
         self.B = to_device(p.B, dev)
         self.C = to_device(p.C, dev)
         self.bias = to_device(p.bias, dev) if p.bias is not None else None
+        self.sa = to_device(p.sa_blk, dev) if p.sa_blk is not None else None
+        self.sb = to_device(p.sb_blk, dev) if p.sb_blk is not None else None
 
     def reset_c(self):
         import torch
@@ -46,9 +48,10 @@ def run(g, p: W.Problem, kernel: int = 0, dev: Device | None = None, epilogue=No
     import tiled_matrix_multiply_amd as tmm
     d = dev or Device(p)
     tmm.run(g.handle, d.A, d.B, d.C, M=p.M, N=p.N, K=p.K, trans_a=p.trans_a, trans_b=p.trans_b,
-            alpha=p.alpha, beta=p.beta, a_type=p.a_type, c_type=p.c_type,
+            alpha=p.alpha, beta=p.beta, a_type=p.a_type, b_type=p.b_type, c_type=p.c_type,
             epilogue=p.epilogue if epilogue is None else epilogue, bias=d.bias,
-            scale_a=p.scale_a, scale_b=p.scale_b, kernel=kernel)
+            scale_a=p.scale_a, scale_b=p.scale_b, sa_blk=d.sa, sb_blk=d.sb,
+            ldsa=p.ldsa or None, ldsb=p.ldsb or None, kernel=kernel)
     torch.cuda.synchronize()
     raw = from_device(d.C, p.c_type)
     return raw, oracle.decode(p.c_type, raw)
@@ -93,13 +96,15 @@ def gate_sampled(p: W.Problem, got: np.ndarray, n: int = 2048, seed: int = 0,
 
 
 POISON = {"f32": np.float32(np.nan).view(np.uint32), "f16": 0xFFFF, "bf16": 0xFFFF,
-          "e4m3": 0xFF}
+          "e4m3": 0xFF, "e5m2": 0xFF, "e2m1": 0xFF}  # e2m1 has no NaN: 0xFF is (-6, -6)
 
 
 def padded_storage(stored: np.ndarray, dtype: str, ld: int) -> np.ndarray:
-    """Copy a stored matrix into rows of length ld, filling the padding with NaN patterns."""
+    """Copy a stored matrix into rows of length ld (elements), filling the padding with NaN
+    patterns (packed E2M1 rows hold ld / 2 bytes)."""
     words = stored.view(np.uint32) if stored.dtype == np.float32 else stored
-    out = np.full((stored.shape[0], ld), POISON[dtype], dtype=words.dtype)
+    width = ld // 2 if dtype == "e2m1" else ld
+    out = np.full((stored.shape[0], width), POISON[dtype], dtype=words.dtype)
     out[:, :stored.shape[1]] = words
     return out.view(np.float32) if stored.dtype == np.float32 else out
 
@@ -115,18 +120,27 @@ def run_padded(g, p: W.Problem, ld_fn=aligned_ld, kernel: int = 0):
     import torch
     import tiled_matrix_multiply_amd as tmm
     lda, ldb, ldc = ld_fn(p.lda), ld_fn(p.ldb), ld_fn(p.ldc)
+    if p.a_type == "e2m1":  # whole 16-byte packed rows
+        lda, ldb = -(-lda // 32) * 32, -(-ldb // 32) * 32
     Ah = padded_storage(p.A, p.a_type, lda)
     Bh = padded_storage(p.B, p.b_type, ldb)
     Ch = padded_storage(p.C, p.c_type, ldc)
     A, B, C = to_device(Ah), to_device(Bh), to_device(Ch)
     bias = to_device(p.bias) if p.bias is not None else None
     kname = tmm.select_kernel(g.handle, p.M, p.N, p.K, trans_a=p.trans_a, trans_b=p.trans_b,
-                              a_type=p.a_type, A=A, B=B, C=C, epilogue=p.epilogue, bias=bias,
-                              lda=lda, ldb=ldb, ldc=ldc)
+                              a_type=p.a_type, b_type=p.b_type, A=A, B=B, C=C,
+                              epilogue=p.epilogue, bias=bias, lda=lda, ldb=ldb, ldc=ldc)
+    sa = sb = None
+    ldsa = ldsb = None
+    if p.sa_blk is not None:
+        # scale rows padded to 16-byte multiples with NaN scales (0xFF) that must never be used
+        ldsa = ldsb = -(-p.ldsa // 16) * 16
+        sa = to_device(padded_storage(p.sa_blk, "e4m3", ldsa))
+        sb = to_device(padded_storage(p.sb_blk, "e4m3", ldsb))
     tmm.run(g.handle, A, B, C, M=p.M, N=p.N, K=p.K, trans_a=p.trans_a, trans_b=p.trans_b,
-            alpha=p.alpha, beta=p.beta, a_type=p.a_type, c_type=p.c_type, epilogue=p.epilogue,
-            bias=bias, scale_a=p.scale_a, scale_b=p.scale_b, lda=lda, ldb=ldb, ldc=ldc,
-            kernel=kernel)
+            alpha=p.alpha, beta=p.beta, a_type=p.a_type, b_type=p.b_type, c_type=p.c_type,
+            epilogue=p.epilogue, bias=bias, scale_a=p.scale_a, scale_b=p.scale_b, lda=lda,
+            ldb=ldb, ldc=ldc, sa_blk=sa, sb_blk=sb, ldsa=ldsa, ldsb=ldsb, kernel=kernel)
     torch.cuda.synchronize()
     raw = from_device(C, p.c_type)
     pad_ok = bool(np.array_equal(raw.view(np.uint8).reshape(p.M, -1)[:, p.N * W.ESIZE[p.c_type]:],

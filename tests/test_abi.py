@@ -23,7 +23,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported():
     syms = declared_symbols()
-    assert len(syms) == 8, syms
+    assert len(syms) == 11, syms
     assert sorted(tmm.EXPORTS) == syms
     nm = subprocess.run(["nm", "-D", "--defined-only", tmm.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
@@ -147,3 +147,67 @@ def test_product_path_never_touches_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text, os.path.join(dirpath, f)
+
+
+# --- 8- and 4-bit types and OCP MX block scales ------------------------------------------------
+
+E5M2, E2M1 = tmm.GEMM_E5M2, tmm.GEMM_E2M1
+PSA, PSB = 0x50000000, 0x60000000
+
+
+def chk_mx(M=64, N=48, K=64, ta=0, tb=0, A=PA, lda=None, sa=PSA, ldsa=None, B=PB, ldb=None,
+           sb=PSB, ldsb=None, C=PC, ldc=None, at=E4M3, bt=None, ct=BF16, epi=0, bias=None):
+    bt = at if bt is None else bt
+    lda = (M if ta else K) if lda is None else lda
+    ldb = (K if tb else N) if ldb is None else ldb
+    ldsa = K // 32 if ldsa is None else ldsa
+    ldsb = K // 32 if ldsb is None else ldsb
+    ldc = N if ldc is None else ldc
+    return tmm.gemm_check_args_mx(M, N, K, ta, tb, A, lda, sa, ldsa, B, ldb, sb, ldsb, C, ldc,
+                                  at, bt, ct, epi, bias)
+
+
+def test_low_precision_type_tuples():
+    OK, U = tmm.GEMM_OK, tmm.GEMM_ERR_UNSUPPORTED
+    for at in (E4M3, E5M2):
+        for bt in (E4M3, E5M2):
+            assert chk(at=at, bt=bt, ct=BF16) == OK
+            assert chk(at=at, bt=bt, ct=F32) == U
+    assert chk(at=E2M1, ct=BF16, tb=1) == OK
+    assert chk(at=E2M1, bt=E4M3, ct=BF16) == U
+    assert chk(at=E4M3, bt=E2M1, ct=BF16) == U
+    assert chk(at=E2M1, ct=E2M1) == U
+
+
+def test_packed_fp4_byte_ranges():
+    """E2M1 rows take half a byte per element: A (64 x 32, lda 32) spans 1024 bytes."""
+    AL, OK = tmm.GEMM_ERR_ALIAS, tmm.GEMM_OK
+    assert chk(at=E2M1, ct=BF16, C=PA + 1023) == AL
+    assert chk(at=E2M1, ct=BF16, C=PA + 1024) == OK
+    # an odd element count rounds the last partly used byte up
+    assert chk(at=E2M1, ct=BF16, M=1, K=3, lda=3, C=PA + 1) == AL
+    assert chk(at=E2M1, ct=BF16, M=1, K=3, lda=3, C=PA + 2) == OK
+
+
+def test_mx_arguments():
+    OK, V, U, AL = (tmm.GEMM_OK, tmm.GEMM_ERR_INVALID_VALUE, tmm.GEMM_ERR_UNSUPPORTED,
+                    tmm.GEMM_ERR_ALIAS)
+    assert chk_mx() == OK
+    assert chk_mx(at=E5M2, bt=E4M3) == OK and chk_mx(ta=1, tb=1) == OK
+    assert chk_mx(at=E2M1, tb=1) == OK
+    assert chk_mx(K=48, ldsa=2, ldsb=2) == V      # K must be a multiple of 32
+    assert chk_mx(sa=None) == V and chk_mx(sb=None) == V
+    assert chk_mx(ldsa=1) == V and chk_mx(ldsb=1) == V
+    assert chk_mx(K=0, A=None, B=None, sa=None, sb=None, lda=0, ldb=48) == OK
+    assert chk_mx(at=F16, ct=F16) == U and chk_mx(at=BF16, ct=BF16) == U
+    assert chk_mx(C=PSA + 10) == AL               # C overlaps the A scales (64 x 2 bytes)
+    assert chk_mx(C=PSA + 128) == OK
+    assert chk_mx(C=PSB + 95) == AL and chk_mx(C=PSB + 96) == OK
+
+
+def test_mx_null_handle():
+    assert tmm.gemm_run_mx(None, None, 4, 4, 32, 0, 0, 1.0, PA, 32, PSA, 1, PB, 4, PSB, 1, 0.0,
+                           PC, 4, E4M3, E4M3, BF16, 0, None) == tmm.GEMM_ERR_INVALID_HANDLE
+    assert tmm.gemm_run_mx_kernel(None, 0, None, 4, 4, 32, 0, 0, 1.0, PA, 32, PSA, 1, PB, 4, PSB,
+                                  1, 0.0, PC, 4, E4M3, E4M3, BF16, 0,
+                                  None) == tmm.GEMM_ERR_INVALID_HANDLE

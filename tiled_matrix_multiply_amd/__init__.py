@@ -27,8 +27,10 @@ GEMM_ERR_LAUNCH = -6
 GEMM_ERR_NO_MEMORY = -7
 
 # gemm_dtype_t
-GEMM_F32, GEMM_F16, GEMM_BF16, GEMM_E4M3 = 0, 1, 2, 3
-DTYPE = {"f32": GEMM_F32, "f16": GEMM_F16, "bf16": GEMM_BF16, "e4m3": GEMM_E4M3}
+GEMM_F32, GEMM_F16, GEMM_BF16, GEMM_E4M3, GEMM_E5M2, GEMM_E2M1 = 0, 1, 2, 3, 4, 5
+DTYPE = {"f32": GEMM_F32, "f16": GEMM_F16, "bf16": GEMM_BF16, "e4m3": GEMM_E4M3,
+         "e5m2": GEMM_E5M2, "e2m1": GEMM_E2M1}
+LOWP = ("e4m3", "e5m2", "e2m1")  # output bf16
 
 # epilogue bits
 GEMM_EPI_NONE, GEMM_EPI_BIAS, GEMM_EPI_GELU = 0, 1, 2
@@ -43,7 +45,8 @@ KERNEL_NAME = {0: "auto", 1: "simt", 2: "mfma64", 3: "mfma128", 4: "mfma256"}
 
 # Every symbol include/gemm.h declares.
 EXPORTS = ("gemm_create", "gemm_destroy", "gemm_check_args", "gemm_run", "gemm_run_kernel",
-           "gemm_select_kernel", "gemm_bias_gelu", "gemm_status_string")
+           "gemm_run_mx", "gemm_run_mx_kernel", "gemm_check_args_mx", "gemm_select_kernel",
+           "gemm_bias_gelu", "gemm_status_string")
 
 # libgemm.so must resolve its libamdhip64.so.7 dependency to the HIP runtime instance that owns
 # the caller's device pointers and streams.  PyTorch ships its own runtime (soname
@@ -80,6 +83,15 @@ _lib.gemm_run.argtypes = [_vp, _vp] + _RUN
 _lib.gemm_run.restype = _int
 _lib.gemm_run_kernel.argtypes = [_vp, _int, _vp] + _RUN
 _lib.gemm_run_kernel.restype = _int
+_RUN_MX = [_i64, _i64, _i64, _int, _int, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _f32,
+           _vp, _i64, _int, _int, _int, _u32, _vp]
+_lib.gemm_run_mx.argtypes = [_vp, _vp] + _RUN_MX
+_lib.gemm_run_mx.restype = _int
+_lib.gemm_run_mx_kernel.argtypes = [_vp, _int, _vp] + _RUN_MX
+_lib.gemm_run_mx_kernel.restype = _int
+_lib.gemm_check_args_mx.argtypes = [_i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _i64, _vp, _i64,
+                                    _vp, _i64, _vp, _i64, _int, _int, _int, _u32, _vp]
+_lib.gemm_check_args_mx.restype = _int
 _lib.gemm_select_kernel.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _i64, _vp,
                                     _i64, _int, _int, _int, _u32, _vp]
 _lib.gemm_select_kernel.restype = _int
@@ -142,6 +154,28 @@ def gemm_run_kernel(handle, kernel, stream, M, N, K, transA, transB, alpha, A, l
                                 epilogue, bias)
 
 
+def gemm_check_args_mx(M, N, K, transA, transB, A, lda, sa, ldsa, B, ldb, sb, ldsb, C, ldc,
+                       a_type, b_type, c_type, epilogue, bias) -> int:
+    """Pointers are integers (device addresses) or None.  Returns the status code."""
+    return _lib.gemm_check_args_mx(M, N, K, transA, transB, A, lda, sa, ldsa, B, ldb, sb, ldsb,
+                                   C, ldc, a_type, b_type, c_type, epilogue, bias)
+
+
+def gemm_run_mx(handle, stream, M, N, K, transA, transB, alpha, A, lda, sa, ldsa, B, ldb, sb,
+                ldsb, beta, C, ldc, a_type, b_type, c_type, epilogue, bias) -> int:
+    """Raw block-scaled (OCP MX) entry point: returns the status code (no exception)."""
+    return _lib.gemm_run_mx(handle, stream, M, N, K, transA, transB, alpha, A, lda, sa, ldsa, B,
+                            ldb, sb, ldsb, beta, C, ldc, a_type, b_type, c_type, epilogue, bias)
+
+
+def gemm_run_mx_kernel(handle, kernel, stream, M, N, K, transA, transB, alpha, A, lda, sa, ldsa,
+                       B, ldb, sb, ldsb, beta, C, ldc, a_type, b_type, c_type, epilogue,
+                       bias) -> int:
+    return _lib.gemm_run_mx_kernel(handle, kernel, stream, M, N, K, transA, transB, alpha, A,
+                                   lda, sa, ldsa, B, ldb, sb, ldsb, beta, C, ldc, a_type, b_type,
+                                   c_type, epilogue, bias)
+
+
 def gemm_select_kernel(handle, M, N, K, transA, transB, A, lda, B, ldb, C, ldc, a_type, b_type,
                        c_type, epilogue, bias) -> int:
     return _lib.gemm_select_kernel(handle, M, N, K, transA, transB, A, lda, B, ldb, C, ldc,
@@ -169,21 +203,36 @@ def _ptr(t):
 
 
 def run(handle, A, B, C, *, M, N, K, trans_a=False, trans_b=False, alpha=1.0, beta=0.0,
-        a_type="f32", c_type=None, epilogue=GEMM_EPI_NONE, bias=None, scale_a=1.0,
-        scale_b=1.0, lda=None, ldb=None, ldc=None, kernel=GEMM_KERNEL_AUTO, stream=None):
+        a_type="f32", b_type=None, c_type=None, epilogue=GEMM_EPI_NONE, bias=None, scale_a=1.0,
+        scale_b=1.0, lda=None, ldb=None, ldc=None, sa_blk=None, sb_blk=None, ldsa=None,
+        ldsb=None, kernel=GEMM_KERNEL_AUTO, stream=None):
     """GEMM on device tensors holding storage words (A, B, C contiguous row-major unless ld*
-    is given).  Raises GemmError on a negative status.  Asynchronous on `stream` (default:
-    torch's current stream)."""
-    c_type = c_type or ("bf16" if a_type == "e4m3" else a_type)
+    is given; E2M1 holds two elements per byte).  With sa_blk / sb_blk (device uint8 tensors
+    of E8M0 scales, M x ldsa and N x ldsb) the call is block-scaled (gemm_run_mx).  Raises
+    GemmError on a negative status.  Asynchronous on `stream` (default: torch's current
+    stream)."""
+    b_type = b_type or a_type
+    c_type = c_type or ("bf16" if a_type in LOWP else a_type)
     lda = lda if lda is not None else (M if trans_a else K)
     ldb = ldb if ldb is not None else (K if trans_b else N)
     ldc = ldc if ldc is not None else N
-    st = gemm_run_kernel(handle, kernel, _stream(stream), M, N, K, int(trans_a), int(trans_b),
-                         float(alpha), _ptr(A), lda, float(scale_a), _ptr(B), ldb,
-                         float(scale_b), float(beta), _ptr(C), ldc, DTYPE[a_type], DTYPE[a_type],
-                         DTYPE[c_type], int(epilogue), _ptr(bias))
+    if sa_blk is not None or sb_blk is not None:
+        ldsa = ldsa if ldsa is not None else K // 32
+        ldsb = ldsb if ldsb is not None else K // 32
+        st = gemm_run_mx_kernel(handle, kernel, _stream(stream), M, N, K, int(trans_a),
+                                int(trans_b), float(alpha), _ptr(A), lda, _ptr(sa_blk), ldsa,
+                                _ptr(B), ldb, _ptr(sb_blk), ldsb, float(beta), _ptr(C), ldc,
+                                DTYPE[a_type], DTYPE[b_type], DTYPE[c_type], int(epilogue),
+                                _ptr(bias))
+        where = "gemm_run_mx"
+    else:
+        st = gemm_run_kernel(handle, kernel, _stream(stream), M, N, K, int(trans_a),
+                             int(trans_b), float(alpha), _ptr(A), lda, float(scale_a), _ptr(B),
+                             ldb, float(scale_b), float(beta), _ptr(C), ldc, DTYPE[a_type],
+                             DTYPE[b_type], DTYPE[c_type], int(epilogue), _ptr(bias))
+        where = "gemm_run"
     if st != GEMM_OK:
-        raise GemmError(st, "gemm_run")
+        raise GemmError(st, where)
 
 
 def bias_gelu(handle, C, bias, *, M, N, c_type, epilogue=GEMM_EPI_BIAS | GEMM_EPI_GELU,
@@ -195,15 +244,16 @@ def bias_gelu(handle, C, bias, *, M, N, c_type, epilogue=GEMM_EPI_BIAS | GEMM_EP
         raise GemmError(st, "gemm_bias_gelu")
 
 
-def select_kernel(handle, M, N, K, *, trans_a=False, trans_b=False, a_type="f32", A=None,
-                  B=None, C=None, epilogue=GEMM_EPI_NONE, bias=None, lda=None, ldb=None,
-                  ldc=None) -> str:
+def select_kernel(handle, M, N, K, *, trans_a=False, trans_b=False, a_type="f32", b_type=None,
+                  A=None, B=None, C=None, epilogue=GEMM_EPI_NONE, bias=None, lda=None,
+                  ldb=None, ldc=None) -> str:
     """Name of the kernel family gemm_run picks for these arguments."""
-    c_type = "bf16" if a_type == "e4m3" else a_type
+    b_type = b_type or a_type
+    c_type = "bf16" if a_type in LOWP else a_type
     k = gemm_select_kernel(handle, M, N, K, int(trans_a), int(trans_b), _ptr(A),
                            lda if lda is not None else (M if trans_a else K), _ptr(B),
                            ldb if ldb is not None else (K if trans_b else N), _ptr(C),
-                           ldc if ldc is not None else N, DTYPE[a_type], DTYPE[a_type],
+                           ldc if ldc is not None else N, DTYPE[a_type], DTYPE[b_type],
                            DTYPE[c_type], int(epilogue), _ptr(bias))
     if k < 0:
         raise GemmError(k, "gemm_select_kernel")

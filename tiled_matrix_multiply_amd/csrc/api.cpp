@@ -11,11 +11,24 @@
 #include "common.hpp"
 
 namespace tgemm {
-hipError_t launch_simt(const GemmParams& p, int a_type, int transA, int transB, hipStream_t s);
+hipError_t launch_simt(const GemmParams& p, int a_type, int b_type, int transA, int transB,
+                       hipStream_t s);
 hipError_t launch_mfma_f32(const GemmParams& p, int tile, bool a_mn, bool b_mn, hipStream_t s);
 hipError_t launch_mfma_f16(const GemmParams& p, int tile, bool a_mn, bool b_mn, hipStream_t s);
 hipError_t launch_mfma_bf16(const GemmParams& p, int tile, bool a_mn, bool b_mn, hipStream_t s);
-hipError_t launch_mfma_e4m3(const GemmParams& p, int tile, bool a_mn, bool b_mn, hipStream_t s);
+#define TGEMM_F8_LAUNCHER(name) \
+  hipError_t launch_mfma_##name(const GemmParams& p, int tile, bool a_mn, bool b_mn, hipStream_t s);
+TGEMM_F8_LAUNCHER(e4m3)
+TGEMM_F8_LAUNCHER(e5m2)
+TGEMM_F8_LAUNCHER(e4m3_e5m2)
+TGEMM_F8_LAUNCHER(e5m2_e4m3)
+TGEMM_F8_LAUNCHER(mx_e4m3)
+TGEMM_F8_LAUNCHER(mx_e5m2)
+TGEMM_F8_LAUNCHER(mx_e4m3_e5m2)
+TGEMM_F8_LAUNCHER(mx_e5m2_e4m3)
+TGEMM_F8_LAUNCHER(e2m1)
+TGEMM_F8_LAUNCHER(mx_e2m1)
+#undef TGEMM_F8_LAUNCHER
 hipError_t launch_bias_gelu(void* C, int64_t ldc, int M, int N, int c_type, const float* bias,
                             uint32_t epi, int cu_count, hipStream_t s);
 }  // namespace tgemm
@@ -38,37 +51,50 @@ struct Args {
   gemm_dtype_t at, bt, ct;
   uint32_t epi;
   const float* bias;
+  // OCP MX block scales (gemm_run_mx): mx set, sa / sb the E8M0 arrays
+  bool mx;
+  const uint8_t* sa;
+  int64_t ldsa;
+  const uint8_t* sb;
+  int64_t ldsb;
 };
 
-int esize(gemm_dtype_t t) {
+// Storage bits per element (E2M1 packs two per byte).
+int ebits(gemm_dtype_t t) {
   switch (t) {
-    case GEMM_F32: return 4;
-    case GEMM_F16: return 2;
-    case GEMM_BF16: return 2;
-    case GEMM_E4M3: return 1;
+    case GEMM_F32: return 32;
+    case GEMM_F16: return 16;
+    case GEMM_BF16: return 16;
+    case GEMM_E4M3: return 8;
+    case GEMM_E5M2: return 8;
+    case GEMM_E2M1: return 4;
     default: return 0;
   }
 }
 
+bool is_fp8(gemm_dtype_t t) { return t == GEMM_E4M3 || t == GEMM_E5M2; }
+
 bool supported_tuple(gemm_dtype_t a, gemm_dtype_t b, gemm_dtype_t c) {
+  if (is_fp8(a) && is_fp8(b)) return c == GEMM_BF16;
   if (a != b) return false;
   switch (a) {
     case GEMM_F32: return c == GEMM_F32;
     case GEMM_F16: return c == GEMM_F16;
     case GEMM_BF16: return c == GEMM_BF16;
-    case GEMM_E4M3: return c == GEMM_BF16;
+    case GEMM_E2M1: return c == GEMM_BF16;
     default: return false;
   }
 }
 
-// Byte range [lo, hi) touched by a rows x cols row-major matrix with leading dimension ld.
+// Byte range [lo, hi) touched by a rows x cols row-major matrix with leading dimension ld
+// (elements of `bits` bits; a partly used last byte counts whole).
 struct Range {
   __int128 lo, hi;
 };
-Range byte_range(const void* p, int64_t rows, int64_t cols, int64_t ld, int es) {
+Range byte_range(const void* p, int64_t rows, int64_t cols, int64_t ld, int bits) {
   const __int128 lo = (__int128)(uintptr_t)p;
   if (rows <= 0 || cols <= 0) return {lo, lo};
-  return {lo, lo + ((__int128)(rows - 1) * ld + cols) * es};
+  return {lo, lo + (((__int128)(rows - 1) * ld + cols) * bits + 7) / 8};
 }
 bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
@@ -77,24 +103,33 @@ gemm_status_t check(const Args& a) {
   if ((a.transA != 0 && a.transA != 1) || (a.transB != 0 && a.transB != 1))
     return GEMM_ERR_INVALID_VALUE;
   if (a.epi & ~(GEMM_EPI_BIAS | GEMM_EPI_GELU)) return GEMM_ERR_INVALID_VALUE;
-  if (!esize(a.at) || !esize(a.bt) || !esize(a.ct)) return GEMM_ERR_UNSUPPORTED;
+  if (!ebits(a.at) || !ebits(a.bt) || !ebits(a.ct)) return GEMM_ERR_UNSUPPORTED;
   if (!supported_tuple(a.at, a.bt, a.ct)) return GEMM_ERR_UNSUPPORTED;
+  if (a.mx && !(is_fp8(a.at) || a.at == GEMM_E2M1)) return GEMM_ERR_UNSUPPORTED;
   if (a.M > kMaxDim || a.N > kMaxDim || a.K > kMaxDim) return GEMM_ERR_UNSUPPORTED;
   if (a.M == 0 || a.N == 0) return GEMM_OK;  // nothing to compute
   if (!a.C) return GEMM_ERR_INVALID_VALUE;
   if (a.ldc < a.N) return GEMM_ERR_INVALID_VALUE;
   if ((a.epi & GEMM_EPI_BIAS) && !a.bias) return GEMM_ERR_INVALID_VALUE;
-  const Range rc = byte_range(a.C, a.M, a.N, a.ldc, esize(a.ct));
+  if (a.mx && a.K % 32 != 0) return GEMM_ERR_INVALID_VALUE;
+  const Range rc = byte_range(a.C, a.M, a.N, a.ldc, ebits(a.ct));
   if (a.K > 0) {
     if (!a.A || !a.B) return GEMM_ERR_INVALID_VALUE;
     const int64_t a_rows = a.transA ? a.K : a.M, a_cols = a.transA ? a.M : a.K;
     const int64_t b_rows = a.transB ? a.N : a.K, b_cols = a.transB ? a.K : a.N;
     if (a.lda < a_cols || a.ldb < b_cols) return GEMM_ERR_INVALID_VALUE;
-    if (overlaps(rc, byte_range(a.A, a_rows, a_cols, a.lda, esize(a.at))) ||
-        overlaps(rc, byte_range(a.B, b_rows, b_cols, a.ldb, esize(a.bt))))
+    if (overlaps(rc, byte_range(a.A, a_rows, a_cols, a.lda, ebits(a.at))) ||
+        overlaps(rc, byte_range(a.B, b_rows, b_cols, a.ldb, ebits(a.bt))))
       return GEMM_ERR_ALIAS;
+    if (a.mx) {
+      const int64_t kb = a.K / 32;
+      if (!a.sa || !a.sb || a.ldsa < kb || a.ldsb < kb) return GEMM_ERR_INVALID_VALUE;
+      if (overlaps(rc, byte_range(a.sa, a.M, kb, a.ldsa, 8)) ||
+          overlaps(rc, byte_range(a.sb, a.N, kb, a.ldsb, 8)))
+        return GEMM_ERR_ALIAS;
+    }
   }
-  if ((a.epi & GEMM_EPI_BIAS) && overlaps(rc, byte_range(a.bias, 1, a.N, a.N, 4)))
+  if ((a.epi & GEMM_EPI_BIAS) && overlaps(rc, byte_range(a.bias, 1, a.N, a.N, 32)))
     return GEMM_ERR_ALIAS;
   return GEMM_OK;
 }
@@ -102,11 +137,23 @@ gemm_status_t check(const Args& a) {
 // Matrix-core kernels read 16-byte chunks of A and B and store 4-element runs of C.
 bool mfma_aligned(const Args& a) {
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (a.at == GEMM_E2M1) {
+    // packed fp4 is staged as bytes along K: A stored M x K, B stored N x K, whole bytes
+    if (a.transA != 0 || a.transB != 1 || a.K % 2 != 0) return false;
+  }
   if (a.K > 0) {
     if (!al16(a.A) || !al16(a.B)) return false;
-    if ((a.lda * esize(a.at)) % 16 != 0 || (a.ldb * esize(a.bt)) % 16 != 0) return false;
+    const int64_t lda_bits = a.lda * ebits(a.at), ldb_bits = a.ldb * ebits(a.bt);
+    if (lda_bits % 128 != 0 || ldb_bits % 128 != 0) return false;
     // per-lane 32-bit buffer offsets span up to 256 rows of a staged tile
-    if (a.lda * esize(a.at) > kMaxRowBytes || a.ldb * esize(a.bt) > kMaxRowBytes) return false;
+    if (lda_bits / 8 > kMaxRowBytes || ldb_bits / 8 > kMaxRowBytes) return false;
+    if (a.mx) {
+      // 16-byte scale pieces per row, addressed by 32-bit offsets
+      if (!al16(a.sa) || !al16(a.sb) || a.ldsa % 16 != 0 || a.ldsb % 16 != 0) return false;
+      if ((__int128)a.M * a.ldsa >= ((__int128)1 << 32) - 16 ||
+          (__int128)a.N * a.ldsb >= ((__int128)1 << 32) - 16)
+        return false;
+    }
   }
   return al16(a.C) && (a.ldc % 4 == 0);
 }
@@ -197,65 +244,144 @@ int gemm_select_kernel(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int tra
   return auto_kernel(a, h->cu_count);
 }
 
-gemm_status_t gemm_run_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* stream, int64_t M,
-                              int64_t N, int64_t K, int transA, int transB, float alpha,
-                              const void* A, int64_t lda, float scale_a, const void* B,
-                              int64_t ldb, float scale_b, float beta, void* C, int64_t ldc,
-                              gemm_dtype_t a_type, gemm_dtype_t b_type, gemm_dtype_t c_type,
-                              uint32_t epilogue, const float* bias) {
+}  // extern "C"
+
+namespace {
+
+// The 8- and 4-bit matrix-core launcher for an (A, B, block-scaled) combination.
+using Launcher = hipError_t (*)(const tgemm::GemmParams&, int, bool, bool, hipStream_t);
+Launcher f8_launcher(gemm_dtype_t at, gemm_dtype_t bt, bool mx) {
+  using namespace tgemm;
+  if (at == GEMM_E2M1) return mx ? launch_mfma_mx_e2m1 : launch_mfma_e2m1;
+  const bool a5 = at == GEMM_E5M2, b5 = bt == GEMM_E5M2;
+  if (mx) {
+    if (!a5 && !b5) return launch_mfma_mx_e4m3;
+    if (a5 && b5) return launch_mfma_mx_e5m2;
+    return a5 ? launch_mfma_mx_e5m2_e4m3 : launch_mfma_mx_e4m3_e5m2;
+  }
+  if (!a5 && !b5) return launch_mfma_e4m3;
+  if (a5 && b5) return launch_mfma_e5m2;
+  return a5 ? launch_mfma_e5m2_e4m3 : launch_mfma_e4m3_e5m2;
+}
+
+gemm_status_t run_impl(gemm_handle_t h, gemm_kernel_t kernel, void* stream, const Args& a,
+                       float alpha, float scale_a, float scale_b, float beta, void* C) {
   if (!valid(h)) return GEMM_ERR_INVALID_HANDLE;
-  const Args a{M, N, K, transA, transB, A, lda, B, ldb, C, ldc, a_type, b_type, c_type,
-               epilogue, bias};
   gemm_status_t st = check(a);
   if (st != GEMM_OK) return st;
-  if (M == 0 || N == 0) return GEMM_OK;
+  if (a.M == 0 || a.N == 0) return GEMM_OK;
   if (kernel == GEMM_KERNEL_AUTO) kernel = auto_kernel(a, h->cu_count);
 
-  tgemm::GemmParams p;
-  p.A = A;
-  p.B = B;
+  tgemm::GemmParams p{};
+  p.A = a.A;
+  p.B = a.B;
   p.C = C;
-  p.bias = bias;
-  p.lda = lda;
-  p.ldb = ldb;
-  p.ldc = ldc;
-  p.M = (int)M;
-  p.N = (int)N;
-  p.K = (int)K;
+  p.bias = a.bias;
+  p.lda = a.lda;
+  p.ldb = a.ldb;
+  p.ldc = a.ldc;
+  p.M = (int)a.M;
+  p.N = (int)a.N;
+  p.K = (int)a.K;
   p.alpha = alpha * scale_a * scale_b;
   p.beta = beta;
-  p.epi = epilogue;
+  p.epi = a.epi;
+  if (a.mx) {
+    p.sa = a.sa;
+    p.sb = a.sb;
+    p.ldsa = a.ldsa;
+    p.ldsb = a.ldsb;
+    p.kblocks = (int)(a.K / 32);
+  }
 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (kernel == GEMM_KERNEL_SIMT) {
-    if ((M + 15) / 16 > 65535) return GEMM_ERR_UNSUPPORTED;
-    p.tiles_m = (int)((M + 15) / 16);
-    p.tiles_n = (int)((N + 15) / 16);
+    if ((a.M + 15) / 16 > 65535) return GEMM_ERR_UNSUPPORTED;
+    p.tiles_m = (int)((a.M + 15) / 16);
+    p.tiles_n = (int)((a.N + 15) / 16);
     DeviceGuard g(h->device);
-    err = tgemm::launch_simt(p, a_type, transA, transB, s);
+    err = tgemm::launch_simt(p, a.at, a.bt, a.transA, a.transB, s);
   } else if (kernel >= GEMM_KERNEL_MFMA_64 && kernel <= GEMM_KERNEL_MFMA_256) {
     if (!mfma_aligned(a)) return GEMM_ERR_UNSUPPORTED;
     const int tile = kernel - GEMM_KERNEL_MFMA_64;
     const int t = 64 << tile;
-    const int64_t tm = (M + t - 1) / t, tn = (N + t - 1) / t;
+    const int64_t tm = (a.M + t - 1) / t, tn = (a.N + t - 1) / t;
     if (tm * tn > kMaxDim) return GEMM_ERR_UNSUPPORTED;
     p.tiles_m = (int)tm;
     p.tiles_n = (int)tn;
+    if (a.at == GEMM_E2M1) {
+      // the matrix-core kernels stage packed fp4 rows as bytes: K and the leading dimensions
+      // are passed in bytes (two elements each); the block count stays in elements / 32
+      p.K = (int)(a.K / 2);
+      p.lda = a.lda / 2;
+      p.ldb = a.ldb / 2;
+    }
     // Storage contiguous along M (A stored K x M) or along N (B stored K x N).
-    const bool a_mn = transA != 0, b_mn = transB == 0;
+    const bool a_mn = a.transA != 0, b_mn = a.transB == 0;
     DeviceGuard g(h->device);
-    switch (a_type) {
+    switch (a.at) {
       case GEMM_F32: err = tgemm::launch_mfma_f32(p, tile, a_mn, b_mn, s); break;
       case GEMM_F16: err = tgemm::launch_mfma_f16(p, tile, a_mn, b_mn, s); break;
       case GEMM_BF16: err = tgemm::launch_mfma_bf16(p, tile, a_mn, b_mn, s); break;
-      case GEMM_E4M3: err = tgemm::launch_mfma_e4m3(p, tile, a_mn, b_mn, s); break;
+      case GEMM_E4M3:
+      case GEMM_E5M2:
+      case GEMM_E2M1: err = f8_launcher(a.at, a.bt, a.mx)(p, tile, a_mn, b_mn, s); break;
       default: return GEMM_ERR_UNSUPPORTED;
     }
   } else {
     return GEMM_ERR_INVALID_VALUE;
   }
   return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_run_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* stream, int64_t M,
+                              int64_t N, int64_t K, int transA, int transB, float alpha,
+                              const void* A, int64_t lda, float scale_a, const void* B,
+                              int64_t ldb, float scale_b, float beta, void* C, int64_t ldc,
+                              gemm_dtype_t a_type, gemm_dtype_t b_type, gemm_dtype_t c_type,
+                              uint32_t epilogue, const float* bias) {
+  const Args a{M, N, K, transA, transB, A, lda, B, ldb, C, ldc, a_type, b_type, c_type,
+               epilogue, bias};
+  return run_impl(h, kernel, stream, a, alpha, scale_a, scale_b, beta, C);
+}
+
+gemm_status_t gemm_run_mx_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* stream, int64_t M,
+                                 int64_t N, int64_t K, int transA, int transB, float alpha,
+                                 const void* A, int64_t lda, const uint8_t* sa, int64_t ldsa,
+                                 const void* B, int64_t ldb, const uint8_t* sb, int64_t ldsb,
+                                 float beta, void* C, int64_t ldc, gemm_dtype_t a_type,
+                                 gemm_dtype_t b_type, gemm_dtype_t c_type, uint32_t epilogue,
+                                 const float* bias) {
+  const Args a{M, N, K, transA, transB, A, lda, B, ldb, C, ldc, a_type, b_type, c_type,
+               epilogue, bias, true, sa, ldsa, sb, ldsb};
+  return run_impl(h, kernel, stream, a, alpha, 1.0f, 1.0f, beta, C);
+}
+
+gemm_status_t gemm_check_args_mx(int64_t M, int64_t N, int64_t K, int transA, int transB,
+                                 const void* A, int64_t lda, const uint8_t* sa, int64_t ldsa,
+                                 const void* B, int64_t ldb, const uint8_t* sb, int64_t ldsb,
+                                 const void* C, int64_t ldc, gemm_dtype_t a_type,
+                                 gemm_dtype_t b_type, gemm_dtype_t c_type, uint32_t epilogue,
+                                 const float* bias) {
+  const Args a{M, N, K, transA, transB, A, lda, B, ldb, C, ldc, a_type, b_type, c_type,
+               epilogue, bias, true, sa, ldsa, sb, ldsb};
+  return check(a);
+}
+
+gemm_status_t gemm_run_mx(gemm_handle_t h, void* stream, int64_t M, int64_t N, int64_t K,
+                          int transA, int transB, float alpha, const void* A, int64_t lda,
+                          const uint8_t* sa, int64_t ldsa, const void* B, int64_t ldb,
+                          const uint8_t* sb, int64_t ldsb, float beta, void* C, int64_t ldc,
+                          gemm_dtype_t a_type, gemm_dtype_t b_type, gemm_dtype_t c_type,
+                          uint32_t epilogue, const float* bias) {
+  return gemm_run_mx_kernel(h, GEMM_KERNEL_AUTO, stream, M, N, K, transA, transB, alpha, A, lda,
+                            sa, ldsa, B, ldb, sb, ldsb, beta, C, ldc, a_type, b_type, c_type,
+                            epilogue, bias);
 }
 
 gemm_status_t gemm_run(gemm_handle_t h, void* stream, int64_t M, int64_t N, int64_t K,
@@ -280,7 +406,7 @@ gemm_status_t gemm_bias_gelu(gemm_handle_t h, void* stream, int64_t M, int64_t N
   if (!C || ldc < N) return GEMM_ERR_INVALID_VALUE;
   if ((epilogue & GEMM_EPI_BIAS) && !bias) return GEMM_ERR_INVALID_VALUE;
   if ((epilogue & GEMM_EPI_BIAS) &&
-      overlaps(byte_range(C, M, N, ldc, esize(c_type)), byte_range(bias, 1, N, N, 4)))
+      overlaps(byte_range(C, M, N, ldc, ebits(c_type)), byte_range(bias, 1, N, N, 32)))
     return GEMM_ERR_ALIAS;
   DeviceGuard g(h->device);
   const hipError_t err = tgemm::launch_bias_gelu(C, ldc, (int)M, (int)N, c_type, bias, epilogue,

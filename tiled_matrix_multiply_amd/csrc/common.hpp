@@ -6,7 +6,9 @@
 
 namespace tgemm {
 
-enum DType : int { F32 = 0, F16 = 1, BF16 = 2, E4M3 = 3 };
+// E2M1 is OCP fp4: two elements per byte along the storage row, the even element in the
+// low nibble.
+enum DType : int { F32 = 0, F16 = 1, BF16 = 2, E4M3 = 3, E5M2 = 4, E2M1 = 5 };
 enum : uint32_t { EPI_BIAS = 1u, EPI_GELU = 2u };
 
 // Arguments every GEMM kernel receives (by value, in the kernel-argument segment).
@@ -20,7 +22,14 @@ struct GemmParams {
   int tiles_m, tiles_n;   // workgroup tiles along M and N
   float alpha;            // alpha * scale_a * scale_b
   float beta;
-  uint32_t epi;           // EPI_BIAS | EPI_GELU
+  uint32_t epi;           // EPI_BIAS | EPI_GELU (kernel-private flags in the upper bits)
+  // OCP microscaling (MX): E8M0 scale of row i of op(A) and k-block kb (32 elements of K) at
+  // sa[i * ldsa + kb], of column j of op(B) at sb[j * ldsb + kb]; kblocks = K / 32.  Null for
+  // per-tensor scaling (folded into alpha).
+  const uint8_t* sa;
+  const uint8_t* sb;
+  int64_t ldsa, ldsb;
+  int kblocks;
 };
 
 template <int DT> struct DTypeInfo;
@@ -28,6 +37,9 @@ template <> struct DTypeInfo<F32> { static constexpr int bytes = 4; };
 template <> struct DTypeInfo<F16> { static constexpr int bytes = 2; };
 template <> struct DTypeInfo<BF16> { static constexpr int bytes = 2; };
 template <> struct DTypeInfo<E4M3> { static constexpr int bytes = 1; };
+template <> struct DTypeInfo<E5M2> { static constexpr int bytes = 1; };
+// The matrix-core kernels see packed fp4 rows as bytes (two elements each).
+template <> struct DTypeInfo<E2M1> { static constexpr int bytes = 1; };
 
 // ------------------------------------------------------------------ element conversions --
 
@@ -50,6 +62,31 @@ __device__ __forceinline__ float e4m3_bits_to_float(uint32_t q) {
   return s ? -v : v;
 }
 
+// OCP E5M2 byte -> float, exact: exponent bias 15, subnormals m * 2^-16, exponent 31 is
+// infinity (m = 0) or NaN.
+__device__ __forceinline__ float e5m2_bits_to_float(uint32_t q) {
+  const uint32_t s = (q >> 7) & 1u, e = (q >> 2) & 31u, m = q & 3u;
+  float v;
+  if (e == 0) v = (float)m * 0x1p-16f;
+  else if (e == 31) v = m ? __builtin_nanf("") : __builtin_inff();
+  else v = __uint_as_float(((e + 112u) << 23) | (m << 21));  // (1 + m/4) * 2^(e-15)
+  return s ? -v : v;
+}
+
+// OCP E2M1 4-bit code -> float, exact: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ float e2m1_bits_to_float(uint32_t q) {
+  const uint32_t s = (q >> 3) & 1u, e = (q >> 1) & 3u, m = q & 1u;
+  const float v = e == 0 ? 0.5f * (float)m : __uint_as_float(((e + 126u) << 23) | (m << 22));
+  return s ? -v : v;
+}
+
+// OCP E8M0 block scale 2^(e - 127) (e = 255 is NaN), exact in fp32: 2^-126 and up are
+// normal numbers (exponent field e), 2^-127 is the subnormal 0x00400000.
+__device__ __forceinline__ float e8m0_to_float(uint32_t e) {
+  if (e == 255u) return __builtin_nanf("");
+  return e == 0u ? 0x1p-127f : __uint_as_float(e << 23);
+}
+
 // float -> storage (round to nearest even), returned in the low bits.
 __device__ __forceinline__ uint32_t float_to_bf16_bits(float v) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
@@ -63,7 +100,9 @@ __device__ __forceinline__ float load_as_float(const void* base, int64_t idx) {
   if constexpr (DT == F32) return reinterpret_cast<const float*>(base)[idx];
   else if constexpr (DT == F16) return f16_bits_to_float(reinterpret_cast<const uint16_t*>(base)[idx]);
   else if constexpr (DT == BF16) return bf16_bits_to_float(reinterpret_cast<const uint16_t*>(base)[idx]);
-  else return e4m3_bits_to_float(reinterpret_cast<const uint8_t*>(base)[idx]);
+  else if constexpr (DT == E4M3) return e4m3_bits_to_float(reinterpret_cast<const uint8_t*>(base)[idx]);
+  else if constexpr (DT == E5M2) return e5m2_bits_to_float(reinterpret_cast<const uint8_t*>(base)[idx]);
+  else return e2m1_bits_to_float((reinterpret_cast<const uint8_t*>(base)[idx >> 1] >> (4 * (idx & 1))) & 15u);
 }
 
 template <int CT>

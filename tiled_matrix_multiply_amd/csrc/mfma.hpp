@@ -68,18 +68,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// Wait until at most n * NL loads are outstanding, for 0 <= n <= MAXN (n is uniform; the count
-// must be an immediate, so each possible n has its own wait).
-template <int NL, int MAXN>
-__device__ __forceinline__ void wait_tiles(int n) {
-  if constexpr (MAXN > 0) {
-    if (n >= MAXN) {
-      wait_vmcnt<MAXN * NL>();
-      return;
-    }
-    wait_tiles<NL, MAXN - 1>(n);
+// Wait until at most n loads are outstanding, LO <= n <= HI (n is uniform; the count must be
+// an immediate, so the possible values are split by a binary search of uniform branches).
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm(int n) {
+  if constexpr (LO >= HI) {
+    wait_vmcnt<LO>();
   } else {
-    wait_vmcnt<0>();
+    constexpr int MID = (LO + HI + 1) / 2;
+    if (n >= MID) wait_vm<MID, HI>(n);
+    else wait_vm<LO, MID - 1>(n);
   }
 }
 
@@ -102,10 +100,14 @@ __device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, uint32_t lds_base,
 
 // ------------------------------------------------------------------------- MFMA ops --
 // Each op consumes, per lane, CPL 16-byte "chunks" of the first operand (32 rows of D) and of
-// the second operand (32 columns of D) for one k-group.  Lanes 0-31 hold the first half of the
-// group's K range for rows/columns 0-31, lanes 32-63 the second half; inside a lane, K runs in
-// order through the chunk.  Both operands use the same assignment, which is all a dot product
-// needs.  Result layout of every 32x32 op: lane l holds column l%32 of D; register r holds row
+// the second operand (32 columns of D) for one k-group of 2*CPL chunks.  Lane half h (lanes
+// 32h .. 32h+31, one row/column each) holds chunk 2x + h of the group in its x-th 16 bytes,
+// K running in order through each chunk.  Any assignment shared by both operands gives the dot
+// product; this one is the hardware's for the scaled 8-bit op, where the K block of a byte is
+// fixed by its position in the operand (bytes 16x .. 16x+15 of both lane halves form block x,
+// scaled by lane half x's scale: measured with a one-wave probe), so that block x of the
+// k-group is chunks 2x and 2x+1.  With one chunk per lane (CPL = 1) lane half h holds chunk h.
+// Result layout of every 32x32 op: lane l holds column l%32 of D; register r holds row
 // 8*(r/4) + 4*(l/32) + r%4.
 template <int DT> struct MmaOp;
 
@@ -139,17 +141,34 @@ template <> struct MmaOp<F32> {
   }
 };
 
-// fp8 E4M3 (OCP): the 32x32x64 f8f6f4 op, format code 0 (E4M3) for both operands, unit block
-// scales (E8M0 exponent 127 = 2^0); the per-tensor scales are folded into alpha instead.
-template <> struct MmaOp<E4M3> {
-  static constexpr int KG = 64, CPL = 2;
-  using Frag = u32x8;
-  __device__ static __forceinline__ f32x16 run(const Frag& x, const Frag& y, f32x16 c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, x),
-                                                           __builtin_bit_cast(i32x8, y), c, 0, 0,
-                                                           0, 127, 0, 127);
+// 8- and 4-bit inputs (OCP E4M3, E5M2, E2M1): the 32x32x64 f8f6f4 op with a format code per
+// operand and one E8M0 scale per lane and operand.  A lane holds 32 consecutive k of its row,
+// which is exactly one 32-element block of the OCP microscaling (MX) formats, so the lane's
+// scale byte is its block's scale; per-tensor scaling passes 2^0 (code 127) and folds the
+// scales into alpha.  XT is the type of the first operand (the B fragment), YT of the second.
+// KG counts staged bytes per k-group: 64 for 8-bit elements, 32 for packed fp4 (64 elements).
+template <int DT>
+constexpr int f8f6f4_format() { return DT == E4M3 ? 0 : (DT == E5M2 ? 1 : 4); }
+
+template <int XT, int YT>
+struct MmaScaled {
+  static_assert((XT == E2M1) == (YT == E2M1), "fp4 pairs only with fp4");
+  static constexpr bool FP4 = XT == E2M1;
+  static constexpr int KG = FP4 ? 32 : 64, CPL = FP4 ? 1 : 2;
+  using Frag = typename std::conditional<FP4, u32x4, u32x8>::type;
+  __device__ static __forceinline__ i32x8 widen(const Frag& x) {
+    if constexpr (FP4) return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
+    else return __builtin_bit_cast(i32x8, x);
+  }
+  __device__ static __forceinline__ f32x16 run(const Frag& x, const Frag& y, f32x16 c, int sx,
+                                               int sy) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        widen(x), widen(y), c, f8f6f4_format<XT>(), f8f6f4_format<YT>(), 0, sx, 0, sy);
   }
 };
+
+template <int DT>
+constexpr bool is_f8f6f4() { return DT == E4M3 || DT == E5M2 || DT == E2M1; }
 
 // ----------------------------------------------------------------------- configuration --
 
@@ -160,10 +179,17 @@ template <> struct MmaOp<E4M3> {
 template <int TILE>
 constexpr int default_stages() { return TILE == 128 ? 3 : 2; }
 
-template <int DT_, int TILE_, int WM_, int WN_, bool A_MN_, bool B_MN_, int S_ = default_stages<TILE_>()>
+// DT_ / BT_: types of A and B (they differ only within the 8-bit family); MX_: OCP
+// microscaling, one E8M0 scale per 32 k of each row of op(A) and column of op(B).
+template <int DT_, int TILE_, int WM_, int WN_, bool A_MN_, bool B_MN_,
+          int S_ = default_stages<TILE_>(), int BT_ = DT_, bool MX_ = false>
 struct MfmaCfg {
-  static constexpr int DT = DT_;
-  static constexpr int CT = (DT_ == E4M3) ? BF16 : DT_;
+  static constexpr int DT = DT_, BT = BT_;
+  static constexpr bool F8 = is_f8f6f4<DT_>(), MX = MX_;
+  static_assert(DT_ == BT_ || (F8 && is_f8f6f4<BT_>()), "mixed types only in the 8-bit family");
+  static_assert(!MX_ || F8, "block scales only with 8- and 4-bit inputs");
+  using Op = typename std::conditional<F8, MmaScaled<BT_, DT_>, MmaOp<DT_>>::type;
+  static constexpr int CT = F8 ? BF16 : DT_;
   static constexpr int BM = TILE_, BN = TILE_;
   static constexpr int WM = WM_, WN = WN_, NW = WM_ * WN_, NT = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
@@ -173,7 +199,12 @@ struct MfmaCfg {
   static constexpr bool A_MN = A_MN_, B_MN = B_MN_;    // operand stored contiguous along M/N
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;  // one staged K tile
   static constexpr int S = S_;  // LDS buffers per operand: K tiles kt .. kt+S-1 are resident or in flight
-  static constexpr int LDS_BYTES = S * (A_BYTES + B_BYTES);
+  // MX scales: a staged K tile covers BPT 32-element blocks (4 for 8-bit elements, 8 for
+  // packed fp4); each row's 16 consecutive scale bytes (TPC = 16 / BPT tiles) are copied as one
+  // piece into a double-buffered region of (BM + BN) rows x 16 bytes after the data stages.
+  static constexpr int BPT = (DT_ == E2M1) ? 8 : 4, TPC = 16 / BPT;
+  static constexpr int SC_OFF = S * (A_BYTES + B_BYTES), SC_BUF = (BM + BN) * 16;
+  static constexpr int LDS_BYTES = SC_OFF + (MX_ ? 2 * SC_BUF : 0);
   static_assert(S >= 2 && LDS_BYTES <= 160 * 1024, "LDS holds at most 160 KB");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is a whole number of 32x32 tiles");
 };
@@ -256,7 +287,7 @@ enum : uint32_t { FIX_A = 1u << 8, FIX_B = 1u << 9 };
 template <class C>
 __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
-  using Op = MmaOp<C::DT>;
+  using Op = typename C::Op;
   using OA = Operand<C, true>;
   using OB = Operand<C, false>;
   constexpr int ES = C::ES;
@@ -392,18 +423,18 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   // Per-lane LDS byte offsets of the fragment reads, computed once and kept opaque so that the
   // compiler holds exactly these few registers instead of materialising one address per
   // (fragment, k-group, chunk).
-  //  * K-contiguous tile: row = wbase + 32 f + lrow and chunk c = KGC g + CPL lhalf + x sit at
+  //  * K-contiguous tile: row = wbase + 32 f + lrow and chunk c = KGC g + 2 x + lhalf sit at
   //    byte row*128 + 16 (c ^ kswz(row)), and kswz(row) = s_lane ^ 4 ((wbase/32 + f) & 1) with
   //    s_lane = (lrow & 7) ^ (lrow >> 3).  So the offset is
-  //      (wbase + 32 f) * 128 + (kbase[par] ^ 16 (KGC g + x)),  par = (wbase/32 + f) & 1,
-  //    kbase[par] = lrow*128 + 16 ((CPL lhalf) ^ s_lane ^ 4 par).
+  //      (wbase + 32 f) * 128 + (kbase[par] ^ 16 (KGC g + 2 x)),  par = (wbase/32 + f) & 1,
+  //    kbase[par] = lrow*128 + 16 (lhalf ^ s_lane ^ 4 par).
   //  * M/N-contiguous tile: the swizzle depends only on k % 4 (16-bit) or k % 8 (8-bit), which is
   //    fixed per lane, so each fragment f has one base and every k-group / k-row step is a
   //    plain offset.
   constexpr int KGC = Op::KG * ES / 16;  // chunks per k-group
   const int s_lane = (lrow & 7) ^ (lrow >> 3);
   auto kbase = [&](int par) {
-    int v = lrow * 128 + 16 * ((Op::CPL * lhalf) ^ s_lane ^ (4 * par));
+    int v = lrow * 128 + 16 * (lhalf ^ s_lane ^ (4 * par));
     asm volatile("" : "+v"(v));
     return v;
   };
@@ -418,7 +449,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
     } else if constexpr (ES == 1) {
       const int q = lane >> 4, sl = lane & 15;
       const int n = wbase + f * 32 + 16 * (q & 1) + 8 * (sl & 1);
-      const int k = 32 * (q >> 1) + (sl >> 1);
+      const int k = 16 * (q >> 1) + (sl >> 1);  // lane half h: k 16h .. (see the op layout)
       v = k * O::RB + (((n >> 4) ^ O::mswz(k)) << 4) + (n & 15);
     } else {
       const int n = wbase + f * 32 + lrow;
@@ -437,7 +468,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
       const int par = ((wbase >> 5) + f) & 1;
 #pragma unroll
       for (int x = 0; x < Op::CPL; ++x) {
-        const int off = (wbase + f * 32) * 128 + (kb[par] ^ (16 * (KGC * g + x)));
+        const int off = (wbase + f * 32) * 128 + (kb[par] ^ (16 * (KGC * g + 2 * x)));
         const u32x4 v = *reinterpret_cast<const u32x4*>(s + off);
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[4 * x + e] = v[e];
@@ -454,7 +485,8 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
     } else if constexpr (ES == 1) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const uint8_t* a = s + mb[f] + (g * 64 + 8 * t) * O::RB;
+        // bytes 8t .. 8t+7: k 32 (t / 2) + 16 h + 8 (t % 2) + 0..7 of the k-group
+        const uint8_t* a = s + mb[f] + (g * 64 + 32 * (t >> 1) + 8 * (t & 1)) * O::RB;
         const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)a);
         out[2 * t] = (uint32_t)v[0];
         out[2 * t + 1] = (uint32_t)v[1];
@@ -502,18 +534,35 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   constexpr int AS = GROUPED ? C::FM : 1;   // A fragments per register set
   constexpr int BS = GROUPED ? 2 : 1;       // B register sets
   Frag af[2][AS], bf[BS][C::FN];
-  auto load_a = [&](uint32_t aoff, int g, int i, Frag& dst) {
+  // MX: the E8M0 scale byte of each fragment lane's 32-element block, read from the staged
+  // scale rows next to the fragment itself (scA / scB mirror af / bf); 127 (2^0) otherwise.
+  // Blocks past K (the last tile's zero-filled tail) take 2^0 whatever the padding holds.
+  int scA[2][AS] = {}, scB[BS][C::FN] = {};
+  int sclane = lrow * 16 + lhalf;  // this lane's byte within a 16-byte scale row
+  asm volatile("" : "+v"(sclane));
+  auto read_scale = [&](auto opnd, int wbase, int f, int g, int kt) -> int {
+    using O = decltype(opnd);
+    constexpr int ROW0 = std::is_same<O, OA>::value ? 0 : C::BM;  // A rows, then B rows
+    const int blk = kt * C::BPT + 2 * g;                           // block of lane half 0
+    const uint8_t v = smem[C::SC_OFF + ((kt / C::TPC) & 1) * C::SC_BUF +
+                           (ROW0 + wbase + 32 * f) * 16 + (kt % C::TPC) * C::BPT + 2 * g + sclane];
+    return blk + lhalf < p.kblocks ? (int)v : 127;
+  };
+  auto load_a = [&](int kt, uint32_t aoff, int g, int i, Frag& dst, int& sdst) {
     read_frag(aoff, OA{}, wm * C::WTM, i, g, kbA, mbA, dst);
+    if constexpr (C::MX) sdst = read_scale(OA{}, wm * C::WTM, i, g, kt);
   };
-  auto load_b = [&](uint32_t boff, int g, int set) {
+  auto load_b = [&](int kt, uint32_t boff, int g, int set) {
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
+    for (int j = 0; j < C::FN; ++j) {
       read_frag(boff, OB{}, wn * C::WTN, j, g, kbB, mbB, bf[set][j]);
+      if constexpr (C::MX) scB[set][j] = read_scale(OB{}, wn * C::WTN, j, g, kt);
+    }
   };
-  auto load_group = [&](uint32_t aoff, uint32_t boff, int g, int set) {
+  auto load_group = [&](int kt, uint32_t aoff, uint32_t boff, int g, int set) {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) load_a(aoff, g, i, af[set][i]);
-    load_b(boff, g, set);
+    for (int i = 0; i < C::FM; ++i) load_a(kt, aoff, g, i, af[set][i], scA[set][i]);
+    load_b(kt, boff, g, set);
   };
   // D = op(B)-fragment x op(A)-fragment: rows of D are n, columns are m, so each lane ends up
   // holding 4 consecutive n of one m (vector stores along the C row).  With the 256 x 256 tile
@@ -523,16 +572,18 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   // schedules are built to save.  Smaller grids keep their accumulators in AccVGPRs, which a
   // VGPR operand constraint would force out and back on every step, so they are not pinned.
   constexpr bool PIN = C::FM * C::FN >= 8;
-  auto mma = [&](int i, const Frag& a, int bset) {
+  auto mma = [&](int i, const Frag& a, int sa_v, int bset) {
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
-      acc[i][j] = Op::run(bf[bset][j], a, acc[i][j]);
+      if constexpr (C::MX) acc[i][j] = Op::run(bf[bset][j], a, acc[i][j], scB[bset][j], sa_v);
+      else if constexpr (C::F8) acc[i][j] = Op::run(bf[bset][j], a, acc[i][j], 127, 127);
+      else acc[i][j] = Op::run(bf[bset][j], a, acc[i][j]);
       if constexpr (PIN) asm volatile("" : "+v"(acc[i][j]));
     }
   };
   auto mma_group = [&](int set) {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) mma(i, af[set][i], set);
+    for (int i = 0; i < C::FM; ++i) mma(i, af[set][i], scA[set][i], set);
   };
   constexpr int S = G * C::FM;
   static_assert(G % 2 == 0 && S % 2 == 0, "register-set parities carry across tiles");
@@ -544,17 +595,49 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   // tile kt+1 are read while the last multiplies of tile kt keep the matrix cores busy.  A wave's
   // copies land in the order they were issued, so "tile kt+1 has landed" is a bound on the
   // number of its copies still outstanding (vmcnt): those of the tiles issued after it.
+  //
+  // MX scales: the piece of scale rows covering tiles c*TPC .. c*TPC+TPC-1 ("chunk" c, buffer
+  // c & 1) is copied just before the data of tile c*TPC, so waiting for that tile covers it.
+  // Its buffer last served tiles up to (c-1)*TPC - 1, whose scale reads precede the barrier of
+  // boundary (c-1)*TPC - 1, and chunk c is issued at boundary c*TPC - S >= (c-1)*TPC - 1.
   const int KT = (p.K + C::BKE - 1) / C::BKE;
   const bool need_fix = (p.epi & (FIX_A | FIX_B)) != 0;
-  constexpr int NL = OA::PER_WAVE + OB::PER_WAVE;  // copies per wave per K tile
+  constexpr int NL = OA::PER_WAVE + OB::PER_WAVE;  // data copies per wave per K tile
+  constexpr int NWL = (C::BM + C::BN) / 64;         // 64-row scale wave-loads per chunk
+  static_assert(!C::MX || (NWL <= C::NW && C::NW % NWL == 0 && C::TPC + 1 >= C::S),
+                "every wave issues one scale copy per chunk; chunk buffers free in time");
+  auto issue_scales = [&](int c) {
+    // wave w copies 64 rows (wave-load w % NWL; extra waves repeat a copy, writing the same
+    // bytes): row r of op(A) (then of op(B)) gives its 16 scale bytes from block 16 c on
+    const int u = (int)(wave_u % NWL);
+    const uint32_t l = (uint32_t)reinterpret_cast<uintptr_t>(smem + C::SC_OFF + (c & 1) * C::SC_BUF) + u * 1024;
+    if (64 * u < C::BM) {
+      const int64_t bytes = (int64_t)p.M * p.ldsa;
+      const i32x4 r = make_rsrc(p.sa, (uint32_t)(bytes < 0xfffffff0LL ? bytes : 0xfffffff0LL) & ~15u);
+      buffer_load_lds16(r, l, (uint32_t)((int64_t)(m0 + 64 * u + lane) * p.ldsa + 16 * c));
+    } else {
+      const int64_t bytes = (int64_t)p.N * p.ldsb;
+      const i32x4 r = make_rsrc(p.sb, (uint32_t)(bytes < 0xfffffff0LL ? bytes : 0xfffffff0LL) & ~15u);
+      buffer_load_lds16(r, l, (uint32_t)((int64_t)(n0 + 64 * u - C::BM + lane) * p.ldsb + 16 * c));
+    }
+  };
   auto issue = [&](int kt, int buf) {
+    if constexpr (C::MX)
+      if (kt % C::TPC == 0) issue_scales(kt / C::TPC);
     issue_b(kt, buf);
     issue_a(kt, buf);
   };
-  static_assert((C::S - 1) * NL < 64, "outstanding-copy counts fit the 6-bit vmcnt");
+  // Copies a wave issues for tiles t0 .. t1 (each tile's data, and its chunk of scales first).
+  auto copies = [&](int t0, int t1) {
+    int n = 0;
+    for (int t = t0; t <= t1; ++t) n += NL + ((C::MX && t % C::TPC == 0) ? 1 : 0);
+    return n;
+  };
+  constexpr int MAXC = (C::S - 1) * (NL + (C::MX ? 1 : 0));
+  static_assert(MAXC < 64, "outstanding-copy counts fit the 6-bit vmcnt");
   auto tile_boundary = [&](int kt, int abuf, int anext) {
     // tiles kt+2 .. min(kt+S-1, KT-1) may stay in flight
-    wait_tiles<NL, C::S - 1>(min(C::S - 2, KT - 2 - kt));
+    wait_vm<0, MAXC>(copies(kt + 2, min(kt + C::S - 1, KT - 1)));
     if (kt + 2 == KT && need_fix) fixup(kt + 1, anext, anext);
     __syncthreads();
     if (kt + C::S < KT) issue(kt + C::S, abuf);  // into the buffers tile kt has released
@@ -563,12 +646,12 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
   for (int t = 0; t < C::S; ++t)
     if (t < KT) issue(t, t);
-  wait_tiles<NL, C::S - 1>(min(C::S - 1, KT - 1));
+  wait_vm<0, MAXC>(copies(1, min(C::S - 1, KT - 1)));
   if (KT == 1 && need_fix) fixup(0, 0, 0);
   __syncthreads();
   int abuf = 0;  // buffer of tile kt (kt % S)
   if constexpr (GROUPED) {
-    if (KT > 0) load_group(0, 0, 0, 0);
+    if (KT > 0) load_group(0, 0, 0, 0, 0);
     for (int kt = 0; kt < KT; ++kt) {
       const uint32_t aoff = abuf * C::A_BYTES, boff = abuf * C::B_BYTES;
       const int anext = abuf + 1 == C::S ? 0 : abuf + 1;
@@ -579,18 +662,18 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
         // while the clock holds (constant operands) and neutral on random operands, where the
         // chip runs near 2.1 GHz.
         __builtin_amdgcn_iglp_opt(1);
-        load_group(aoff, boff, g + 1, (g + 1) & 1);
+        load_group(kt, aoff, boff, g + 1, (g + 1) & 1);
         mma_group(g & 1);
       }
       tile_boundary(kt, abuf, anext);
-      if (kt + 1 < KT) load_group(anext * C::A_BYTES, anext * C::B_BYTES, 0, 0);
+      if (kt + 1 < KT) load_group(kt + 1, anext * C::A_BYTES, anext * C::B_BYTES, 0, 0);
       mma_group((G - 1) & 1);
       abuf = anext;
     }
   } else {
     if (KT > 0) {
-      load_b(0, 0, 0);
-      load_a(0, 0, 0, af[0][0]);
+      load_b(0, 0, 0, 0);
+      load_a(0, 0, 0, 0, af[0][0], scA[0][0]);
     }
     for (int kt = 0; kt < KT; ++kt) {
       const uint32_t aoff = abuf * C::A_BYTES, boff = abuf * C::B_BYTES;
@@ -598,16 +681,16 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
       for (int st = 0; st < S; ++st) {
         const int g = st / C::FM, i = st % C::FM;
-        if (i == 0 && g > 0) load_b(boff, g, 0);
+        if (i == 0 && g > 0) load_b(kt, boff, g, 0);
         if (st + 1 < S) {
-          load_a(aoff, (st + 1) / C::FM, (st + 1) % C::FM, af[(st + 1) & 1][0]);
-          mma(i, af[st & 1][0], 0);
+          load_a(kt, aoff, (st + 1) / C::FM, (st + 1) % C::FM, af[(st + 1) & 1][0], scA[(st + 1) & 1][0]);
+          mma(i, af[st & 1][0], scA[st & 1][0], 0);
         } else {
           tile_boundary(kt, abuf, anext);
-          if (kt + 1 < KT) load_a(anext * C::A_BYTES, 0, 0, af[0][0]);
-          mma(i, af[st & 1][0], 0);
+          if (kt + 1 < KT) load_a(kt + 1, anext * C::A_BYTES, 0, 0, af[0][0], scA[0][0]);
+          mma(i, af[st & 1][0], scA[st & 1][0], 0);
           // the single B set is still read by the last step: refill it only afterwards
-          if (kt + 1 < KT) load_b(anext * C::B_BYTES, 0, 0);
+          if (kt + 1 < KT) load_b(kt + 1, anext * C::B_BYTES, 0, 0);
         }
       }
       abuf = anext;
@@ -748,21 +831,28 @@ hipError_t launch_mfma_cfg(GemmParams p, hipStream_t s) {
 }
 
 // Tile families: 0 -> 64x64 (2x2 waves of 32x32), 1 -> 128x128 (2x2 waves of 64x64),
-// 2 -> 256x256 (2x4 waves of 128x64).
-template <int DT, int TILE, int WM, int WN>
+// 2 -> 256x256 (2x4 waves of 128x64).  BT: type of B (differs from A only in the 8-bit
+// family); MX: block-scaled.  Packed fp4 is staged K-contiguous only (A stored M x K, B stored
+// N x K): the other layouts return an error (the host never routes them here).
+template <int DT, int TILE, int WM, int WN, int BT, bool MX>
 hipError_t launch_mfma_layout(const GemmParams& p, bool a_mn, bool b_mn, hipStream_t s) {
-  if (!a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, false>>(p, s);
-  if (!a_mn && b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, true>>(p, s);
-  if (a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, true, false>>(p, s);
-  return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, true, true>>(p, s);
+  constexpr int S = default_stages<TILE>();
+  if (!a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, false, S, BT, MX>>(p, s);
+  if constexpr (DT == E2M1) {
+    return hipErrorInvalidValue;
+  } else {
+    if (!a_mn && b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, true, S, BT, MX>>(p, s);
+    if (a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, true, false, S, BT, MX>>(p, s);
+    return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, true, true, S, BT, MX>>(p, s);
+  }
 }
 
-template <int DT>
+template <int DT, int BT = DT, bool MX = false>
 hipError_t launch_mfma_dtype(const GemmParams& p, int tile, bool a_mn, bool b_mn, hipStream_t s) {
   switch (tile) {
-    case 0: return launch_mfma_layout<DT, 64, 2, 2>(p, a_mn, b_mn, s);
-    case 1: return launch_mfma_layout<DT, 128, 2, 2>(p, a_mn, b_mn, s);
-    case 2: return launch_mfma_layout<DT, 256, 2, 4>(p, a_mn, b_mn, s);
+    case 0: return launch_mfma_layout<DT, 64, 2, 2, BT, MX>(p, a_mn, b_mn, s);
+    case 1: return launch_mfma_layout<DT, 128, 2, 2, BT, MX>(p, a_mn, b_mn, s);
+    case 2: return launch_mfma_layout<DT, 256, 2, 4, BT, MX>(p, a_mn, b_mn, s);
     default: return hipErrorInvalidValue;
   }
 }

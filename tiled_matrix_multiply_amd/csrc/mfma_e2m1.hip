@@ -1,0 +1,15 @@
+// Matrix-core GEMM instantiations for packed fp4 (OCP E2M1) inputs, per-tensor and block-scaled
+// (MX).  Packed operands are staged K-contiguous only: A stored M x K, B stored N x K.
+#include "mfma.hpp"
+
+namespace tgemm {
+
+hipError_t launch_mfma_e2m1(const GemmParams& p, int tile, bool a_mn, bool b_mn, hipStream_t s) {
+  return launch_mfma_dtype<E2M1, E2M1, false>(p, tile, a_mn, b_mn, s);
+}
+
+hipError_t launch_mfma_mx_e2m1(const GemmParams& p, int tile, bool a_mn, bool b_mn, hipStream_t s) {
+  return launch_mfma_dtype<E2M1, E2M1, true>(p, tile, a_mn, b_mn, s);
+}
+
+}  // namespace tgemm

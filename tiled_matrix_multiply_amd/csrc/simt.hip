@@ -9,14 +9,15 @@
 //
 // It serves as the library's fallback for any layout and alignment, and as the no-matrix-core
 // baseline the matrix-core kernels are measured against.  Inputs of every type are decoded to
-// fp32 while staging; products are accumulated with fp32 FMA.
+// fp32 while staging (with their E8M0 block scale when the call is block-scaled); products are
+// accumulated with fp32 FMA.
 #include "common.hpp"
 
 namespace tgemm {
 
 constexpr int TS = 16;
 
-template <int AT, int CT>
+template <int AT, int BT, int CT>
 __global__ __launch_bounds__(TS * TS) void gemm_simt_kernel(GemmParams p, int transA, int transB) {
   __shared__ float As[TS][TS + 1];
   __shared__ float Bs[TS][TS + 1];
@@ -28,10 +29,14 @@ __global__ __launch_bounds__(TS * TS) void gemm_simt_kernel(GemmParams p, int tr
     // op(A)[row, k0 + tx] and op(B)[k0 + ty, col], zero outside the matrices.
     const int ka = k0 + tx, kb = k0 + ty;
     float a = 0.0f, b = 0.0f;
-    if (row < p.M && ka < p.K)
+    if (row < p.M && ka < p.K) {
       a = load_as_float<AT>(p.A, transA ? (int64_t)ka * p.lda + row : (int64_t)row * p.lda + ka);
-    if (kb < p.K && col < p.N)
-      b = load_as_float<AT>(p.B, transB ? (int64_t)col * p.ldb + kb : (int64_t)kb * p.ldb + col);
+      if (p.sa) a *= e8m0_to_float(p.sa[(int64_t)row * p.ldsa + (ka >> 5)]);
+    }
+    if (kb < p.K && col < p.N) {
+      b = load_as_float<BT>(p.B, transB ? (int64_t)col * p.ldb + kb : (int64_t)kb * p.ldb + col);
+      if (p.sb) b *= e8m0_to_float(p.sb[(int64_t)col * p.ldsb + (kb >> 5)]);
+    }
     As[ty][tx] = a;
     Bs[ty][tx] = b;
     __syncthreads();  // every element written before any is read
@@ -47,22 +52,28 @@ __global__ __launch_bounds__(TS * TS) void gemm_simt_kernel(GemmParams p, int tr
   }
 }
 
-template <int AT, int CT>
+template <int AT, int BT, int CT>
 static hipError_t launch(const GemmParams& p, int transA, int transB, hipStream_t s) {
   dim3 grid((p.N + TS - 1) / TS, (p.M + TS - 1) / TS);
-  hipLaunchKernelGGL((gemm_simt_kernel<AT, CT>), grid, dim3(TS * TS), 0, s, p, transA, transB);
+  hipLaunchKernelGGL((gemm_simt_kernel<AT, BT, CT>), grid, dim3(TS * TS), 0, s, p, transA, transB);
   return hipGetLastError();
 }
 
 // Launch for a supported (A type, C type) pair.  Grid: one 16x16 workgroup per output tile,
 // counted in workgroups (not threads); y indexes tile rows, x tile columns.
-hipError_t launch_simt(const GemmParams& p, int a_type, int transA, int transB, hipStream_t s) {
+hipError_t launch_simt(const GemmParams& p, int a_type, int b_type, int transA, int transB,
+                       hipStream_t s) {
   if (p.M > 65535 * TS) return hipErrorInvalidValue;  // grid.y limit
-  switch (a_type) {
-    case F32: return launch<F32, F32>(p, transA, transB, s);
-    case F16: return launch<F16, F16>(p, transA, transB, s);
-    case BF16: return launch<BF16, BF16>(p, transA, transB, s);
-    case E4M3: return launch<E4M3, BF16>(p, transA, transB, s);
+  const int pair = a_type * 8 + b_type;
+  switch (pair) {
+    case F32 * 8 + F32: return launch<F32, F32, F32>(p, transA, transB, s);
+    case F16 * 8 + F16: return launch<F16, F16, F16>(p, transA, transB, s);
+    case BF16 * 8 + BF16: return launch<BF16, BF16, BF16>(p, transA, transB, s);
+    case E4M3 * 8 + E4M3: return launch<E4M3, E4M3, BF16>(p, transA, transB, s);
+    case E4M3 * 8 + E5M2: return launch<E4M3, E5M2, BF16>(p, transA, transB, s);
+    case E5M2 * 8 + E4M3: return launch<E5M2, E4M3, BF16>(p, transA, transB, s);
+    case E5M2 * 8 + E5M2: return launch<E5M2, E5M2, BF16>(p, transA, transB, s);
+    case E2M1 * 8 + E2M1: return launch<E2M1, E2M1, BF16>(p, transA, transB, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "TFLOP/s & % MFMA peak: bf16 GEMM+bias+GELU 4096³; fp32/fp16/fp8 sweeps"
 # MI355X published dense peaks (256 CUs at 2.4 GHz).
-PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2}
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2,
+               "e2m1": 10066.3}
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_bf16_bias_gelu_4096.txt")
 
@@ -86,6 +87,15 @@ class Cell:
             self.B.data_ptr(), p.ldb, self.C.data_ptr(), p.ldc, dt[p.a_type], dt[p.b_type],
             dt[p.c_type], epi, args[-1])]
         run = tmm.library().gemm_run
+        if p.mx:
+            # OCP MX block scales: one E8M0 byte per 32 k of each row of op(A) / column of op(B)
+            self.sa, self.sb = dev(p.sa_blk), dev(p.sb_blk)
+            args = (p.M, p.N, p.K, int(p.trans_a), int(p.trans_b), float(p.alpha),
+                    self.A.data_ptr(), p.lda, self.sa.data_ptr(), p.ldsa, self.B.data_ptr(),
+                    p.ldb, self.sb.data_ptr(), p.ldsb, float(p.beta), self.C.data_ptr(), p.ldc,
+                    dt[p.a_type], dt[p.b_type], dt[p.c_type], epi,
+                    self.bias.data_ptr() if self.bias is not None else None)
+            run = tmm.library().gemm_run_mx
         bias_gelu = tmm.library().gemm_bias_gelu
         post = (h, s, p.M, p.N, self.C.data_ptr(), p.ldc, dt[p.c_type], args[-1], p.epilogue)
 
@@ -123,8 +133,10 @@ class Cell:
     def algorithmic_bytes(self) -> int:
         p = self.p
         import workloads as W
-        es, cs = W.ESIZE[p.a_type], W.ESIZE[p.c_type]
-        b = p.M * p.K * es + p.K * p.N * es + p.M * p.N * cs
+        cs = W.ESIZE[p.c_type]
+        b = int(p.M * p.K * W.ESIZE[p.a_type] + p.K * p.N * W.ESIZE[p.b_type]) + p.M * p.N * cs
+        if p.mx:
+            b += p.sa_blk.size + p.sb_blk.size
         if p.beta != 0:
             b += p.M * p.N * cs
         if p.bias is not None:
@@ -316,6 +328,9 @@ def main():
             cell(f"bf16 GEMM then bias+GELU {n}", p, "bf16", unfused=True)
         cell("fp8 e4m3 4096 (scaled, bf16 out)", W.fp8_4096(4096), "e4m3")
         cell("bf16 4096 (fp8 twin)", W.bf16_twin_of_fp8(4096), "bf16")
+        cell("fp8 e5m2 4096 (scaled, bf16 out)", W.e5m2_4096(4096), "e5m2")
+        cell("mxfp8 e4m3 4096 (E8M0 / 32 k)", W.mxfp8_4096(4096), "e4m3")
+        cell("mxfp4 e2m1 4096 (E8M0 / 32 k)", W.mxfp4_4096(4096), "e2m1")
 
     cpu = None
     if not args.no_cpu:

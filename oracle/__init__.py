@@ -9,8 +9,10 @@ the passages of the pages it follows.
 Parity pins (tests/test_oracle.py): exact brute force with fractions.Fraction on every shape in
 {1..4}^3, identity and permutation matrices, rank-1 closed forms, alpha/beta linearity,
 A*B == (B^T A^T)^T, an exhaustive OCP E4M3 table, bf16 ties-to-even, closed-form GELU values, and
-a numpy float64 matmul cross-check, exhaustive OCP E5M2 / E2M1 / E8M0 tables, and exact
-block-scaled (MX) brute force.
+a numpy float64 matmul cross-check, exhaustive OCP E5M2 / E2M1 / E8M0 tables, exact
+block-scaled (MX) brute force, and for the group-quantized product (tests/test_oracle_q.py)
+exact brute force, the unit-scale reduction to the plain product, nibble order, group
+locality and offset-only closed forms.
 """
 from __future__ import annotations
 
@@ -62,6 +64,12 @@ def lib():
         L.oracle_gemm_mx.restype = _int
         L.oracle_gemm_mx_points.argtypes = _PROBLEM + _MX + [_i64, _vp, _vp, _vp, _vp]
         L.oracle_gemm_mx_points.restype = _int
+        _Q = [_i64, _i64, _i64, _dbl, _vp, _i64, _int, _vp, _i64, _int, _i64, _vp, _vp, _i64,
+              _int, _dbl, _vp, _i64, _int, ctypes.c_uint, _vp]
+        L.oracle_qgemm.argtypes = _Q + [_vp, _vp]
+        L.oracle_qgemm.restype = _int
+        L.oracle_qgemm_points.argtypes = _Q + [_i64, _vp, _vp, _vp, _vp]
+        L.oracle_qgemm_points.restype = _int
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = _int
         _lib = L
@@ -189,6 +197,49 @@ def gemm_points(p, rows: np.ndarray, cols: np.ndarray) -> Tuple[np.ndarray, np.n
     del keep
     if rc != 0:
         raise ValueError(f"oracle_gemm_points failed: {rc}")
+    return Cref, D
+
+
+def _q_args(q):
+    """(keep, args) for a group-quantized problem with the fields of workloads.QProblem."""
+    X = np.ascontiguousarray(q.X)
+    W = np.ascontiguousarray(q.Wq, dtype=np.uint8)
+    S = np.ascontiguousarray(q.scales)
+    O = np.ascontiguousarray(q.offsets)
+    C = np.ascontiguousarray(q.C)
+    bias = None if q.bias is None else np.ascontiguousarray(q.bias, dtype=np.float32)
+    keep = (X, W, S, O, C, bias)
+    args = (q.M, q.N, q.K, float(q.alpha), _ptr(X), q.ldx, TYPE_CODE[q.x_type], _ptr(W),
+            W.shape[1], int(q.bits), int(q.group), _ptr(S), _ptr(O), S.shape[1],
+            TYPE_CODE[q.x_type], float(q.beta), _ptr(C) if q.beta != 0.0 else None, q.N,
+            TYPE_CODE[q.x_type], int(q.epilogue), _ptr(bias))
+    return keep, args
+
+
+def qgemm(q) -> Tuple[np.ndarray, np.ndarray]:
+    """(Cref, D), each M x N float64, for C = epi(alpha X W^T + beta C + bias) with W affine
+    group-quantized (oracle.c: w = s*q + o per row and group of G consecutive k)."""
+    keep, args = _q_args(q)
+    Cref = np.empty((q.M, q.N), dtype=np.float64)
+    D = np.empty((q.M, q.N), dtype=np.float64)
+    rc = lib().oracle_qgemm(*args, _ptr(Cref), _ptr(D))
+    del keep
+    if rc != 0:
+        raise ValueError(f"oracle_qgemm failed: {rc}")
+    return Cref, D
+
+
+def qgemm_points(q, rows: np.ndarray, cols: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """(Cref, D) of the quantized product at the listed entries, each computed on its own."""
+    keep, args = _q_args(q)
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    c = np.ascontiguousarray(cols, dtype=np.int64)
+    Cref = np.empty(r.size, dtype=np.float64)
+    D = np.empty(r.size, dtype=np.float64)
+    rc = lib().oracle_qgemm_points(*args, r.size, _ptr(r), _ptr(c), _ptr(Cref), _ptr(D))
+    del keep
+    if rc != 0:
+        raise ValueError(f"oracle_qgemm_points failed: {rc}")
     return Cref, D
 
 

@@ -312,6 +312,140 @@ int oracle_gemm_mx_points(PROBLEM_ARGS, MX_ARGS, int64_t npts, const int64_t* ro
   return run_points(&p, npts, rows, cols, Cref, D);
 }
 
+/* ---------------------------------------------------------------------------------------
+ * Affine group-quantized weights (the quantized matmul the "X3" page names as the main LLM
+ * workload: a memory-bound matrix-vector product for decode and a matrix product for prefill,
+ * with dequantisation fused into the multiply-add, section 7).  The page fixes no format; the
+ * reading taken here:
+ *
+ *   x(i,k) = dec(X[i*ldx + k])                                  activations, f16 or bf16
+ *   q(j,k) = bits == 8 ? Wq[j*ldw + k]                          unsigned codes, row j of W,
+ *                      : (Wq[j*ldw + k/2] >> 4*(k%2)) & 15      low nibble first
+ *   w(j,k) = s(j, k/G) * q(j,k) + o(j, k/G)                     s, o: f16 or bf16, one per
+ *                                                               G consecutive k of a row
+ *   S(i,j) = sum_k x(i,k) w(j,k),  D(i,j) = sum_k |x(i,k) w(j,k)|   double, k ascending
+ *   Cref   = epi(alpha*S + beta*C_in + bias)                    as for the plain product
+ *
+ * that is C = X W^T with W (N x K) dequantised.  s*q is exact in double (at most 11 + 8
+ * significant bits) and so is s*q + o whenever the two terms are within 2^34 of each other in
+ * magnitude, which holds for every generated input; the products with x are then exact too.
+ */
+typedef struct {
+  const uint8_t* W;
+  int64_t ldw; /* bytes per row of W */
+  int bits;
+  int64_t G;
+  const uint8_t *S, *O;
+  int64_t ldg; /* scales / offsets per row */
+  int st;
+} qweights_t;
+
+static int qcheck(const problem_t* p, const qweights_t* q) {
+  if (check(p)) return -1;
+  if (p->at != OR_F16 && p->at != OR_BF16) return -1;
+  if (q->st != OR_F16 && q->st != OR_BF16) return -1;
+  if (q->bits != 4 && q->bits != 8) return -1;
+  if (q->G <= 0 || p->K % q->G != 0) return -1;
+  if (p->K > 0 && (!q->W || !q->S || !q->O)) return -1;
+  if (q->ldw * 8 < p->K * q->bits || q->ldg < p->K / q->G) return -1;
+  return 0;
+}
+
+static double q_weight(const qweights_t* q, int64_t j, int64_t k) {
+  const uint8_t* row = q->W + j * q->ldw;
+  const unsigned v = q->bits == 8 ? row[k] : (unsigned)((row[k >> 1] >> (4 * (k & 1))) & 15);
+  const int64_t g = j * q->ldg + k / q->G;
+  return dec_one(q->st, q->S, g) * (double)v + dec_one(q->st, q->O, g);
+}
+
+static int run_q(const problem_t* p, const qweights_t* q, int64_t npts, const int64_t* rows,
+                 const int64_t* cols, double* Cref, double* D) {
+  if (qcheck(p, q)) return -1;
+  if (!rows) { /* every entry: W^T decoded once as a K x N matrix, then i-k-j */
+    if (p->M == 0 || p->N == 0) return 0;
+    double* w = (double*)malloc(sizeof(double) * (size_t)(p->K > 0 ? p->K : 1) * (size_t)p->N);
+    if (!w) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < p->N; ++j)
+      for (int64_t k = 0; k < p->K; ++k) w[k * p->N + j] = q_weight(q, j, k);
+    int fail = 0;
+#pragma omp parallel
+    {
+      double* sv = (double*)malloc(sizeof(double) * (size_t)p->N);
+      double* dv = (double*)malloc(sizeof(double) * (size_t)p->N);
+      if (!sv || !dv) {
+#pragma omp atomic write
+        fail = 1;
+      } else {
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < p->M; ++i) {
+          for (int64_t j = 0; j < p->N; ++j) { sv[j] = 0.0; dv[j] = 0.0; }
+          for (int64_t k = 0; k < p->K; ++k) {
+            const double x = dec_one(p->at, p->A, i * p->lda + k);
+            const double* wr = w + k * p->N;
+            for (int64_t j = 0; j < p->N; ++j) {
+              const double prod = x * wr[j];
+              sv[j] += prod;
+              dv[j] += fabs(prod);
+            }
+          }
+          for (int64_t j = 0; j < p->N; ++j) {
+            Cref[i * p->N + j] = apply_epilogue(p, i, j, sv[j]);
+            D[i * p->N + j] = dv[j];
+          }
+        }
+      }
+      free(sv);
+      free(dv);
+    }
+    free(w);
+    return fail ? -2 : 0;
+  }
+  for (int64_t t = 0; t < npts; ++t)
+    if (rows[t] < 0 || rows[t] >= p->M || cols[t] < 0 || cols[t] >= p->N) return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < npts; ++t) {
+    const int64_t i = rows[t], j = cols[t];
+    double sv = 0.0, dv = 0.0;
+    for (int64_t k = 0; k < p->K; ++k) {
+      const double prod = dec_one(p->at, p->A, i * p->lda + k) * q_weight(q, j, k);
+      sv += prod;
+      dv += fabs(prod);
+    }
+    Cref[t] = apply_epilogue(p, i, j, sv);
+    D[t] = dv;
+  }
+  return 0;
+}
+
+#define Q_ARGS                                                                           \
+  int64_t M, int64_t N, int64_t K, double alpha, const void* X, int64_t ldx, int x_type, \
+      const void* Wq, int64_t ldw, int bits, int64_t group, const void* scales,          \
+      const void* offsets, int64_t ldg, int s_type, double beta, const void* Cin,        \
+      int64_t ldc, int c_type, unsigned epilogue, const float* bias
+
+#define FILL_Q(p, q)                                                                          \
+  problem_t p = {M, N, K, 0, 0, alpha, 1.0, 1.0, beta, (const uint8_t*)X, NULL,              \
+                 (const uint8_t*)Cin, ldx, 0, ldc, x_type, x_type, c_type, epilogue, bias,   \
+                 NULL, NULL, 0, 0};                                                          \
+  qweights_t q = {(const uint8_t*)Wq, ldw, bits, group, (const uint8_t*)scales,              \
+                  (const uint8_t*)offsets, ldg, s_type}
+
+/* C = epi(alpha * X W^T + beta * C_in + bias) with W group-quantized (above): full M x N. */
+int oracle_qgemm(Q_ARGS, double* Cref, double* D) {
+  FILL_Q(p, q);
+  p.B = q.W; /* only so that check() sees a non-null B when K > 0 */
+  return run_q(&p, &q, 0, NULL, NULL, Cref, D);
+}
+
+/* The same at selected entries (rows[t], cols[t]). */
+int oracle_qgemm_points(Q_ARGS, int64_t npts, const int64_t* rows, const int64_t* cols,
+                        double* Cref, double* D) {
+  FILL_Q(p, q);
+  p.B = q.W;
+  return run_q(&p, &q, npts, rows, cols, Cref, D);
+}
+
 /* Number of OpenMP threads a parallel region of the oracle uses. */
 int oracle_num_threads(void) {
   int n = 1;

@@ -425,3 +425,113 @@ def mxfp4_4096(n: int = 4096) -> Problem:
     out, seed 5."""
     return make_problem(n, n, n, a_type="e2m1", c_type="bf16", trans_b=True, seed=5, mx=True,
                         dist_a=("normal", 1.0), dist_b=("normal", 1.0), name=f"mxfp4_{n}")
+
+
+# --------------------------------------------------------------------------------------------
+# Group-quantized weights (C = X W^T with W stored as affine codes; see oracle.c for the
+# definition): the decode matrix-vector product and the prefill matrix product
+# --------------------------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class QProblem:
+    """Activations X (M x K, row-major, ldx = K, storage of x_type), codes Wq (N rows of
+    K * bits / 8 bytes, 4-bit codes two per byte with the low nibble first), scales and offsets
+    (N x K / group, storage of x_type) such that w[j, k] = s[j, k // G] * q[j, k] + o[j, k // G];
+    C (M x N, x_type) holds C_in (zero when beta == 0)."""
+    name: str
+    M: int
+    N: int
+    K: int
+    bits: int
+    group: int
+    x_type: str
+    alpha: float
+    beta: float
+    epilogue: int
+    X: np.ndarray
+    Wq: np.ndarray
+    scales: np.ndarray
+    offsets: np.ndarray
+    C: np.ndarray
+    bias: Optional[np.ndarray]
+    recipe: dict = dataclasses.field(default_factory=dict)
+
+    @property
+    def ldx(self) -> int:
+        return self.K
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.M * self.N * self.K
+
+    def weight_bytes(self) -> int:
+        return int(self.Wq.nbytes + self.scales.nbytes + self.offsets.nbytes)
+
+
+def q_codes(w: np.ndarray, bits: int, group: int, x_type: str):
+    """Affine group quantization of a rows x K float64 matrix, one (scale, offset) per `group`
+    consecutive values of a row: offset o = min, scale s = (max - min) / (2^bits - 1), both
+    rounded to x_type; codes q = round((w - o) / s) clipped to [0, 2^bits - 1] (q = 0 where
+    s = 0).  Returns (uint8 codes rows x K, scales, offsets as x_type storage)."""
+    rows, K = w.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    blk = w.reshape(rows, K // group, group)
+    lo, hi = blk.min(axis=2), blk.max(axis=2)
+    top = (1 << bits) - 1
+    S = encode((hi - lo) / top, x_type)
+    O = encode(lo, x_type)
+    dec = (lambda v: v.view(np.float16).astype(np.float64)) if x_type == "f16" else \
+          (lambda v: (v.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    s, o = dec(S), dec(O)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s[..., None] > 0, np.rint((blk - o[..., None]) / s[..., None]), 0.0)
+    q = np.clip(q, 0, top).astype(np.uint8).reshape(rows, K)
+    return q, S, O
+
+
+def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
+    """Store codes: 8-bit one per byte; 4-bit two per byte along the row, low nibble first."""
+    if bits == 8:
+        return np.ascontiguousarray(q, dtype=np.uint8)
+    if bits == 4:
+        return pack_e2m1(q)
+    raise ValueError(f"bits must be 4 or 8, not {bits}")
+
+
+def make_qproblem(M: int, N: int, K: int, *, bits: int = 4, group: int = 64,
+                  x_type: str = "bf16", alpha: float = 1.0, beta: float = 0.0,
+                  epilogue: int = EPI_NONE, seed: int = 0, x_std: float = 1.0,
+                  w_std: Optional[float] = None, bias_std: float = 0.1,
+                  name: str = "") -> QProblem:
+    """Seeded problem: X ~ N(0, x_std^2), W ~ N(0, w_std^2) (default 1/K) quantized by q_codes,
+    C_in ~ U[-1, 1] when beta != 0, bias ~ N(0, bias_std^2) with the BIAS epilogue.  Draw
+    order: X, W, C_in, bias."""
+    if x_type not in ("bf16", "f16"):
+        raise ValueError("activations are bf16 or f16")
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0.0, x_std, size=(M, K))
+    w = rng.normal(0.0, w_std if w_std is not None else 1.0 / np.sqrt(K), size=(N, K))
+    c_in = rng.uniform(-1.0, 1.0, size=(M, N)) if beta != 0.0 else None
+    bias = rng.normal(0.0, bias_std, size=N).astype(np.float32) if epilogue & EPI_BIAS else None
+    q, S, O = q_codes(w, bits, group, x_type)
+    C = encode(c_in, x_type) if c_in is not None else np.zeros((M, N), dtype=STORAGE[x_type])
+    recipe = dict(name=name, M=M, N=N, K=K, bits=bits, group=group, x_type=x_type, alpha=alpha,
+                  beta=beta, epilogue=epilogue, seed=seed, x_std=x_std, w_std=w_std,
+                  bias_std=bias_std, rng="numpy.default_rng(PCG64)", order="X,W,C_in,bias")
+    return QProblem(name=name or f"q{bits}_{M}x{N}x{K}", M=M, N=N, K=K, bits=bits, group=group,
+                    x_type=x_type, alpha=float(alpha), beta=float(beta), epilogue=epilogue,
+                    X=encode(x, x_type), Wq=pack_codes(q, bits), scales=S, offsets=O, C=C,
+                    bias=bias, recipe=recipe)
+
+
+def q4_decode(N: int = 28672, K: int = 8192, seed: int = 6) -> QProblem:
+    """Decode step of a large-model MLP projection: one token (M = 1), 4-bit weights in groups
+    of 64, bf16 activations and output.  N x K = 28672 x 8192 is the up-projection shape of the
+    70B-class open models: 117 MiB of codes and 7.3 MiB of scales and offsets per matrix."""
+    return make_qproblem(1, N, K, bits=4, group=64, seed=seed, name=f"q4_decode_{N}x{K}")
+
+
+def q4_prefill(n: int = 4096, seed: int = 7) -> QProblem:
+    """Prefill: M = N = K = n, 4-bit weights in groups of 64, bf16 activations and output."""
+    return make_qproblem(n, n, n, bits=4, group=64, seed=seed, name=f"q4_prefill_{n}")

@@ -146,6 +146,61 @@ class Cell:
         return b
 
 
+class QCell:
+    """Device-resident operands of one group-quantized workload.  `copies` > 1 keeps that many
+    copies of the weights (codes, scales, offsets) and steps through them, so that a launch
+    reads its weights from HBM rather than from the 256 MB last-level cache."""
+
+    def __init__(self, g, q, copies: int = 1):
+        import torch
+        import tiled_matrix_multiply_amd as tmm
+
+        def dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to("cuda:0")
+
+        self.p = q
+        self.X, self.C = dev(q.X), dev(q.C)
+        self.bias = dev(q.bias) if q.bias is not None else None
+        self.W = [(dev(q.Wq), dev(q.scales), dev(q.offsets)) for _ in range(copies)]
+        self.stream = torch.cuda.current_stream()
+        s = self.stream.cuda_stream
+        h = g.handle
+        run = tmm.library().gemm_run_q
+        bptr = self.bias.data_ptr() if self.bias is not None else None
+        xt = tmm.DTYPE[q.x_type]
+        w0 = self.W[0]
+        self.kernel = tmm.KERNEL_NAME[tmm.gemm_select_kernel_q(
+            h, q.M, q.N, q.K, self.X.data_ptr(), q.ldx, w0[0].data_ptr(), q.Wq.shape[1], q.bits,
+            q.group, w0[1].data_ptr(), w0[2].data_ptr(), q.scales.shape[1], self.C.data_ptr(),
+            q.N, xt, q.epilogue, bptr)]
+        self.args = [(h, s, q.M, q.N, q.K, float(q.alpha), self.X.data_ptr(), q.ldx,
+                      w[0].data_ptr(), q.Wq.shape[1], q.bits, q.group, w[1].data_ptr(),
+                      w[2].data_ptr(), q.scales.shape[1], float(q.beta), self.C.data_ptr(), q.N,
+                      xt, q.epilogue, bptr) for w in self.W]
+        self.i = 0
+
+        def step():
+            st = run(*self.args[self.i])
+            self.i = (self.i + 1) % len(self.args)
+            if st != 0:
+                raise RuntimeError(f"gemm_run_q: {tmm.gemm_status_string(st)}")
+        self.step = step
+
+    time = Cell.time
+
+    def algorithmic_bytes(self) -> int:
+        q = self.p
+        b = q.weight_bytes() + q.X.nbytes + q.M * q.N * 2
+        if q.beta != 0:
+            b += q.M * q.N * 2
+        if q.bias is not None:
+            b += 4 * q.N
+        return int(b)
+
+
 def summarize(name, cell: Cell, ms: np.ndarray, dtype: str) -> dict:
     p = cell.p
     med = float(np.median(ms))
@@ -331,6 +386,17 @@ def main():
         cell("fp8 e5m2 4096 (scaled, bf16 out)", W.e5m2_4096(4096), "e5m2")
         cell("mxfp8 e4m3 4096 (E8M0 / 32 k)", W.mxfp8_4096(4096), "e4m3")
         cell("mxfp4 e2m1 4096 (E8M0 / 32 k)", W.mxfp4_4096(4096), "e2m1")
+        # Quantized decode: one token through a 28672 x 8192 projection with 4-bit weights in
+        # groups of 64; three weight copies (375 MB) are cycled so that every launch streams
+        # its weights from HBM.  Bound by HBM: GB/s against 8 TB/s is its roofline.
+        qc = QCell(g, W.q4_decode(), copies=3)
+        row = summarize("q4 decode 1x28672x8192 (G=64)", qc, qc.time(R), "bf16")
+        row["pct_hbm"] = round(100 * row["gbs"] / PEAK_HBM_GBS, 2)
+        print(f"[bench] {'':34s} {row['pct_hbm']:.1f}% of HBM peak "
+              f"({qc.algorithmic_bytes() / 1e6:.1f} MB per launch)", file=sys.stderr, flush=True)
+        sweeps.append(row)
+        del qc
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:

@@ -94,7 +94,11 @@ typedef enum gemm_kernel {
                                section 2, translated to HIP).  Any alignment. */
   GEMM_KERNEL_MFMA_64 = 2,  /* matrix-core kernel, 64x64 workgroup tile, 4 wavefronts */
   GEMM_KERNEL_MFMA_128 = 3, /* matrix-core kernel, 128x128 workgroup tile, 4 wavefronts */
-  GEMM_KERNEL_MFMA_256 = 4  /* matrix-core kernel, 256x256 workgroup tile, 8 wavefronts */
+  GEMM_KERNEL_MFMA_256 = 4, /* matrix-core kernel, 256x256 workgroup tile, 8 wavefronts */
+  GEMM_KERNEL_QGEMV = 5,    /* gemm_run_q only: matrix-vector kernel for a few activation rows,
+                               bound by the bandwidth of the weight codes */
+  GEMM_KERNEL_QMFMA = 6     /* gemm_run_q only: matrix-core kernel that dequantises the codes
+                               in registers (prefill) */
 } gemm_kernel_t;
 
 typedef struct gemm_handle* gemm_handle_t;
@@ -198,6 +202,63 @@ GEMM_API int gemm_select_kernel(gemm_handle_t h, int64_t M, int64_t N, int64_t K
 GEMM_API gemm_status_t gemm_bias_gelu(gemm_handle_t h, void* stream, int64_t M, int64_t N, void* C,
                              int64_t ldc, gemm_dtype_t c_type, const float* bias,
                              uint32_t epilogue);
+
+/* Quantized weights: the matrix-vector product of decode and the matrix product of prefill
+ * with dequantisation fused into the multiply-add ("X3: Metal GEMM", section 7, which names
+ * these as the main workload of LLMs on the GPU without fixing a format).  The format read
+ * here is affine group quantization of the weight matrix W (N x K, one row per output):
+ *
+ *     w[j][k] = scales[j * ldg + k / group] * q[j][k] + offsets[j * ldg + k / group]
+ *     C = epi(alpha * X W^T + beta * C [+ bias])        (C is M x N, X is M x K)
+ *
+ * X: DEVICE pointer, M x K activations, row-major, ldx >= K, type x_type (GEMM_F16 or
+ *    GEMM_BF16).  C, scales and offsets have the same type; bias (if any) is fp32[N].
+ * Wq: DEVICE pointer, N rows of codes, ldw bytes apart.  bits = 8: one unsigned code per byte
+ *    (ldw >= K).  bits = 4: two codes per byte along the row, code k in byte k / 2, in the low
+ *    nibble when k is even (ldw >= K / 2, K even).
+ * scales, offsets: DEVICE pointers, N rows of ldg >= K / group values.  group >= 1 and
+ *    K % group == 0.
+ * All buffers are owned by the caller; nothing is allocated.  Asynchronous on `stream`.
+ * Errors: as gemm_run (C overlapping X, Wq, scales, offsets or bias is GEMM_ERR_ALIAS), plus
+ * GEMM_ERR_INVALID_VALUE for bits not 4 or 8, group < 1, K % group != 0, an odd K with 4-bit
+ * codes, or ldx / ldw / ldg too small; GEMM_ERR_UNSUPPORTED for an x_type other than F16 / BF16.
+ * Kernel choice (AUTO): GEMM_KERNEL_QGEMV for M <= 4 when its staged activations fit 64 KiB
+ * of LDS, GEMM_KERNEL_QMFMA otherwise, each when its alignment needs hold (below), else
+ * GEMM_KERNEL_SIMT (one output per thread, any alignment). */
+GEMM_API gemm_status_t gemm_run_q(gemm_handle_t h, void* stream, int64_t M, int64_t N,
+                                  int64_t K, float alpha, const void* X, int64_t ldx,
+                                  const uint8_t* Wq, int64_t ldw, int bits, int64_t group,
+                                  const void* scales, const void* offsets, int64_t ldg,
+                                  float beta, void* C, int64_t ldc, gemm_dtype_t x_type,
+                                  uint32_t epilogue, const float* bias);
+
+/* gemm_run_q with an explicit kernel: GEMM_KERNEL_SIMT, GEMM_KERNEL_QGEMV (needs Wq and ldw
+ * 16-byte aligned and group a multiple of 32 (4-bit) or 16 (8-bit)), or GEMM_KERNEL_QMFMA
+ * (needs X, Wq, C 16-byte aligned, ldx a multiple of 8, ldw a multiple of 16, ldc a multiple of
+ * 4 and group a multiple of 64 (4-bit) or 32 (8-bit)).  Any other kernel, or one whose needs do
+ * not hold, returns GEMM_ERR_UNSUPPORTED. */
+GEMM_API gemm_status_t gemm_run_q_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* stream,
+                                         int64_t M, int64_t N, int64_t K, float alpha,
+                                         const void* X, int64_t ldx, const uint8_t* Wq,
+                                         int64_t ldw, int bits, int64_t group,
+                                         const void* scales, const void* offsets, int64_t ldg,
+                                         float beta, void* C, int64_t ldc, gemm_dtype_t x_type,
+                                         uint32_t epilogue, const float* bias);
+
+/* Check the arguments of gemm_run_q without touching any device (as gemm_check_args). */
+GEMM_API gemm_status_t gemm_check_args_q(int64_t M, int64_t N, int64_t K, const void* X,
+                                         int64_t ldx, const uint8_t* Wq, int64_t ldw, int bits,
+                                         int64_t group, const void* scales, const void* offsets,
+                                         int64_t ldg, const void* C, int64_t ldc,
+                                         gemm_dtype_t x_type, uint32_t epilogue,
+                                         const float* bias);
+
+/* The kernel gemm_run_q would use for these arguments, or a negative status. */
+GEMM_API int gemm_select_kernel_q(gemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                  const void* X, int64_t ldx, const uint8_t* Wq, int64_t ldw,
+                                  int bits, int64_t group, const void* scales,
+                                  const void* offsets, int64_t ldg, const void* C, int64_t ldc,
+                                  gemm_dtype_t x_type, uint32_t epilogue, const float* bias);
 
 /* A static, human-readable name for a status code (never NULL). */
 GEMM_API const char* gemm_status_string(gemm_status_t s);

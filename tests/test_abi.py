@@ -23,7 +23,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported():
     syms = declared_symbols()
-    assert len(syms) == 11, syms
+    assert len(syms) == 15, syms
     assert sorted(tmm.EXPORTS) == syms
     nm = subprocess.run(["nm", "-D", "--defined-only", tmm.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
@@ -211,3 +211,50 @@ def test_mx_null_handle():
     assert tmm.gemm_run_mx_kernel(None, 0, None, 4, 4, 32, 0, 0, 1.0, PA, 32, PSA, 1, PB, 4, PSB,
                                   1, 0.0, PC, 4, E4M3, E4M3, BF16, 0,
                                   None) == tmm.GEMM_ERR_INVALID_HANDLE
+
+
+# Group-quantized entry points: fake addresses as above.
+PX, PW, PS, PO = 0x50000000, 0x60000000, 0x70000000, 0x78000000
+
+
+def chk_q(M=4, N=48, K=256, X=PX, ldx=None, W=PW, ldw=None, bits=4, group=64, S=PS, O=PO,
+          ldg=None, C=PC, ldc=None, xt=BF16, epi=0, bias=None):
+    ldx = K if ldx is None else ldx
+    ldw = K * bits // 8 if ldw is None else ldw
+    ldg = K // group if (ldg is None and group) else (ldg or 0)
+    ldc = N if ldc is None else ldc
+    return tmm.gemm_check_args_q(M, N, K, X, ldx, W, ldw, bits, group, S, O, ldg, C, ldc, xt,
+                                 epi, bias)
+
+
+def test_q_arguments():
+    OK, V, U, AL = (tmm.GEMM_OK, tmm.GEMM_ERR_INVALID_VALUE, tmm.GEMM_ERR_UNSUPPORTED,
+                    tmm.GEMM_ERR_ALIAS)
+    assert chk_q() == OK and chk_q(bits=8) == OK and chk_q(xt=F16) == OK
+    assert chk_q(epi=BIAS | GELU, bias=PBIAS) == OK
+    assert chk_q(xt=F32) == U and chk_q(xt=E4M3) == U
+    assert chk_q(bits=3) == V and chk_q(bits=2) == V
+    assert chk_q(group=0, ldg=4) == V and chk_q(group=48) == V      # K % group != 0
+    assert chk_q(K=255, group=1, ldg=255) == V                      # odd K with 4-bit codes
+    assert chk_q(K=255, bits=8, group=1, ldg=255) == OK
+    assert chk_q(ldx=255) == V and chk_q(ldw=127) == V and chk_q(ldg=3) == V
+    assert chk_q(ldc=47) == V and chk_q(C=None) == V
+    assert chk_q(X=None) == V and chk_q(W=None) == V and chk_q(S=None) == V and chk_q(O=None) == V
+    assert chk_q(epi=BIAS) == V and chk_q(epi=8) == V
+    assert chk_q(M=-1) == V
+    assert chk_q(M=0, C=None) == OK and chk_q(N=0, C=None) == OK
+    assert chk_q(K=0, X=None, W=None, S=None, O=None, ldx=0, ldw=0, ldg=0) == OK
+    # C (4 x 48 bf16 = 384 bytes) against each input
+    assert chk_q(C=PX + 10) == AL and chk_q(C=PW + 100) == AL
+    assert chk_q(C=PS + 2) == AL and chk_q(C=PO + 2) == AL
+    assert chk_q(C=PX - 384) == OK and chk_q(C=PX - 383) == AL
+    assert chk_q(C=PBIAS, epi=BIAS, bias=PBIAS + 4) == AL
+
+
+def test_q_null_handle():
+    assert tmm.gemm_run_q(None, None, 1, 8, 64, 1.0, PX, 64, PW, 32, 4, 64, PS, PO, 1, 0.0, PC, 8,
+                          BF16, 0, None) == tmm.GEMM_ERR_INVALID_HANDLE
+    assert tmm.gemm_run_q_kernel(None, 5, None, 1, 8, 64, 1.0, PX, 64, PW, 32, 4, 64, PS, PO, 1,
+                                 0.0, PC, 8, BF16, 0, None) == tmm.GEMM_ERR_INVALID_HANDLE
+    assert tmm.gemm_select_kernel_q(None, 1, 8, 64, PX, 64, PW, 32, 4, 64, PS, PO, 1, PC, 8,
+                                    BF16, 0, None) == tmm.GEMM_ERR_INVALID_HANDLE

@@ -41,12 +41,16 @@ GEMM_KERNEL_SIMT = 1
 GEMM_KERNEL_MFMA_64 = 2
 GEMM_KERNEL_MFMA_128 = 3
 GEMM_KERNEL_MFMA_256 = 4
-KERNEL_NAME = {0: "auto", 1: "simt", 2: "mfma64", 3: "mfma128", 4: "mfma256"}
+GEMM_KERNEL_QGEMV = 5
+GEMM_KERNEL_QMFMA = 6
+KERNEL_NAME = {0: "auto", 1: "simt", 2: "mfma64", 3: "mfma128", 4: "mfma256", 5: "qgemv",
+               6: "qmfma"}
 
 # Every symbol include/gemm.h declares.
 EXPORTS = ("gemm_create", "gemm_destroy", "gemm_check_args", "gemm_run", "gemm_run_kernel",
            "gemm_run_mx", "gemm_run_mx_kernel", "gemm_check_args_mx", "gemm_select_kernel",
-           "gemm_bias_gelu", "gemm_status_string")
+           "gemm_bias_gelu", "gemm_status_string", "gemm_run_q", "gemm_run_q_kernel",
+           "gemm_check_args_q", "gemm_select_kernel_q")
 
 # libgemm.so must resolve its libamdhip64.so.7 dependency to the HIP runtime instance that owns
 # the caller's device pointers and streams.  PyTorch ships its own runtime (soname
@@ -97,6 +101,18 @@ _lib.gemm_select_kernel.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _vp, _i64
 _lib.gemm_select_kernel.restype = _int
 _lib.gemm_bias_gelu.argtypes = [_vp, _vp, _i64, _i64, _vp, _i64, _int, _vp, _u32]
 _lib.gemm_bias_gelu.restype = _int
+_Q = [_i64, _i64, _i64, _f32, _vp, _i64, _vp, _i64, _int, _i64, _vp, _vp, _i64, _f32, _vp,
+      _i64, _int, _u32, _vp]
+_lib.gemm_run_q.argtypes = [_vp, _vp] + _Q
+_lib.gemm_run_q.restype = _int
+_lib.gemm_run_q_kernel.argtypes = [_vp, _int, _vp] + _Q
+_lib.gemm_run_q_kernel.restype = _int
+_QCHK = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _int, _i64, _vp, _vp, _i64, _vp, _i64, _int,
+         _u32, _vp]
+_lib.gemm_check_args_q.argtypes = _QCHK
+_lib.gemm_check_args_q.restype = _int
+_lib.gemm_select_kernel_q.argtypes = [_vp] + _QCHK
+_lib.gemm_select_kernel_q.restype = _int
 _lib.gemm_status_string.argtypes = [_int]
 _lib.gemm_status_string.restype = ctypes.c_char_p
 
@@ -186,6 +202,32 @@ def gemm_bias_gelu(handle, stream, M, N, C, ldc, c_type, bias, epilogue) -> int:
     return _lib.gemm_bias_gelu(handle, stream, M, N, C, ldc, c_type, bias, epilogue)
 
 
+def gemm_run_q(handle, stream, M, N, K, alpha, X, ldx, Wq, ldw, bits, group, scales, offsets,
+               ldg, beta, C, ldc, x_type, epilogue, bias) -> int:
+    """Raw group-quantized entry point: returns the status code (no exception)."""
+    return _lib.gemm_run_q(handle, stream, M, N, K, alpha, X, ldx, Wq, ldw, bits, group, scales,
+                           offsets, ldg, beta, C, ldc, x_type, epilogue, bias)
+
+
+def gemm_run_q_kernel(handle, kernel, stream, M, N, K, alpha, X, ldx, Wq, ldw, bits, group,
+                      scales, offsets, ldg, beta, C, ldc, x_type, epilogue, bias) -> int:
+    return _lib.gemm_run_q_kernel(handle, kernel, stream, M, N, K, alpha, X, ldx, Wq, ldw, bits,
+                                  group, scales, offsets, ldg, beta, C, ldc, x_type, epilogue,
+                                  bias)
+
+
+def gemm_check_args_q(M, N, K, X, ldx, Wq, ldw, bits, group, scales, offsets, ldg, C, ldc,
+                      x_type, epilogue, bias) -> int:
+    return _lib.gemm_check_args_q(M, N, K, X, ldx, Wq, ldw, bits, group, scales, offsets, ldg,
+                                  C, ldc, x_type, epilogue, bias)
+
+
+def gemm_select_kernel_q(handle, M, N, K, X, ldx, Wq, ldw, bits, group, scales, offsets, ldg,
+                         C, ldc, x_type, epilogue, bias) -> int:
+    return _lib.gemm_select_kernel_q(handle, M, N, K, X, ldx, Wq, ldw, bits, group, scales,
+                                     offsets, ldg, C, ldc, x_type, epilogue, bias)
+
+
 # ----------------------------------------------------------------- tensor helpers --
 
 def _stream(stream):
@@ -260,6 +302,35 @@ def select_kernel(handle, M, N, K, *, trans_a=False, trans_b=False, a_type="f32"
     return KERNEL_NAME[k]
 
 
+def run_q(handle, X, Wq, scales, offsets, C, *, M, N, K, bits, group, x_type="bf16",
+          alpha=1.0, beta=0.0, epilogue=GEMM_EPI_NONE, bias=None, ldx=None, ldw=None,
+          ldg=None, ldc=None, kernel=GEMM_KERNEL_AUTO, stream=None):
+    """Group-quantized C = epi(alpha X W^T + beta C + bias) on device tensors of storage words
+    (X, scales, offsets, C: 16-bit words; Wq: bytes).  Raises GemmError on a negative status."""
+    st = gemm_run_q_kernel(handle, kernel, _stream(stream), M, N, K, float(alpha), _ptr(X),
+                           ldx if ldx is not None else K, _ptr(Wq),
+                           ldw if ldw is not None else K * bits // 8, int(bits), int(group),
+                           _ptr(scales), _ptr(offsets), ldg if ldg is not None else K // group,
+                           float(beta), _ptr(C), ldc if ldc is not None else N, DTYPE[x_type],
+                           int(epilogue), _ptr(bias))
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_run_q")
+
+
+def select_kernel_q(handle, M, N, K, *, bits, group, x_type="bf16", X=None, Wq=None,
+                    scales=None, offsets=None, C=None, epilogue=GEMM_EPI_NONE, bias=None,
+                    ldx=None, ldw=None, ldg=None, ldc=None) -> str:
+    """Name of the kernel gemm_run_q picks for these arguments."""
+    k = gemm_select_kernel_q(handle, M, N, K, _ptr(X), ldx if ldx is not None else K, _ptr(Wq),
+                             ldw if ldw is not None else K * bits // 8, int(bits), int(group),
+                             _ptr(scales), _ptr(offsets), ldg if ldg is not None else K // group,
+                             _ptr(C), ldc if ldc is not None else N, DTYPE[x_type],
+                             int(epilogue), _ptr(bias))
+    if k < 0:
+        raise GemmError(k, "gemm_select_kernel_q")
+    return KERNEL_NAME[k]
+
+
 class Gemm:
     """Owns one handle (gemm_create / gemm_destroy)."""
 
@@ -291,3 +362,9 @@ class Gemm:
 
     def select_kernel(self, M, N, K, **kw) -> str:
         return select_kernel(self.handle, M, N, K, **kw)
+
+    def run_q(self, X, Wq, scales, offsets, C, **kw):
+        run_q(self.handle, X, Wq, scales, offsets, C, **kw)
+
+    def select_kernel_q(self, M, N, K, **kw) -> str:
+        return select_kernel_q(self.handle, M, N, K, **kw)

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include "common.hpp"
+#include "handle.hpp"
 
 namespace tgemm {
 hipError_t launch_simt(const GemmParams& p, int a_type, int b_type, int transA, int transB,
@@ -35,7 +36,6 @@ hipError_t launch_bias_gelu(void* C, int64_t ldc, int M, int N, int c_type, cons
 
 namespace {
 
-constexpr uint32_t kMagic = 0x47454d4du;  // "GEMM"
 constexpr int64_t kMaxDim = 0x7fffffff;
 constexpr int64_t kMaxRowBytes = int64_t(1) << 23;
 
@@ -168,28 +168,11 @@ gemm_kernel_t auto_kernel(const Args& a, int cu_count) {
   return GEMM_KERNEL_MFMA_64;
 }
 
-struct DeviceGuard {
-  int prev = -1;
-  bool switched = false;
-  explicit DeviceGuard(int dev) {
-    if (hipGetDevice(&prev) == hipSuccess && prev != dev && hipSetDevice(dev) == hipSuccess)
-      switched = true;
-  }
-  ~DeviceGuard() {
-    if (switched) (void)hipSetDevice(prev);
-  }
-};
+using tgemm::DeviceGuard;
 
 }  // namespace
 
-struct gemm_handle {
-  uint32_t magic;
-  int device;
-  int cu_count;
-  char arch[64];
-};
-
-static bool valid(gemm_handle_t h) { return h && h->magic == kMagic; }
+static bool valid(gemm_handle_t h) { return h && h->magic == tgemm::kHandleMagic; }
 
 extern "C" {
 
@@ -206,7 +189,7 @@ gemm_status_t gemm_create(gemm_handle_t* out, int device) {
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_ERR_DEVICE;
   gemm_handle* h = static_cast<gemm_handle*>(calloc(1, sizeof(gemm_handle)));
   if (!h) return GEMM_ERR_NO_MEMORY;
-  h->magic = kMagic;
+  h->magic = tgemm::kHandleMagic;
   h->device = device;
   h->cu_count = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   strncpy(h->arch, prop.gcnArchName, sizeof(h->arch) - 1);
@@ -216,7 +199,7 @@ gemm_status_t gemm_create(gemm_handle_t* out, int device) {
 
 gemm_status_t gemm_destroy(gemm_handle_t h) {
   if (!h) return GEMM_OK;
-  if (h->magic != kMagic) return GEMM_ERR_INVALID_HANDLE;
+  if (h->magic != tgemm::kHandleMagic) return GEMM_ERR_INVALID_HANDLE;
   h->magic = 0;
   free(h);
   return GEMM_OK;

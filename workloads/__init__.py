@@ -476,6 +476,9 @@ def q_codes(w: np.ndarray, bits: int, group: int, x_type: str):
     rows, K = w.shape
     if K % group:
         raise ValueError("K must be a multiple of the group size")
+    if K == 0:
+        z = np.zeros((rows, 0), dtype=STORAGE[x_type])
+        return np.zeros((rows, 0), dtype=np.uint8), z, z.copy()
     blk = w.reshape(rows, K // group, group)
     lo, hi = blk.min(axis=2), blk.max(axis=2)
     top = (1 << bits) - 1
@@ -511,7 +514,7 @@ def make_qproblem(M: int, N: int, K: int, *, bits: int = 4, group: int = 64,
         raise ValueError("activations are bf16 or f16")
     rng = np.random.default_rng(seed)
     x = rng.normal(0.0, x_std, size=(M, K))
-    w = rng.normal(0.0, w_std if w_std is not None else 1.0 / np.sqrt(K), size=(N, K))
+    w = rng.normal(0.0, w_std if w_std is not None else 1.0 / np.sqrt(max(K, 1)), size=(N, K))
     c_in = rng.uniform(-1.0, 1.0, size=(M, N)) if beta != 0.0 else None
     bias = rng.normal(0.0, bias_std, size=N).astype(np.float32) if epilogue & EPI_BIAS else None
     q, S, O = q_codes(w, bits, group, x_type)

@@ -397,6 +397,13 @@ def main():
         sweeps.append(row)
         del qc
         torch.cuda.empty_cache()
+        # Quantized prefill: 4096 tokens through a 4096 x 4096 projection, 4-bit weights in
+        # groups of 64 dequantised into the bf16 matrix-core kernel; MFMA-bound like the bf16
+        # GEMM it replaces (compare with "bf16 4096").
+        qc = QCell(g, W.q4_prefill())
+        sweeps.append(summarize("q4 prefill 4096^3 (G=64)", qc, qc.time(R), "bf16"))
+        del qc
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:

@@ -235,8 +235,9 @@ GEMM_API gemm_status_t gemm_run_q(gemm_handle_t h, void* stream, int64_t M, int6
 /* gemm_run_q with an explicit kernel: GEMM_KERNEL_SIMT, GEMM_KERNEL_QGEMV (needs Wq and ldw
  * 16-byte aligned and group a multiple of 32 (4-bit) or 16 (8-bit)), or GEMM_KERNEL_QMFMA
  * (needs X, Wq, C 16-byte aligned, ldx a multiple of 8, ldw a multiple of 16, ldc a multiple of
- * 4 and group a multiple of 64 (4-bit) or 32 (8-bit)).  Any other kernel, or one whose needs do
- * not hold, returns GEMM_ERR_UNSUPPORTED. */
+ * 4, group a multiple of 32 and K a multiple of 64; the weights are rounded to x_type once
+ * dequantised, a relative 2^-9 (bf16) or 2^-12 (f16) per weight).  Any other kernel, or one
+ * whose needs do not hold, returns GEMM_ERR_UNSUPPORTED. */
 GEMM_API gemm_status_t gemm_run_q_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* stream,
                                          int64_t M, int64_t N, int64_t K, float alpha,
                                          const void* X, int64_t ldx, const uint8_t* Wq,

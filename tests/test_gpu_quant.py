@@ -131,3 +131,50 @@ def test_q_decode_full_size(g):
     r = qgate(q, qrun(g, q))
     print(r)
     assert r.ok, r
+
+
+@pytest.mark.parametrize("bits,G", [(4, 32), (4, 64), (4, 128), (8, 32), (8, 64)])
+@pytest.mark.parametrize("x_type", ["bf16", "f16"])
+def test_qmfma_parity(g, bits, G, x_type):
+    """Matrix-core kernel: ragged M and N (not multiples of any tile), K spanning many K tiles.
+    The weights pass through the 16-bit type once dequantised: at most 2^-9 (bf16) or 2^-12
+    (f16) of each product, inside the u_out term of the gate."""
+    import tiled_matrix_multiply_amd as tmm
+    q = W.make_qproblem(300, 520, 1024, bits=bits, group=G, x_type=x_type, seed=G + bits,
+                        epilogue=W.EPI_BIAS | W.EPI_GELU)
+    r = qgate(q, qrun(g, q, kernel=tmm.GEMM_KERNEL_QMFMA))
+    print(r)
+    assert r.ok, r
+
+
+def test_qmfma_epilogue_variants(g):
+    import tiled_matrix_multiply_amd as tmm
+    for epi in (0, W.EPI_BIAS | W.EPI_GELU):
+        for beta in (0.0, -0.5):
+            q = W.make_qproblem(264, 392, 512, bits=4, group=64, seed=epi + 20, beta=beta,
+                                alpha=0.75, epilogue=epi)
+            r = qgate(q, qrun(g, q, kernel=tmm.GEMM_KERNEL_QMFMA))
+            assert r.ok, (epi, beta, r)
+
+
+def test_qmfma_is_auto_for_many_rows(g):
+    kw = dict(bits=4, group=64, X=0x10000000, Wq=0x20000000, scales=0x30000000,
+              offsets=0x40000000, C=0x50000000)
+    assert g.select_kernel_q(512, 4096, 4096, **kw) == "qmfma"
+    assert g.select_kernel_q(5, 4096, 4096, **kw) == "qmfma"
+    # K not a whole number of 64-element tiles: the scalar kernel
+    assert g.select_kernel_q(512, 4096, 4064, **dict(kw, group=32)) == "simt"
+
+
+def test_q_prefill_full_size_sampled(g):
+    """The prefill workload at full size (4096^3, 4-bit, groups of 64) on sampled outputs: tile
+    corners and edges and random entries, each against the oracle computed on its own."""
+    from gemm_harness import sample_points
+    q = W.q4_prefill()
+    got = qrun(g, q)
+    rows, cols = sample_points(q.M, q.N, n=2048, seed=1, tile=256)
+    Cref, D = oracle.qgemm_points(q, rows, cols)
+    tol = gate.tolerance(q.K, q.x_type, 1, False)
+    r = gate.check(got[rows, cols], Cref, D, tol, q.x_type)
+    print(r)
+    assert r.ok, r

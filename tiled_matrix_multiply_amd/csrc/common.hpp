@@ -30,6 +30,13 @@ struct GemmParams {
   const uint8_t* sb;
   int64_t ldsa, ldsb;
   int kblocks;
+  // Group-quantized B (the matrix-core kernel with dequantisation): B holds codes, ldb bytes
+  // per row of op(B)^T; code k of row j is worth qs[j*ldg + k/group] * q + qo[j*ldg + k/group]
+  // (16-bit, the activation type).  Null otherwise.
+  const void* qs;
+  const void* qo;
+  int64_t ldg;
+  int group;
 };
 
 template <int DT> struct DTypeInfo;

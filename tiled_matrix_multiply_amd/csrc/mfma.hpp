@@ -181,8 +181,11 @@ constexpr int default_stages() { return TILE == 128 ? 3 : 2; }
 
 // DT_ / BT_: types of A and B (they differ only within the 8-bit family); MX_: OCP
 // microscaling, one E8M0 scale per 32 k of each row of op(A) and column of op(B).
+// QB_: B is given as affine group-quantized codes of QB_ bits (4 or 8; 0 = B is plain data),
+// dequantised into the 16-bit type of A as it is staged (the B tile then looks exactly like a
+// K-contiguous 16-bit B).
 template <int DT_, int TILE_, int WM_, int WN_, bool A_MN_, bool B_MN_,
-          int S_ = default_stages<TILE_>(), int BT_ = DT_, bool MX_ = false>
+          int S_ = default_stages<TILE_>(), int BT_ = DT_, bool MX_ = false, int QB_ = 0>
 struct MfmaCfg {
   static constexpr int DT = DT_, BT = BT_;
   static constexpr bool F8 = is_f8f6f4<DT_>(), MX = MX_;
@@ -199,6 +202,10 @@ struct MfmaCfg {
   static constexpr bool A_MN = A_MN_, B_MN = B_MN_;    // operand stored contiguous along M/N
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;  // one staged K tile
   static constexpr int S = S_;  // LDS buffers per operand: K tiles kt .. kt+S-1 are resident or in flight
+  static constexpr int QB = QB_;
+  static_assert(QB_ == 0 || ((QB_ == 4 || QB_ == 8) && !B_MN_ && !MX_ && S_ == 2 &&
+                             (DT_ == BF16 || DT_ == F16)),
+                "quantized B: K-contiguous codes, 16-bit A, two stages");
   // MX scales: a staged K tile covers BPT 32-element blocks (4 for 8-bit elements, 8 for
   // packed fp4); each row's 16 consecutive scale bytes (TPC = 16 / BPT tiles) are copied as one
   // piece into a double-buffered region of (BM + BN) rows x 16 bytes after the data stages.
@@ -602,7 +609,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   // boundary (c-1)*TPC - 1, and chunk c is issued at boundary c*TPC - S >= (c-1)*TPC - 1.
   const int KT = (p.K + C::BKE - 1) / C::BKE;
   const bool need_fix = (p.epi & (FIX_A | FIX_B)) != 0;
-  constexpr int NL = OA::PER_WAVE + OB::PER_WAVE;  // data copies per wave per K tile
+  constexpr int NL = OA::PER_WAVE + (C::QB ? 0 : OB::PER_WAVE);  // data copies per wave per K tile
   constexpr int NWL = (C::BM + C::BN) / 64;         // 64-row scale wave-loads per chunk
   static_assert(!C::MX || (NWL <= C::NW && C::NW % NWL == 0 && C::TPC + 1 >= C::S),
                 "every wave issues one scale copy per chunk; chunk buffers free in time");
@@ -624,7 +631,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   auto issue = [&](int kt, int buf) {
     if constexpr (C::MX)
       if (kt % C::TPC == 0) issue_scales(kt / C::TPC);
-    issue_b(kt, buf);
+    if constexpr (!C::QB) issue_b(kt, buf);
     issue_a(kt, buf);
   };
   // Copies a wave issues for tiles t0 .. t1 (each tile's data, and its chunk of scales first).
@@ -642,7 +649,86 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
     __syncthreads();
     if (kt + C::S < KT) issue(kt + C::S, abuf);  // into the buffers tile kt has released
   };
+  // Quantized B.  Thread t dequantises the 32 codes k0 + 32 (t % 2) .. +31 of row t / 2 of the
+  // B tile (one 16-byte code chunk at 4 bits, two at 8), one group (group % 32 == 0): w =
+  // fma(s, q, o) in fp32, rounded once to the 16-bit type, written as four 16-byte chunks of
+  // the K-contiguous B layout above.  The codes of K tile u are loaded into registers at the
+  // boundary after tile u-3 and dequantised during tile u-1 (part i, 8 codes, after k-group i),
+  // into the buffer tile u-2 released: their load has a whole tile to land, and the stores
+  // are published by the barrier ending tile u-1.
+  struct QCodes {
+    u32x4 w[C::QB == 8 ? 2 : 1];
+    uint32_t s, o;
+  };
+  const int qrow = tid >> 1, qh = tid & 1;
+  auto qload = [&](int u) {
+    QCodes q{};
+    if constexpr (C::QB != 0) {
+      // rows past N feed only columns that are not stored: read any valid row instead
+      const int64_t n = min(n0 + qrow, p.N - 1);
+      const bool ok = qrow < C::BN && u < KT;
+      const int64_t k = ok ? (int64_t)u * C::BKE + 32 * qh : 0;
+      const uint8_t* src = Bg + n * p.ldb + k * C::QB / 8;
+#pragma unroll
+      for (int i = 0; i < (C::QB == 8 ? 2 : 1); ++i) q.w[i] = *reinterpret_cast<const u32x4*>(src + 16 * i);
+      const int64_t g = n * p.ldg + k / p.group;
+      q.s = reinterpret_cast<const uint16_t*>(p.qs)[g];
+      q.o = reinterpret_cast<const uint16_t*>(p.qo)[g];
+    }
+    return q;
+  };
+  auto qstore_part = [&](const QCodes& q, int buf, int i) {
+    if constexpr (C::QB != 0) {
+      if (qrow >= C::BN) return;
+      const float sc = C::DT == BF16 ? bf16_bits_to_float(q.s) : f16_bits_to_float(q.s);
+      const float of = C::DT == BF16 ? bf16_bits_to_float(q.o) : f16_bits_to_float(q.o);
+      float w[8];
+      if constexpr (C::QB == 4) {
+        const uint32_t d = q.w[0][i];
+        const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;  // even / odd codes
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[2 * e] = fmaf(sc, (float)((lo >> (8 * e)) & 255u), of);
+          w[2 * e + 1] = fmaf(sc, (float)((hi >> (8 * e)) & 255u), of);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int dw = 2 * i + e / 4;
+          w[e] = fmaf(sc, (float)((q.w[dw / 4][dw % 4] >> (8 * (e % 4))) & 255u), of);
+        }
+      }
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (C::DT == BF16) {
+          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+          typedef float f32x2_t __attribute__((ext_vector_type(2)));
+          h[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{w[2 * e], w[2 * e + 1]}), bf16x2_t));
+        } else {
+          h[e] = float_to_f16_bits(w[2 * e]) | (float_to_f16_bits(w[2 * e + 1]) << 16);
+        }
+      }
+      const int c = 4 * qh + i;  // 8-element chunk of the 64-element K tile
+      *reinterpret_cast<u32x4*>(smem + OB::LDS_OFF + buf * C::B_BYTES + qrow * 128 +
+                                ((c ^ OB::kswz(qrow)) << 4)) = u32x4{h[0], h[1], h[2], h[3]};
+    }
+  };
+  QCodes qcur{}, qnext{};  // codes of tiles kt+1 and kt+2 during tile kt
+  // Makes the codes' registers ready at this point (the compiler waits for their loads here).
+  auto qpin = [&](QCodes& q) {
+#pragma unroll
+    for (int i = 0; i < (C::QB == 8 ? 2 : 1); ++i) asm volatile("" : "+v"(q.w[i]));
+    asm volatile("" : "+v"(q.s), "+v"(q.o));
+  };
   // Prologue: copies of tiles 0 .. S-1, then wait for tile 0.
+  if constexpr (C::QB != 0) {
+    const QCodes q0 = qload(0);
+    qcur = qload(1);
+    qnext = qload(2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qstore_part(q0, 0, i);
+  }
 #pragma unroll
   for (int t = 0; t < C::S; ++t)
     if (t < KT) issue(t, t);
@@ -664,8 +750,20 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
         __builtin_amdgcn_iglp_opt(1);
         load_group(kt, aoff, boff, g + 1, (g + 1) & 1);
         mma_group(g & 1);
+        if constexpr (C::QB != 0)
+          if (kt + 1 < KT) qstore_part(qcur, anext, g);
+      }
+      if constexpr (C::QB != 0) {
+        static_assert(!C::QB || G == 4, "four 8-code parts per K tile");
+        if (kt + 1 < KT) qstore_part(qcur, anext, G - 1);
+        // Rotate before the boundary's own wait for every outstanding copy.  The compiler
+        // cannot count the inline-assembly copies, so a wait for the codes placed after the
+        // boundary would also wait for the copies the boundary has just issued.
+        qcur = qnext;
+        qpin(qcur);
       }
       tile_boundary(kt, abuf, anext);
+      if constexpr (C::QB != 0) qnext = qload(kt + 3);
       if (kt + 1 < KT) load_group(kt + 1, anext * C::A_BYTES, anext * C::B_BYTES, 0, 0);
       mma_group((G - 1) & 1);
       abuf = anext;

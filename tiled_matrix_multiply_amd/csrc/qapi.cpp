@@ -10,7 +10,7 @@
 namespace tgemm {
 hipError_t launch_qsimt(const QParams& p, int x_type, int cu_count, hipStream_t s);
 hipError_t launch_qgemv(const QParams& p, int x_type, int cu_count, hipStream_t s);
-hipError_t launch_qmfma(const QParams& p, int x_type, hipStream_t s);
+hipError_t launch_qmfma(const QParams& p, int x_type, int cu_count, hipStream_t s);
 }  // namespace tgemm
 
 namespace {
@@ -88,15 +88,13 @@ bool qgemv_ok(const QArgs& a) {
   return lds <= kQgemvMaxLds;
 }
 
-// Needs of the matrix-core kernel (see launch_qmfma).
+// Needs of the matrix-core kernel (see launch_qmfma): 16-byte chunks of X, codes and C; whole
+// 64-element K tiles, each thread's 32 codes inside one group; 32-bit byte offsets.
 bool qmfma_ok(const QArgs& a) {
-  if (a.K >= 0) return false;  // matrix-core kernel not built yet
-  if (a.K == 0) return false;
-  const int kt = a.bits == 4 ? 64 : 32;  // codes per 32-byte K step
-  if (a.group % kt != 0) return false;
+  if (a.K == 0 || a.K % 64 != 0 || a.group % 32 != 0) return false;
   if (!al16(a.X) || !al16(a.W) || !al16(a.C)) return false;
   if (a.ldx % 8 != 0 || a.ldw % 16 != 0 || a.ldc % 4 != 0) return false;
-  return (__int128)a.N * a.ldw < ((__int128)1 << 31) && (__int128)a.M * a.ldx * 2 < ((__int128)1 << 31);
+  return a.ldx * 2 <= (int64_t(1) << 23) && a.ldw <= (int64_t(1) << 23);
 }
 
 gemm_kernel_t auto_q(const QArgs& a) {
@@ -146,7 +144,7 @@ gemm_status_t run_q(gemm_handle_t h, gemm_kernel_t kernel, void* stream, const Q
       break;
     case GEMM_KERNEL_QMFMA:
       if (!qmfma_ok(a)) return GEMM_ERR_UNSUPPORTED;
-      err = tgemm::launch_qmfma(p, xt, s);
+      err = tgemm::launch_qmfma(p, xt, h->cu_count, s);
       break;
     default: return GEMM_ERR_UNSUPPORTED;
   }

@@ -128,7 +128,18 @@ class Cell:
             self.step()
             e.record(self.stream)
         torch.cuda.synchronize()
-        return np.array([s.elapsed_time(e) for s, e in ev], dtype=np.float64)
+        ms = np.array([s.elapsed_time(e) for s, e in ev], dtype=np.float64)
+        # the same launches back to back between one event pair (no per-launch event in the
+        # stream): the launch-to-launch period, which the per-launch pairs inflate for small
+        # problems
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(reps):
+            self.step()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        self.b2b_ms = e0.elapsed_time(e1) / reps
+        return ms
 
     def algorithmic_bytes(self) -> int:
         p = self.p
@@ -213,10 +224,12 @@ def summarize(name, cell: Cell, ms: np.ndarray, dtype: str) -> dict:
            "tflops_ci95": [round(p.flops / (hi * 1e-3) / 1e12, 2),
                            round(p.flops / (lo * 1e-3) / 1e12, 2)],
            "pct_peak": round(100 * tf / PEAK_TFLOPS[dtype], 2),
-           "gbs": round(cell.algorithmic_bytes() / (med * 1e-3) / 1e9, 1)}
+           "gbs": round(cell.algorithmic_bytes() / (med * 1e-3) / 1e9, 1),
+           "back_to_back_us": round(getattr(cell, "b2b_ms", float("nan")) * 1e3, 3)}
     print(f"[bench] {name:34s} {cell.kernel:8s} {row['median_us']:10.2f} us  "
           f"{row['tflops']:8.1f} TFLOP/s  {row['pct_peak']:5.1f}% of {dtype} peak  "
-          f"{row['gbs']:8.1f} GB/s", file=sys.stderr, flush=True)
+          f"{row['gbs']:8.1f} GB/s  (back to back {row['back_to_back_us']:.2f} us)",
+          file=sys.stderr, flush=True)
     return row
 
 

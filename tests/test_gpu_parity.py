@@ -295,3 +295,18 @@ def test_alias_rejected_before_launch(g):
     with pytest.raises(tmm.GemmError) as e:
         tmm.run(g.handle, d.A, d.B, d.A, M=64, N=64, K=64)
     assert e.value.status == tmm.GEMM_ERR_ALIAS
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_k_split_paths(g, dtype):
+    """The 64 x 64 kernel splits its K loop between two groups of waves when its tiles leave no
+    compute unit a second workgroup and K holds at least four tiles; both forms, ragged K."""
+    for M, N, K in [(1100, 1100, 300),   # 324 tiles > 256 compute units: one group
+                    (512, 520, 1000),    # 72 tiles: two groups, ragged last tile
+                    (130, 200, 4500)]:   # 12 tiles, long K: two groups
+        p = W.make_problem(M, N, K, a_type=dtype, alpha=1.25, beta=-0.5, seed=M + K,
+                           epilogue=W.EPI_BIAS | W.EPI_GELU, dist_a=("normal", 1.0),
+                           dist_b=("normal", 1.0))
+        got, kname, pad_ok = H.run_padded(g, p, kernel=KERNELS["mfma64"])
+        res = H.gate_full(p, got)
+        assert res.ok and pad_ok, f"{dtype} {M}x{N}x{K}: {res}"

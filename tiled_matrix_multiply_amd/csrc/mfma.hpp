@@ -183,9 +183,12 @@ constexpr int default_stages() { return TILE == 128 ? 3 : 2; }
 // microscaling, one E8M0 scale per 32 k of each row of op(A) and column of op(B).
 // QB_: B is given as affine group-quantized codes of QB_ bits (4 or 8; 0 = B is plain data),
 // dequantised into the 16-bit type of A as it is staged (the B tile then looks exactly like a
-// K-contiguous 16-bit B).
+// K-contiguous 16-bit B).  KS_: K split inside the workgroup: KS_ groups of WM_ x WN_ waves
+// each walk every KS_-th K tile with their own LDS stages and add their accumulators at the
+// end (small problems, whose time is the chain of K tiles rather than the multiplies).
 template <int DT_, int TILE_, int WM_, int WN_, bool A_MN_, bool B_MN_,
-          int S_ = default_stages<TILE_>(), int BT_ = DT_, bool MX_ = false, int QB_ = 0>
+          int S_ = default_stages<TILE_>(), int BT_ = DT_, bool MX_ = false, int QB_ = 0,
+          int KS_ = 1>
 struct MfmaCfg {
   static constexpr int DT = DT_, BT = BT_;
   static constexpr bool F8 = is_f8f6f4<DT_>(), MX = MX_;
@@ -194,7 +197,8 @@ struct MfmaCfg {
   using Op = typename std::conditional<F8, MmaScaled<BT_, DT_>, MmaOp<DT_>>::type;
   static constexpr int CT = F8 ? BF16 : DT_;
   static constexpr int BM = TILE_, BN = TILE_;
-  static constexpr int WM = WM_, WN = WN_, NW = WM_ * WN_, NT = NW * 64;
+  static constexpr int KS = KS_;
+  static constexpr int WM = WM_, WN = WN_, NW = WM_ * WN_, NT = NW * 64 * KS_;  // NW waves per K group
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 accumulators per wave
   static constexpr int ES = DTypeInfo<DT_>::bytes;
@@ -210,8 +214,15 @@ struct MfmaCfg {
   // packed fp4); each row's 16 consecutive scale bytes (TPC = 16 / BPT tiles) are copied as one
   // piece into a double-buffered region of (BM + BN) rows x 16 bytes after the data stages.
   static constexpr int BPT = (DT_ == E2M1) ? 8 : 4, TPC = 16 / BPT;
-  static constexpr int SC_OFF = S * (A_BYTES + B_BYTES), SC_BUF = (BM + BN) * 16;
+  static constexpr int GS = S * (A_BYTES + B_BYTES);  // one K group's stages
+  static constexpr int SC_OFF = KS_ * GS, SC_BUF = (BM + BN) * 16;
   static constexpr int LDS_BYTES = SC_OFF + (MX_ ? 2 * SC_BUF : 0);
+  // K split: the partial accumulators of groups 1 .. KS-1 (fp32, wave by wave), then the
+  // epilogue's output staging
+  static constexpr int ACC_BYTES = (BM / WM) * (BN / WN) * 4 * NW;  // one group's accumulators
+  static constexpr int STG_OFF = (KS_ - 1) * ACC_BYTES;
+  static_assert(KS_ == 1 || ((KS_ == 2 || KS_ == 4) && !MX_ && QB_ == 0),
+                "K split: 2 or 4 groups, plain inputs");
   static_assert(S >= 2 && LDS_BYTES <= 160 * 1024, "LDS holds at most 160 KB");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is a whole number of 32x32 tiles");
 };
@@ -300,8 +311,12 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   constexpr int ES = C::ES;
   constexpr int G = C::BKE / Op::KG;  // k-groups per staged tile
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lane_id = lane;
+  const int tid = threadIdx.x, lane = tid & 63, lane_id = lane;
+  // K group (0 unless the K loop is split), wave-uniform so that tile addresses stay scalar
+  const int kg = __builtin_amdgcn_readfirstlane((tid >> 6) / C::NW);
+  const int wave = (tid >> 6) % C::NW;  // wave within the group
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave index, in a scalar register
+  uint8_t* const gsm = smem + kg * C::GS;  // the group's stages
 
   // Tile order.  Workgroups are dealt to the 8 XCDs round-robin by id; renumber so each XCD
   // receives a contiguous range, then walk tiles in groups of TILE_GROUP_M tile rows so the
@@ -348,7 +363,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
       ext = extent_bytes(p.K, p.M, p.lda, k0, m0, ES);
     }
     const i32x4 r = make_rsrc(base, ext);
-    const uint32_t l = (uint32_t)reinterpret_cast<uintptr_t>(smem + OA::LDS_OFF + buf * C::A_BYTES) + wave_u * 1024;
+    const uint32_t l = (uint32_t)reinterpret_cast<uintptr_t>(gsm + OA::LDS_OFF + buf * C::A_BYTES) + wave_u * 1024;
 #pragma unroll
     for (int i = 0; i < OA::PER_WAVE; ++i) buffer_load_lds16(r, l + C::NW * i * 1024, voA[i]);
   };
@@ -364,7 +379,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
       ext = extent_bytes(p.N, p.K, p.ldb, n0, k0, ES);
     }
     const i32x4 r = make_rsrc(base, ext);
-    const uint32_t l = (uint32_t)reinterpret_cast<uintptr_t>(smem + OB::LDS_OFF + buf * C::B_BYTES) + wave_u * 1024;
+    const uint32_t l = (uint32_t)reinterpret_cast<uintptr_t>(gsm + OB::LDS_OFF + buf * C::B_BYTES) + wave_u * 1024;
 #pragma unroll
     for (int i = 0; i < OB::PER_WAVE; ++i) buffer_load_lds16(r, l + C::NW * i * 1024, voB[i]);
   };
@@ -384,7 +399,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
         const int u = wave + C::NW * i;
         int r, c;
         OA::chunk_of(u, lane, r, c);
-        uint8_t* dst = smem + OA::LDS_OFF + abuf * C::A_BYTES + u * 1024 + lane * 16;
+        uint8_t* dst = gsm + OA::LDS_OFF + abuf * C::A_BYTES + u * 1024 + lane * 16;
         if constexpr (!OA::MN) {
           const int gm = m0 + r, gk = k0 + c * OA::CE;
           if (gk + OA::CE > p.K) {
@@ -405,7 +420,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
         const int u = wave + C::NW * i;
         int r, c;
         OB::chunk_of(u, lane, r, c);
-        uint8_t* dst = smem + OB::LDS_OFF + bbuf * C::B_BYTES + u * 1024 + lane * 16;
+        uint8_t* dst = gsm + OB::LDS_OFF + bbuf * C::B_BYTES + u * 1024 + lane * 16;
         if constexpr (!OB::MN) {
           const int gn = n0 + r, gk = k0 + c * OB::CE;
           if (gk + OB::CE > p.K) {
@@ -470,7 +485,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   auto read_frag = [&](uint32_t boff, auto opnd, int wbase, int f, int g, const int* kb,
                        const int* mb, Frag& out) {
     using O = decltype(opnd);
-    const uint8_t* s = smem + O::LDS_OFF + boff;
+    const uint8_t* s = gsm + O::LDS_OFF + boff;
     if constexpr (!O::MN) {
       const int par = ((wbase >> 5) + f) & 1;
 #pragma unroll
@@ -607,7 +622,13 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   // c & 1) is copied just before the data of tile c*TPC, so waiting for that tile covers it.
   // Its buffer last served tiles up to (c-1)*TPC - 1, whose scale reads precede the barrier of
   // boundary (c-1)*TPC - 1, and chunk c is issued at boundary c*TPC - S >= (c-1)*TPC - 1.
-  const int KT = (p.K + C::BKE - 1) / C::BKE;
+  // K tiles.  With the K loop split, group kg takes tiles kg, kg + KS, ... (KT of them) in NI
+  // iterations that every group runs, so that all reach the same barriers; the loop below
+  // counts iterations, which are tiles when KS = 1.
+  const int KT_ALL = (p.K + C::BKE - 1) / C::BKE;
+  const int NI = (KT_ALL + C::KS - 1) / C::KS;
+  const int KT = C::KS == 1 ? KT_ALL : (KT_ALL - kg + C::KS - 1) / C::KS;
+  auto tile_of = [&](int i) { return C::KS == 1 ? i : i * C::KS + kg; };
   const bool need_fix = (p.epi & (FIX_A | FIX_B)) != 0;
   constexpr int NL = OA::PER_WAVE + (C::QB ? 0 : OB::PER_WAVE);  // data copies per wave per K tile
   constexpr int NWL = (C::BM + C::BN) / 64;         // 64-row scale wave-loads per chunk
@@ -628,7 +649,8 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
       buffer_load_lds16(r, l, (uint32_t)((int64_t)(n0 + 64 * u - C::BM + lane) * p.ldsb + 16 * c));
     }
   };
-  auto issue = [&](int kt, int buf) {
+  auto issue = [&](int it, int buf) {  // the tile of iteration it
+    const int kt = tile_of(it);
     if constexpr (C::MX)
       if (kt % C::TPC == 0) issue_scales(kt / C::TPC);
     if constexpr (!C::QB) issue_b(kt, buf);
@@ -645,7 +667,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   auto tile_boundary = [&](int kt, int abuf, int anext) {
     // tiles kt+2 .. min(kt+S-1, KT-1) may stay in flight
     wait_vm<0, MAXC>(copies(kt + 2, min(kt + C::S - 1, KT - 1)));
-    if (kt + 2 == KT && need_fix) fixup(kt + 1, anext, anext);
+    if (kt + 2 == KT && need_fix && tile_of(kt + 1) == KT_ALL - 1) fixup(tile_of(kt + 1), anext, anext);
     __syncthreads();
     if (kt + C::S < KT) issue(kt + C::S, abuf);  // into the buffers tile kt has released
   };
@@ -733,12 +755,13 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   for (int t = 0; t < C::S; ++t)
     if (t < KT) issue(t, t);
   wait_vm<0, MAXC>(copies(1, min(C::S - 1, KT - 1)));
-  if (KT == 1 && need_fix) fixup(0, 0, 0);
+  if (KT == 1 && need_fix && tile_of(0) == KT_ALL - 1) fixup(tile_of(0), 0, 0);
   __syncthreads();
   int abuf = 0;  // buffer of tile kt (kt % S)
   if constexpr (GROUPED) {
     if (KT > 0) load_group(0, 0, 0, 0, 0);
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = 0; kt < NI; ++kt) {
+      const bool work = C::KS == 1 || kt < KT;  // a split group may have one tile fewer
       const uint32_t aoff = abuf * C::A_BYTES, boff = abuf * C::B_BYTES;
       const int anext = abuf + 1 == C::S ? 0 : abuf + 1;
 #pragma unroll
@@ -747,9 +770,13 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
         // reads (LLVM's MFMA / DS-read interleaving strategy 1).  At 4096^3 this is 4% faster
         // while the clock holds (constant operands) and neutral on random operands, where the
         // chip runs near 2.1 GHz.
-        __builtin_amdgcn_iglp_opt(1);
-        load_group(kt, aoff, boff, g + 1, (g + 1) & 1);
-        mma_group(g & 1);
+        if (work) {
+          // (not with the K split: the compiler's interleaving search runs out of memory on
+          // those instantiations)
+          if constexpr (C::KS == 1) __builtin_amdgcn_iglp_opt(1);
+          load_group(kt, aoff, boff, g + 1, (g + 1) & 1);
+          mma_group(g & 1);
+        }
         if constexpr (C::QB != 0)
           if (kt + 1 < KT) qstore_part(qcur, anext, g);
       }
@@ -765,10 +792,11 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
       tile_boundary(kt, abuf, anext);
       if constexpr (C::QB != 0) qnext = qload(kt + 3);
       if (kt + 1 < KT) load_group(kt + 1, anext * C::A_BYTES, anext * C::B_BYTES, 0, 0);
-      mma_group((G - 1) & 1);
+      if (work) mma_group((G - 1) & 1);
       abuf = anext;
     }
   } else {
+    static_assert(C::KS == 1, "K split with the grouped schedule only");
     if (KT > 0) {
       load_b(0, 0, 0, 0);
       load_a(0, 0, 0, 0, af[0][0], scA[0][0]);
@@ -792,6 +820,43 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
         }
       }
       abuf = anext;
+    }
+  }
+
+  if constexpr (C::KS > 1) {
+    // K split: groups 1 .. KS-1 hand their accumulators to group 0 through LDS (wave by wave,
+    // float4 by float4, consecutive lanes 16 bytes apart), which adds them and stores.
+    constexpr int NF = C::FM * C::FN * 4;  // float4 pieces per lane
+    float4* const part = reinterpret_cast<float4*>(smem);
+    __syncthreads();  // every group is done with its stages
+    if (kg > 0) {
+      float4* dst = part + ((kg - 1) * C::NW + wave) * NF * 64 + lane;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            dst[((i * C::FN + j) * 4 + q) * 64] =
+                float4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int h = 1; h < C::KS; ++h) {
+      const float4* src = part + ((h - 1) * C::NW + wave) * NF * 64 + lane;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 v = src[((i * C::FN + j) * 4 + q) * 64];
+            acc[i][j][4 * q] += v.x;
+            acc[i][j][4 * q + 1] += v.y;
+            acc[i][j][4 * q + 2] += v.z;
+            acc[i][j][4 * q + 3] += v.w;
+          }
     }
   }
 
@@ -832,8 +897,8 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
     constexpr int OES = C::CT == F32 ? 4 : 2;           // output element bytes
     constexpr int ROWB = C::WTN * OES, GPR = ROWB / 16;  // staged row bytes, granules per row
     constexpr int CHUNK = 32 * ROWB;                      // one wave's region
-    static_assert(C::NW * CHUNK <= C::LDS_BYTES, "output staging fits the K loop's LDS");
-    uint8_t* const ostage = smem + wave_u * CHUNK;
+    static_assert(C::STG_OFF + C::NW * CHUNK <= C::LDS_BYTES, "output staging fits the K loop's LDS");
+    uint8_t* const ostage = smem + C::STG_OFF + wave_u * CHUNK;
     const int m_w0 = m0 + wm * C::WTM, n_w0 = n0 + wn * C::WTN;
     typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
     auto store_tile = [&](auto has_beta, auto has_gelu) {
@@ -942,21 +1007,28 @@ hipError_t launch_mfma_cfg(GemmParams p, hipStream_t s) {
 // 2 -> 256x256 (2x4 waves of 128x64).  BT: type of B (differs from A only in the 8-bit
 // family); MX: block-scaled.  Packed fp4 is staged K-contiguous only (A stored M x K, B stored
 // N x K): the other layouts return an error (the host never routes them here).
-template <int DT, int TILE, int WM, int WN, int BT, bool MX>
+template <int DT, int TILE, int WM, int WN, int BT, bool MX, int KS = 1>
 hipError_t launch_mfma_layout(const GemmParams& p, bool a_mn, bool b_mn, hipStream_t s) {
   constexpr int S = default_stages<TILE>();
-  if (!a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, false, S, BT, MX>>(p, s);
+  if (!a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, false, S, BT, MX, 0, KS>>(p, s);
   if constexpr (DT == E2M1) {
     return hipErrorInvalidValue;
   } else {
-    if (!a_mn && b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, true, S, BT, MX>>(p, s);
-    if (a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, true, false, S, BT, MX>>(p, s);
-    return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, true, true, S, BT, MX>>(p, s);
+    if (!a_mn && b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, true, S, BT, MX, 0, KS>>(p, s);
+    if (a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, true, false, S, BT, MX, 0, KS>>(p, s);
+    return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, true, true, S, BT, MX, 0, KS>>(p, s);
   }
 }
 
+// ks (64 x 64 tile only, 16- and 32-bit inputs): the K split, 1 or 2 groups of four waves (four
+// groups measured no faster than two at 512^3 and 1024^3).
 template <int DT, int BT = DT, bool MX = false>
-hipError_t launch_mfma_dtype(const GemmParams& p, int tile, bool a_mn, bool b_mn, hipStream_t s) {
+hipError_t launch_mfma_dtype(const GemmParams& p, int tile, bool a_mn, bool b_mn, hipStream_t s,
+                             int ks = 1) {
+  if constexpr (DT == F32 || DT == F16 || DT == BF16) {
+    if (tile == 0 && ks == 2) return launch_mfma_layout<DT, 64, 2, 2, BT, MX, 2>(p, a_mn, b_mn, s);
+  }
+  if (ks != 1) return hipErrorInvalidValue;
   switch (tile) {
     case 0: return launch_mfma_layout<DT, 64, 2, 2, BT, MX>(p, a_mn, b_mn, s);
     case 1: return launch_mfma_layout<DT, 128, 2, 2, BT, MX>(p, a_mn, b_mn, s);

@@ -64,6 +64,24 @@ def test_qgemv_parity(g, M, bits, G, x_type):
     assert r.ok, r
 
 
+@pytest.mark.parametrize("M,N,K,bits,G", [
+    (1, 77, 4352, 4, 64),   # 136 chunks: two units per row block, the second mostly masked
+    (1, 77, 4288, 4, 64),   # 67 groups (odd): per-lane scales and offsets, two units
+    (2, 50, 2112, 4, 64),   # 33 groups (odd), one unit
+    (1, 40, 8320, 4, 32),   # 260 groups: per-lane scales and offsets, three units
+    (1, 33, 8192, 8, 64),   # 8-bit: four units
+])
+def test_qgemv_unit_shapes(g, M, N, K, bits, G):
+    """Row blocks that take several units of chunks, ragged last units, and both forms of the
+    scale and offset loads, with beta and the full epilogue."""
+    import tiled_matrix_multiply_amd as tmm
+    q = W.make_qproblem(M, N, K, bits=bits, group=G, x_type="bf16", seed=K + M, beta=0.5,
+                        alpha=0.75, epilogue=W.EPI_BIAS | W.EPI_GELU)
+    r = qgate(q, qrun(g, q, kernel=tmm.GEMM_KERNEL_QGEMV))
+    print(r)
+    assert r.ok, r
+
+
 @pytest.mark.parametrize("bits,G", [(4, 8), (4, 64), (8, 3)])
 def test_qsimt_parity_any_shape(g, bits, G):
     import tiled_matrix_multiply_amd as tmm

@@ -29,10 +29,11 @@ __global__ __launch_bounds__(256) void qsimt_kernel(QParams p) {
 // ------------------------------------------------------------------ matrix-vector kernel --
 // Decode: few activation rows (MT at most), many weight rows.  A fixed number of workgroups per
 // compute unit each stage the activations once in LDS (16-byte loads when X allows them), then
-// walk blocks of weight rows: each wave takes R rows of a block, in units of B 16-byte chunks
-// per lane and row (chunk c = lane + 64 u; 32 codes at 4 bits, 16 at 8 bits; a chunk never
-// straddles a group because the group is a multiple of the chunk), so that each load
-// instruction of a wave covers 1 KiB of consecutive code bytes.
+// walk blocks of weight rows: each wave takes R rows of a block, in ncb units of B 16-byte
+// chunks per lane and row (unit t takes chunks c = lane + 64 (t + ncb b), b < B: each load
+// instruction of a wave covers 1 KiB of consecutive code bytes, and a unit spreads over the
+// whole row; a chunk holds 32 codes at 4 bits, 16 at 8 bits, and never straddles a group
+// because the group is a multiple of the chunk).
 //  * 4-bit codes: the two codes k and k+4 of each run of eight become one 16-bit pair in the
 //    activation type, each half an exact value e(q) = B0 + q / Q (see code_pairs), and v_dot2
 //    multiplies the pair with the staged activations (x_k, x_{k+4}) into an fp32 sum T.  Over a
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(64 * QGEMV_WAVES, MT == 1 ? QGEMV_WG_PER_CU : 1) vo
   // C_in is read even when beta = 0 (C is the output, so the address is valid) and not used.
   const float* const biasp = (p.epi & EPI_BIAS) ? p.bias : reinterpret_cast<const float*>(p.W);
   auto load = [&](Cursor u, Unit& d) {
-    const int cb = lane + 64 * B * u.t;
+    const int cb = lane + 64 * u.t;
     const int64_t j0 = (u.jb * QGEMV_WAVES + wave) * R;
     // The small operands first: a wait for them is then a wait for the oldest loads only.
 #pragma unroll
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(64 * QGEMV_WAVES, MT == 1 ? QGEMV_WG_PER_CU : 1) vo
       } else {
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-          const int c = cb + 64 * b;
+          const int c = cb + 64 * ncb * b;
           const int64_t gi = jc * p.ldg + (int64_t)(c < NCH ? c : NCH - 1) * CH / p.group;
           d.so[r][b] = (uint32_t)reinterpret_cast<const uint16_t*>(p.S)[gi] |
                        ((uint32_t)reinterpret_cast<const uint16_t*>(p.O)[gi] << 16);
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(64 * QGEMV_WAVES, MT == 1 ? QGEMV_WG_PER_CU : 1) vo
       const uint8_t* const row = p.W + jc * p.ldw;  // uniform
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const int c = cb + 64 * b;
+        const int c = cb + 64 * ncb * b;
         const uint32_t off = (uint32_t)(c < NCH ? c : NCH - 1) * 16u;
         d.w[r][b] = *reinterpret_cast<const u32x4_t*>(row + off);
       }
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(64 * QGEMV_WAVES, MT == 1 ? QGEMV_WG_PER_CU : 1) vo
   float acc[R][MT];
   auto compute = [&](Cursor u, const Unit& d) {
     const int t = u.t;
-    const int cb = lane + 64 * B * t;
+    const int cb = lane + 64 * t;
     const int64_t j0 = (u.jb * QGEMV_WAVES + wave) * R;
     if (t == 0) {
 #pragma unroll
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(64 * QGEMV_WAVES, MT == 1 ? QGEMV_WG_PER_CU : 1) vo
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const int c = cb + 64 * b;
+      const int c = cb + 64 * ncb * b;
       const bool cok = c < NCH;
       const int cc = cok ? c : NCH - 1;
       const int gi = (int)((int64_t)cc * CH / p.group);  // group of the chunk

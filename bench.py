@@ -36,15 +36,25 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_bf16_bias_gelu_4096.txt")
 
 
-def source_hash() -> str:
-    """Hash of the library sources: ties a stored counter measurement to the kernel it saw."""
+# The files the headline kernel is built from: its template, its instantiation, the host code
+# that picks its tile and launches it, and the build flags.  Other kernels' sources do not
+# change it, so a stored counter measurement stays valid across their edits.
+HEADLINE_SOURCES = ("tiled_matrix_multiply_amd/csrc/common.hpp",
+                    "tiled_matrix_multiply_amd/csrc/mfma.hpp",
+                    "tiled_matrix_multiply_amd/csrc/mfma_bf16.hip",
+                    "tiled_matrix_multiply_amd/csrc/api.cpp",
+                    "tiled_matrix_multiply_amd/csrc/handle.hpp",
+                    "tiled_matrix_multiply_amd/build.py",
+                    "include/gemm.h")
+
+
+def source_hash(files=HEADLINE_SOURCES) -> str:
+    """Hash of the sources of a kernel: ties a stored counter measurement to the kernel it saw."""
     h = hashlib.sha256()
-    for d in ("tiled_matrix_multiply_amd/csrc", "include"):
-        base = os.path.join(ROOT, d)
-        for f in sorted(os.listdir(base)):
-            with open(os.path.join(base, f), "rb") as fh:
-                h.update(f.encode())
-                h.update(fh.read())
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -311,6 +321,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--headline-only-loop", type=int, default=0,
                     help="run only N headline steps (for profiler passes) and exit")
+    ap.add_argument("--loop-cell", default="headline",
+                    choices=["headline", "q4_decode", "q4_prefill"],
+                    help="with --headline-only-loop: the workload to run instead of the headline")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --headline-only-loop: also run a plain device copy of this many "
                          "bytes three times (a known-size reference for HBM byte counters)")
@@ -339,10 +352,18 @@ def main():
           file=sys.stderr, flush=True)
 
     if args.headline_only_loop:
+        if args.loop_cell == "headline":
+            loop = head
+        else:
+            # the decode cycles three weight copies, as in the sweep, so that each launch reads
+            # its weights from HBM
+            qp = W.q4_decode() if args.loop_cell == "q4_decode" else W.q4_prefill()
+            loop = QCell(g, qp, copies=3 if args.loop_cell == "q4_decode" else 1)
+            print(f"[bench] loop cell {args.loop_cell}, kernel {loop.kernel}", file=sys.stderr)
         for _ in range(args.headline_only_loop):
-            head.step()
+            loop.step()
         torch.cuda.synchronize()
-        print(f"[bench] ran {args.headline_only_loop} headline steps", file=sys.stderr)
+        print(f"[bench] ran {args.headline_only_loop} {args.loop_cell} steps", file=sys.stderr)
         if args.copy_bytes:
             src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
             dst = torch.empty_like(src)

@@ -421,7 +421,7 @@ def main():
         cell("mxfp8 e4m3 4096 (E8M0 / 32 k)", W.mxfp8_4096(4096), "e4m3")
         cell("mxfp4 e2m1 4096 (E8M0 / 32 k)", W.mxfp4_4096(4096), "e2m1")
         # Quantized decode: one token through a 28672 x 8192 projection with 4-bit weights in
-        # groups of 64; three weight copies (375 MB) are cycled so that every launch streams
+        # groups of 64; three weight copies (397 MB) are cycled so that every launch streams
         # its weights from HBM.  Bound by HBM: GB/s against 8 TB/s is its roofline.
         qc = QCell(g, W.q4_decode(), copies=3)
         row = summarize("q4 decode 1x28672x8192 (G=64)", qc, qc.time(R), "bf16")

@@ -81,6 +81,7 @@ class Cell:
 
         self.p = p
         self.unfused = unfused
+        self.launches_per_step = 2 if unfused else 1
         self.A, self.B, self.C = dev(p.A), dev(p.B), dev(p.C)
         self.bias = dev(p.bias) if p.bias is not None else None
         self.stream = torch.cuda.current_stream()
@@ -183,6 +184,7 @@ class QCell:
             return torch.from_numpy(a).to("cuda:0")
 
         self.p = q
+        self.launches_per_step = 1
         self.X, self.C = dev(q.X), dev(q.C)
         self.bias = dev(q.bias) if q.bias is not None else None
         self.W = [(dev(q.Wq), dev(q.scales), dev(q.offsets)) for _ in range(copies)]
@@ -220,6 +222,63 @@ class QCell:
         if q.bias is not None:
             b += 4 * q.N
         return int(b)
+
+
+def sweep_cells():
+    """Every sweep cell as (name, dtype, make), make(g) building its device operands (a Cell
+    or a QCell).  The timed sweep and the counter pass both walk this list."""
+    import workloads as W
+    cells = [("fp32 256", "f32", lambda g: Cell(g, W.fp32_256())),
+             ("fp32 1000 a=1.5 b=-0.5 NN", "f32", lambda g: Cell(g, W.fp32_1000_ragged(False))),
+             ("fp32 1000 a=1.5 b=-0.5 TN", "f32", lambda g: Cell(g, W.fp32_1000_ragged(True)))]
+    for n in (512, 1024, 2048, 4096):
+        cells.append((f"fp16 {n}", "f16", lambda g, n=n: Cell(g, W.fp16_square(n))))
+    for n in (512, 1024, 2048, 4096):
+        cells.append((f"bf16+bias+GELU fused {n}", "bf16",
+                      lambda g, n=n: Cell(g, W.bf16_bias_gelu(n))))
+        cells.append((f"bf16 GEMM then bias+GELU {n}", "bf16",
+                      lambda g, n=n: Cell(g, W.bf16_bias_gelu(n), unfused=True)))
+    cells += [
+        ("fp8 e4m3 4096 (scaled, bf16 out)", "e4m3", lambda g: Cell(g, W.fp8_4096(4096))),
+        ("bf16 4096 (fp8 twin)", "bf16", lambda g: Cell(g, W.bf16_twin_of_fp8(4096))),
+        ("fp8 e5m2 4096 (scaled, bf16 out)", "e5m2", lambda g: Cell(g, W.e5m2_4096(4096))),
+        ("mxfp8 e4m3 4096 (E8M0 / 32 k)", "e4m3", lambda g: Cell(g, W.mxfp8_4096(4096))),
+        ("mxfp4 e2m1 4096 (E8M0 / 32 k)", "e2m1", lambda g: Cell(g, W.mxfp4_4096(4096))),
+        # Quantized decode: one token through a 28672 x 8192 projection with 4-bit weights in
+        # groups of 64; three weight copies (397 MB) are cycled so that every launch streams
+        # its weights from HBM.  Bound by HBM: GB/s against 8 TB/s is its roofline.
+        ("q4 decode 1x28672x8192 (G=64)", "bf16", lambda g: QCell(g, W.q4_decode(), copies=3)),
+        # Quantized prefill: 4096 tokens through a 4096 x 4096 projection, 4-bit weights in
+        # groups of 64 dequantised into the bf16 matrix-core kernel; MFMA-bound like the bf16
+        # GEMM it replaces (compare with "bf16 4096").
+        ("q4 prefill 4096^3 (G=64)", "bf16", lambda g: QCell(g, W.q4_prefill())),
+    ]
+    return cells
+
+
+def counter_pass(g, reps: int, copy_bytes: int) -> None:
+    """Untimed: every sweep cell `reps` steps in list order, then a plain device copy of
+    `copy_bytes` three times.  A counter run over it (rocprofv3 --pmc) sees the library's
+    dispatches in that order; the manifest printed to stderr gives each cell's count."""
+    import torch
+    for name, dtype, make in sweep_cells():
+        c = make(g)
+        for _ in range(reps):
+            c.step()
+        torch.cuda.synchronize()
+        print(f"[counter-pass] cell={name!r} kernel={c.kernel} dtype={dtype} "
+              f"dispatches={reps * c.launches_per_step} flops={c.p.flops} "
+              f"bytes={c.algorithmic_bytes()}", file=sys.stderr, flush=True)
+        del c
+        torch.cuda.empty_cache()
+    if copy_bytes:
+        src = torch.empty(copy_bytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[counter-pass] copied {copy_bytes} bytes 3 times", file=sys.stderr, flush=True)
 
 
 def summarize(name, cell: Cell, ms: np.ndarray, dtype: str) -> dict:
@@ -324,6 +383,8 @@ def main():
     ap.add_argument("--loop-cell", default="headline",
                     choices=["headline", "q4_decode", "q4_prefill"],
                     help="with --headline-only-loop: the workload to run instead of the headline")
+    ap.add_argument("--counter-pass", type=int, default=0,
+                    help="run every sweep cell this many times, untimed, for counter runs, and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --headline-only-loop: also run a plain device copy of this many "
                          "bytes three times (a known-size reference for HBM byte counters)")
@@ -350,6 +411,10 @@ def main():
     head = Cell(g, head_p)
     print(f"[bench] headline: bf16 GEMM+bias+GELU 4096^3 fused, kernel {head.kernel}",
           file=sys.stderr, flush=True)
+
+    if args.counter_pass:
+        counter_pass(g, args.counter_pass, args.copy_bytes)
+        return
 
     if args.headline_only_loop:
         if args.loop_cell == "headline":
@@ -398,46 +463,17 @@ def main():
 
     sweeps = []
     if not args.no_sweeps:
-        R = args.reps
-
-        def cell(name, p, dtype, unfused=False):
-            c = Cell(g, p, unfused)
-            sweeps.append(summarize(name, c, c.time(R), dtype))
+        for name, dtype, make in sweep_cells():
+            c = make(g)
+            row = summarize(name, c, c.time(args.reps), dtype)
+            if isinstance(c, QCell) and c.p.M <= 4:
+                row["pct_hbm"] = round(100 * row["gbs"] / PEAK_HBM_GBS, 2)
+                print(f"[bench] {'':34s} {row['pct_hbm']:.1f}% of HBM peak "
+                      f"({c.algorithmic_bytes() / 1e6:.1f} MB per launch)", file=sys.stderr,
+                      flush=True)
+            sweeps.append(row)
             del c
             torch.cuda.empty_cache()
-
-        cell("fp32 256", W.fp32_256(), "f32")
-        cell("fp32 1000 a=1.5 b=-0.5 NN", W.fp32_1000_ragged(False), "f32")
-        cell("fp32 1000 a=1.5 b=-0.5 TN", W.fp32_1000_ragged(True), "f32")
-        for n in (512, 1024, 2048, 4096):
-            cell(f"fp16 {n}", W.fp16_square(n), "f16")
-        for n in (512, 1024, 2048, 4096):
-            p = W.bf16_bias_gelu(n)
-            cell(f"bf16+bias+GELU fused {n}", p, "bf16")
-            cell(f"bf16 GEMM then bias+GELU {n}", p, "bf16", unfused=True)
-        cell("fp8 e4m3 4096 (scaled, bf16 out)", W.fp8_4096(4096), "e4m3")
-        cell("bf16 4096 (fp8 twin)", W.bf16_twin_of_fp8(4096), "bf16")
-        cell("fp8 e5m2 4096 (scaled, bf16 out)", W.e5m2_4096(4096), "e5m2")
-        cell("mxfp8 e4m3 4096 (E8M0 / 32 k)", W.mxfp8_4096(4096), "e4m3")
-        cell("mxfp4 e2m1 4096 (E8M0 / 32 k)", W.mxfp4_4096(4096), "e2m1")
-        # Quantized decode: one token through a 28672 x 8192 projection with 4-bit weights in
-        # groups of 64; three weight copies (397 MB) are cycled so that every launch streams
-        # its weights from HBM.  Bound by HBM: GB/s against 8 TB/s is its roofline.
-        qc = QCell(g, W.q4_decode(), copies=3)
-        row = summarize("q4 decode 1x28672x8192 (G=64)", qc, qc.time(R), "bf16")
-        row["pct_hbm"] = round(100 * row["gbs"] / PEAK_HBM_GBS, 2)
-        print(f"[bench] {'':34s} {row['pct_hbm']:.1f}% of HBM peak "
-              f"({qc.algorithmic_bytes() / 1e6:.1f} MB per launch)", file=sys.stderr, flush=True)
-        sweeps.append(row)
-        del qc
-        torch.cuda.empty_cache()
-        # Quantized prefill: 4096 tokens through a 4096 x 4096 projection, 4-bit weights in
-        # groups of 64 dequantised into the bf16 matrix-core kernel; MFMA-bound like the bf16
-        # GEMM it replaces (compare with "bf16 4096").
-        qc = QCell(g, W.q4_prefill())
-        sweeps.append(summarize("q4 prefill 4096^3 (G=64)", qc, qc.time(R), "bf16"))
-        del qc
-        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:

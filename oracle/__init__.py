@@ -9,8 +9,8 @@ the passages of the pages it follows.
 Parity pins (tests/test_oracle.py): exact brute force with fractions.Fraction on every shape in
 {1..4}^3, identity and permutation matrices, rank-1 closed forms, alpha/beta linearity,
 A*B == (B^T A^T)^T, an exhaustive OCP E4M3 table, bf16 ties-to-even, closed-form GELU values, and
-a numpy float64 matmul cross-check, exhaustive OCP E5M2 / E2M1 / E8M0 tables, exact
-block-scaled (MX) brute force, and for the group-quantized product (tests/test_oracle_q.py)
+a numpy float64 matmul cross-check, exhaustive OCP E5M2 / E2M1 / E2M3 / E3M2 / E8M0 tables,
+6-bit packing, exact block-scaled (MX) brute force, and for the group-quantized product (tests/test_oracle_q.py)
 exact brute force, the unit-scale reduction to the plain product, nibble order, group
 locality and offset-only closed forms.
 """
@@ -25,7 +25,9 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
-TYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3, "e5m2": 4, "e2m1": 5}
+TYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3, "e5m2": 4, "e2m1": 5, "e2m3": 6, "e3m2": 7}
+# Packed types: (elements, bytes) per packing unit along a row.
+PACKED = {"e2m1": (2, 1), "e2m3": (4, 3), "e3m2": (4, 3)}
 EPI_BIAS = 1
 EPI_GELU = 2
 
@@ -82,10 +84,17 @@ def _ptr(a: Optional[np.ndarray]):
 
 def decode(dtype: str, stored: np.ndarray) -> np.ndarray:
     """Decode stored words/bytes of `dtype` to float64 with the oracle's own decoders (E2M1:
-    two elements per byte along the last axis, low nibble first)."""
+    two elements per byte along the last axis, low nibble first; E2M3 / E3M2: four elements per
+    three bytes along the last axis, element i at bits 6i of the little-endian byte string)."""
     a = np.ascontiguousarray(stored)
-    n = a.size * (2 if dtype == "e2m1" else 1)
-    shape = a.shape[:-1] + (a.shape[-1] * 2,) if dtype == "e2m1" else a.shape
+    if dtype in PACKED:
+        e, b = PACKED[dtype]
+        if a.shape[-1] % b:
+            raise ValueError(f"{dtype}: last axis of {a.shape[-1]} bytes is not whole units")
+        n = a.size // b * e
+        shape = a.shape[:-1] + (a.shape[-1] // b * e,)
+    else:
+        n, shape = a.size, a.shape
     out = np.empty(shape, dtype=np.float64)
     rc = lib().oracle_decode(TYPE_CODE[dtype], _ptr(a), n, _ptr(out))
     if rc != 0:

@@ -23,7 +23,9 @@
  * and of a column of op(B) shares one E8M0 scale 2^(e - 127) (e = 255 is NaN), so
  *   a(i,k) = dec(A ...) * 2^(sa[i*ldsa + k/32] - 127),  b(k,j) = dec(B ...) * 2^(sb[j*ldsb + k/32] - 127)
  * with the per-tensor scales then 1.  This is the plain reading of the MX formats that
- * "Rigel" (arXiv 2606.12765) lists next to fp8 (section 4, the block-scaled MXFP4 rows).
+ * "Rigel" (arXiv 2606.12765) lists next to fp8 (section 4, the block-scaled MXFP4 rows); the
+ * 6-bit element types E2M3 and E3M2 of the same MX family are decoded as the OCP MX v1.0
+ * specification defines them (the pages name no 6-bit type).
  *
  * Every product of two decoded inputs is exact in double (at most 24+24 significant bits; a
  * power-of-two block scale only moves the exponent, and 2^(+-127) products stay inside the
@@ -36,10 +38,12 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_E4M3 = 3, OR_E5M2 = 4, OR_E2M1 = 5 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_E4M3 = 3, OR_E5M2 = 4, OR_E2M1 = 5, OR_E2M3 = 6,
+       OR_E3M2 = 7 };
 enum { OR_EPI_BIAS = 1u, OR_EPI_GELU = 2u };
 
-/* Storage bits per element (E2M1 packs two elements per byte). */
+/* Storage bits per element (E2M1 packs two elements per byte, the 6-bit types four per three
+ * bytes). */
 static int ebits_of(int t) {
   switch (t) {
     case OR_F32: return 32;
@@ -48,6 +52,8 @@ static int ebits_of(int t) {
     case OR_E4M3: return 8;
     case OR_E5M2: return 8;
     case OR_E2M1: return 4;
+    case OR_E2M3: return 6;
+    case OR_E3M2: return 6;
     default: return 0;
   }
 }
@@ -100,6 +106,32 @@ static double dec_e2m1(uint8_t q) {
   return s ? -v : v;
 }
 
+/* The 6-bit element types of the OCP Microscaling Formats (MX) v1.0 specification, neither with
+ * infinities or NaN:
+ *   E2M3: 1 sign, 2 exponent (bias 1), 3 mantissa bits; largest 7.5, subnormals m * 2^-3;
+ *   E3M2: 1 sign, 3 exponent (bias 3), 2 mantissa bits; largest 28, subnormals m * 2^-4. */
+static double dec_e2m3(uint8_t q) {
+  int s = (q >> 5) & 1, e = (q >> 3) & 3, m = q & 7;
+  double v = (e == 0) ? ldexp((double)m, -3) : ldexp((double)(8 + m), e - 4);
+  return s ? -v : v;
+}
+static double dec_e3m2(uint8_t q) {
+  int s = (q >> 5) & 1, e = (q >> 2) & 7, m = q & 3;
+  double v = (e == 0) ? ldexp((double)m, -4) : ldexp((double)(4 + m), e - 5);
+  return s ? -v : v;
+}
+
+/* Packed 6-bit storage: element idx occupies bits 6 idx .. 6 idx + 5 of the byte string read
+ * as one little-endian integer (four elements per three bytes).  The second byte is read only
+ * when the element reaches into it. */
+static uint8_t get6(const uint8_t* base, int64_t idx) {
+  const int64_t bit = 6 * idx, by = bit >> 3;
+  const int sh = (int)(bit & 7);
+  unsigned v = (unsigned)base[by] >> sh;
+  if (sh > 2) v |= (unsigned)base[by + 1] << (8 - sh);
+  return (uint8_t)(v & 63u);
+}
+
 /* OCP E8M0 block scale: 2^(e - 127); e = 255 is NaN. */
 static double dec_e8m0(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
 
@@ -118,6 +150,8 @@ static double dec_one(int t, const uint8_t* base, int64_t idx) {
     case OR_E5M2: return dec_e5m2(base[idx]);
     /* element idx sits in byte idx/2: the low nibble for even idx, the high one for odd */
     case OR_E2M1: return dec_e2m1((uint8_t)((base[idx >> 1] >> (4 * (idx & 1))) & 15));
+    case OR_E2M3: return dec_e2m3(get6(base, idx));
+    case OR_E3M2: return dec_e3m2(get6(base, idx));
     default: return NAN;
   }
 }
@@ -157,7 +191,8 @@ typedef struct {
 
 static int check(const problem_t* p) {
   if (p->M < 0 || p->N < 0 || p->K < 0) return -1;
-  if (!ebits_of(p->at) || !ebits_of(p->bt) || !ebits_of(p->ct) || p->ct == OR_E2M1) return -1;
+  if (!ebits_of(p->at) || !ebits_of(p->bt) || !ebits_of(p->ct)) return -1;
+  if (p->ct == OR_E2M1 || p->ct == OR_E2M3 || p->ct == OR_E3M2) return -1;
   if ((p->sa_blk != NULL) != (p->sb_blk != NULL)) return -1;
   if (p->sa_blk && (p->K % 32 != 0 || p->ldsa < p->K / 32 || p->ldsb < p->K / 32)) return -1;
   if (p->K > 0 && (!p->A || !p->B)) return -1;

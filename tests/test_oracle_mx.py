@@ -1,6 +1,6 @@
-"""Pins for the oracle's 8-bit E5M2, 4-bit E2M1 and OCP microscaling (MX) paths: values the
-OCP formats define, an independent library decoder where one exists, and exact rational brute
-force.  CPU only."""
+"""Pins for the oracle's 8-bit E5M2, 4-bit E2M1, 6-bit E2M3 / E3M2 and OCP microscaling (MX)
+paths: values the OCP formats define, an independent library decoder where one exists, and exact
+rational brute force.  CPU only."""
 import itertools
 from fractions import Fraction
 
@@ -56,6 +56,53 @@ def test_e2m1_table_packing_and_encoder():
     assert np.array_equal(W.to_e2m1_codes(np.array(E2M1_TABLE)), np.arange(8))
 
 
+# The 6-bit types of the OCP MX v1.0 specification as value grids: each binade of the format,
+# from the subnormals up, with its step (a description independent of the bit fields).
+#   E2M3: [0, 1) in steps of 1/8 (subnormals 0 .. 7/8), then [1, 2) by 1/8, [2, 4) by 1/4,
+#         [4, 8) by 1/2 up to 7.5.
+#   E3M2: [0, 1/4) by 1/16, [1/4, 1/2) by 1/16, [1/2, 1) by 1/8, [1, 2) by 1/4, [2, 4) by 1/2,
+#         [4, 8) by 1, [8, 16) by 2, [16, 32) by 4 up to 28.
+def _grid(parts):
+    out = []
+    for lo, n, step in parts:
+        out += [Fraction(lo) + i * Fraction(step) for i in range(n)]
+    return [float(v) for v in out]
+
+
+E2M3_GRID = _grid([(0, 8, Fraction(1, 8)), (1, 8, Fraction(1, 8)), (2, 8, Fraction(1, 4)),
+                   (4, 8, Fraction(1, 2))])
+E3M2_GRID = _grid([(0, 4, Fraction(1, 16)), (Fraction(1, 4), 4, Fraction(1, 16)),
+                   (Fraction(1, 2), 4, Fraction(1, 8)), (1, 4, Fraction(1, 4)),
+                   (2, 4, Fraction(1, 2)), (4, 4, 1), (8, 4, 2), (16, 4, 4)])
+
+
+@pytest.mark.parametrize("elem,grid,top", [("e2m3", E2M3_GRID, 7.5), ("e3m2", E3M2_GRID, 28.0)])
+def test_fp6_tables_packing_and_encoder(elem, grid, top):
+    codes = np.arange(64, dtype=np.uint8).reshape(1, 64)
+    packed = W.pack_fp6(codes)
+    assert packed.shape == (1, 48)
+    d = oracle.decode(elem, packed)[0]
+    assert list(d[:32]) == grid and d[31] == top
+    assert list(d[32:]) == [-v for v in grid] and np.signbit(d[32])
+    # encode(decode(c)) is the identity on the non-negative codes; nearest with ties to the
+    # even code; saturation at the largest finite value
+    assert np.array_equal(W.to_fp6_codes(np.array(grid), elem), np.arange(32))
+    mid = (np.array(grid[8:12]) + np.array(grid[9:13])) / 2  # halfway between codes 8..12
+    assert list(W.to_fp6_codes(mid, elem)) == [8, 10, 10, 12]
+    assert W.to_fp6_codes(np.array([1e6, -1e6]), elem).tolist() == [31, 63]
+
+
+def test_fp6_packing_by_hand():
+    """Codes 1, 2, 3, 4 packed: 1 | 2 << 6 | 3 << 12 | 4 << 18 = 0x103081, bytes 81 30 10."""
+    packed = W.pack_fp6(np.array([[1, 2, 3, 4]], dtype=np.uint8))
+    assert packed.tolist() == [[0x81, 0x30, 0x10]]
+    assert oracle.decode("e2m3", packed).tolist() == [[0.125, 0.25, 0.375, 0.5]]
+    # an element that straddles a byte boundary: code 63 in slot 1 (bits 6..11)
+    p2 = W.pack_fp6(np.array([[0, 63, 0, 0]], dtype=np.uint8))
+    assert p2.tolist() == [[0xC0, 0x0F, 0x00]]
+    assert oracle.decode("e3m2", p2).tolist() == [[0.0, -28.0, 0.0, 0.0]]
+
+
 def test_e8m0_scales():
     d = oracle.decode_e8m0(np.array([127, 128, 126, 0, 254, 255], dtype=np.uint8))
     assert d[0] == 1.0 and d[1] == 2.0 and d[2] == 0.5
@@ -68,6 +115,8 @@ def _rand_elems(rng, dtype, shape):
     partial sum of the brute-force shapes is exact in float64."""
     if dtype == "e2m1":
         mags = np.array(E2M1_TABLE)
+    elif dtype in W.FP6:
+        mags = np.array(E2M3_GRID if dtype == "e2m3" else E3M2_GRID)
     else:
         mags = W._E4M3_MAG if dtype == "e4m3" else W._E5M2_MAG
         mags = mags[(mags >= 0.25) & (mags <= 8.0)]
@@ -80,7 +129,8 @@ def _encode_elems(v, dtype):
 
 
 @pytest.mark.parametrize("ta,tb,elem", [(False, False, "e4m3"), (True, True, "e5m2"),
-                                        (False, True, "e2m1"), (True, False, "e4m3")])
+                                        (False, True, "e2m1"), (True, False, "e4m3"),
+                                        (False, True, "e2m3"), (False, True, "e3m2")])
 def test_mx_brute_force_exact(ta, tb, elem):
     """MX block scaling against exact rationals: op(A)[i,k] = v * 2^(sa[i,k//32]-127)."""
     rng = np.random.default_rng(7)
@@ -145,7 +195,8 @@ def test_mx_quantize_recipe():
     rng = np.random.default_rng(10)
     x = rng.normal(0, 3.0, size=(4, 96))
     x[1, 32:64] = 0.0
-    for elem, eps in (("e4m3", 2.0 ** -4), ("e5m2", 2.0 ** -3), ("e2m1", 2.0 ** -2)):
+    for elem, eps in (("e4m3", 2.0 ** -4), ("e5m2", 2.0 ** -3), ("e2m1", 2.0 ** -2),
+                      ("e2m3", 2.0 ** -4), ("e3m2", 2.0 ** -3)):
         q, s = W.mx_quantize(x, elem)
         assert s.shape == (4, 3) and s[1, 1] == 127
         scale = oracle.decode_e8m0(s)
@@ -155,10 +206,12 @@ def test_mx_quantize_recipe():
         assert np.array_equal(scale[nz], 2.0 ** (np.floor(np.log2(amax[nz])) - W.MX_EMAX[elem]))
         # per element: one rounding (relative eps, or half the block's smallest step) after
         # clipping |v| / scale to the format's largest finite value
-        top = {"e4m3": W.E4M3_MAX, "e5m2": W.E5M2_MAX, "e2m1": W.E2M1_MAX}[elem]
+        top = {"e4m3": W.E4M3_MAX, "e5m2": W.E5M2_MAX, "e2m1": W.E2M1_MAX, "e2m3": W.E2M3_MAX,
+               "e3m2": W.E3M2_MAX}[elem]
         sc = np.repeat(scale, 32, axis=1)
         clipped = np.sign(x) * np.minimum(np.abs(x), top * sc)
-        step = sc * {"e4m3": 2.0 ** -9, "e5m2": 2.0 ** -16, "e2m1": 0.5}[elem]
+        step = sc * {"e4m3": 2.0 ** -9, "e5m2": 2.0 ** -16, "e2m1": 0.5, "e2m3": 0.125,
+                     "e3m2": 0.0625}[elem]
         assert (np.abs(vals - clipped) <= np.maximum(eps * np.abs(clipped), step / 2)).all()
         # the block maximum sits in [2^emax, 2^(emax+1)) before clipping
         hi = np.abs(x.reshape(4, 3, 32)).max(axis=2)[nz] / scale[nz]

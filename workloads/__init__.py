@@ -30,12 +30,16 @@ from typing import Optional
 
 import numpy as np
 
-DTYPES = ("f32", "f16", "bf16", "e4m3", "e5m2", "e2m1")
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3, "e5m2": 4, "e2m1": 5}
-ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1, "e2m1": 0.5}
+DTYPES = ("f32", "f16", "bf16", "e4m3", "e5m2", "e2m1", "e2m3", "e3m2")
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3, "e5m2": 4, "e2m1": 5, "e2m3": 6,
+              "e3m2": 7}
+ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1, "e2m1": 0.5, "e2m3": 0.75,
+         "e3m2": 0.75}
 STORAGE = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8,
-           "e5m2": np.uint8, "e2m1": np.uint8}
+           "e5m2": np.uint8, "e2m1": np.uint8, "e2m3": np.uint8, "e3m2": np.uint8}
 FP8 = ("e4m3", "e5m2")
+FP6 = ("e2m3", "e3m2")
+PACKED = ("e2m1",) + FP6  # stored several elements per byte along the row
 MX_BLOCK = 32  # elements per E8M0 block scale (OCP microscaling)
 
 EPI_NONE = 0
@@ -44,7 +48,7 @@ EPI_GELU = 2
 
 # Output type for each supported input type.
 OUT_TYPE = {"f32": "f32", "f16": "f16", "bf16": "bf16", "e4m3": "bf16", "e5m2": "bf16",
-            "e2m1": "bf16"}
+            "e2m1": "bf16", "e2m3": "bf16", "e3m2": "bf16"}
 
 
 # --------------------------------------------------------------------------------------------
@@ -169,8 +173,49 @@ def pack_e2m1(codes: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray((c[..., 0::2] & 15) | ((c[..., 1::2] & 15) << 4))
 
 
+def _fp6_magnitudes(mbits: int, bias: int) -> np.ndarray:
+    """Magnitudes of the 32 non-negative codes of an OCP 6-bit type with `mbits` mantissa bits
+    and exponent bias `bias` (no infinities or NaN), increasing with the code."""
+    vals = np.empty(32, dtype=np.float64)
+    for code in range(32):
+        e, m = code >> mbits, code & ((1 << mbits) - 1)
+        vals[code] = (m * 2.0 ** (1 - bias - mbits) if e == 0
+                      else ((1 << mbits) + m) * 2.0 ** (e - bias - mbits))
+    return vals
+
+
+# OCP MX v1.0 6-bit types: E2M3 (bias 1, largest 7.5) and E3M2 (bias 3, largest 28).
+_FP6_MAG = {"e2m3": _fp6_magnitudes(3, 1), "e3m2": _fp6_magnitudes(2, 3)}
+E2M3_MAX = 7.5
+E3M2_MAX = 28.0
+
+
+def to_fp6_codes(y: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 -> 6-bit codes of `dtype` (one per uint8, sign in bit 5): nearest, ties to even,
+    saturating.  NaN has no code; it must not occur."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    if np.isnan(y).any():
+        raise ValueError(f"{dtype} has no NaN")
+    return _nearest_code(y, _FP6_MAG[dtype], 5)
+
+
+def pack_fp6(codes: np.ndarray) -> np.ndarray:
+    """Pack 6-bit codes four per three bytes along the last axis: element i occupies bits
+    6i .. 6i+5 of the row's byte string read as one little-endian integer.  The last axis must
+    be a multiple of 4."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8).astype(np.uint32) & 63
+    if c.shape[-1] % 4:
+        raise ValueError("6-bit rows must hold a multiple of 4 elements")
+    w = c[..., 0::4] | (c[..., 1::4] << 6) | (c[..., 2::4] << 12) | (c[..., 3::4] << 18)
+    out = np.empty(c.shape[:-1] + (c.shape[-1] // 4 * 3,), dtype=np.uint8)
+    out[..., 0::3] = w & 255
+    out[..., 1::3] = (w >> 8) & 255
+    out[..., 2::3] = (w >> 16) & 255
+    return out
+
+
 # Largest binade of each MX element format (2^emax <= max finite < 2^(emax+1)).
-MX_EMAX = {"e4m3": 8, "e5m2": 15, "e2m1": 2}
+MX_EMAX = {"e4m3": 8, "e5m2": 15, "e2m1": 2, "e2m3": 2, "e3m2": 4}
 
 
 def mx_quantize(x: np.ndarray, elem: str):
@@ -178,7 +223,8 @@ def mx_quantize(x: np.ndarray, elem: str):
     run of 32 consecutive values in a row shares the E8M0 scale 2^X with
     X = floor(log2(max|v|)) - emax(elem) (X clamped to [-127, 127]; an all-zero block takes
     X = 0); the elements are v / 2^X rounded to `elem`, saturating.
-    Returns (element storage, rows x K (x K/2 packed for e2m1), uint8 scales rows x K/32)."""
+    Returns (element storage, rows x K (K/2 bytes packed for e2m1, 3K/4 for the 6-bit types),
+    uint8 scales rows x K/32)."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     rows, K = x.shape
     if K % MX_BLOCK:
@@ -196,6 +242,8 @@ def mx_quantize(x: np.ndarray, elem: str):
         q = to_e5m2_bits(scaled)
     elif elem == "e2m1":
         q = pack_e2m1(to_e2m1_codes(scaled))
+    elif elem in FP6:
+        q = pack_fp6(to_fp6_codes(scaled, elem))
     else:
         raise ValueError(f"no MX element format {elem!r}")
     return q, (X + 127).astype(np.uint8)
@@ -216,12 +264,15 @@ def encode(x: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
         return to_e5m2_bits(np.asarray(x, dtype=np.float64) / float(scale))
     if dtype == "e2m1":
         return pack_e2m1(to_e2m1_codes(np.asarray(x, dtype=np.float64) / float(scale)))
+    if dtype in FP6:
+        return pack_fp6(to_fp6_codes(np.asarray(x, dtype=np.float64) / float(scale), dtype))
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
 def fp8_scale(x: np.ndarray, dtype: str) -> np.float32:
     """Per-tensor dequantisation scale: fp32(max|x| / max finite of `dtype`), 1 if all zero."""
-    top = {"e4m3": E4M3_MAX, "e5m2": E5M2_MAX, "e2m1": E2M1_MAX}[dtype]
+    top = {"e4m3": E4M3_MAX, "e5m2": E5M2_MAX, "e2m1": E2M1_MAX, "e2m3": E2M3_MAX,
+           "e3m2": E3M2_MAX}[dtype]
     amax = float(np.max(np.abs(x))) if x.size else 0.0
     return np.float32(amax / top) if amax > 0 else np.float32(1.0)
 
@@ -333,17 +384,17 @@ def make_problem(M: int, N: int, K: int, *, a_type: str = "f32", c_type: Optiona
         # quantise op(A) by rows and op(B) by columns (rows of B^T), then store as asked
         qa, sa_blk = mx_quantize(a, a_type)
         qb, sb_blk = mx_quantize(b.T, b_type)
-        if a_type == "e2m1" or b_type == "e2m1":
+        if a_type in PACKED or b_type in PACKED:
             if trans_a or not trans_b:
-                raise ValueError("packed E2M1 operands are stored K-contiguous (A M x K, B N x K)")
+                raise ValueError("packed MX operands are stored K-contiguous (A M x K, B N x K)")
             A, B = qa, qb
         else:
             A = np.ascontiguousarray(qa.T if trans_a else qa)
             B = np.ascontiguousarray(qb if trans_b else qb.T)
     else:
-        if a_type in FP8 and fp8_scaled:
+        if a_type in FP8 + FP6 and fp8_scaled:
             sa = fp8_scale(a, a_type)
-        if b_type in FP8 and fp8_scaled:
+        if b_type in FP8 + FP6 and fp8_scaled:
             sb = fp8_scale(b, b_type)
         a_st = np.ascontiguousarray(a.T if trans_a else a)
         b_st = np.ascontiguousarray(b.T if trans_b else b)
@@ -417,6 +468,13 @@ def mxfp8_4096(n: int = 4096) -> Problem:
     A,B ~ N(0,1), bf16 out, seed 5."""
     return make_problem(n, n, n, a_type="e4m3", c_type="bf16", seed=5, mx=True,
                         dist_a=("normal", 1.0), dist_b=("normal", 1.0), name=f"mxfp8_{n}")
+
+
+def mxfp6_4096(n: int = 4096, elem: str = "e2m3") -> Problem:
+    """MXFP6 (E2M3 elements packed four per three bytes, E8M0 scale per 32 k) C = A*B, n^3,
+    A stored M x K and B stored N x K, A,B ~ N(0,1), bf16 out, seed 8."""
+    return make_problem(n, n, n, a_type=elem, c_type="bf16", trans_b=True, seed=8, mx=True,
+                        dist_a=("normal", 1.0), dist_b=("normal", 1.0), name=f"mxfp6_{elem}_{n}")
 
 
 def mxfp4_4096(n: int = 4096) -> Problem:

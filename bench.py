@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "TFLOP/s & % MFMA peak: bf16 GEMM+bias+GELU 4096³; fp32/fp16/fp8 sweeps"
 # MI355X published dense peaks (256 CUs at 2.4 GHz).
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2,
-               "e2m1": 10066.3}
+               "e2m1": 10066.3, "e2m3": 10066.3, "e3m2": 10066.3}
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_bf16_bias_gelu_4096.txt")
 
@@ -243,6 +243,7 @@ def sweep_cells():
         ("bf16 4096 (fp8 twin)", "bf16", lambda g: Cell(g, W.bf16_twin_of_fp8(4096))),
         ("fp8 e5m2 4096 (scaled, bf16 out)", "e5m2", lambda g: Cell(g, W.e5m2_4096(4096))),
         ("mxfp8 e4m3 4096 (E8M0 / 32 k)", "e4m3", lambda g: Cell(g, W.mxfp8_4096(4096))),
+        ("mxfp6 e2m3 4096 (E8M0 / 32 k)", "e2m3", lambda g: Cell(g, W.mxfp6_4096(4096))),
         ("mxfp4 e2m1 4096 (E8M0 / 32 k)", "e2m1", lambda g: Cell(g, W.mxfp4_4096(4096))),
         # Quantized decode: one token through a 28672 x 8192 projection with 4-bit weights in
         # groups of 64; three weight copies (397 MB) are cycled so that every launch streams

@@ -20,7 +20,9 @@
  *   - the fused GEMM + bias + GELU versus the decomposed path, and fp8 E4M3 operands:
  *     "Rigel", abstract and section 1 (contribution 7);
  *   - the other low-precision formats it lists beside fp8, block-scaled MXFP4 among them:
- *     "Rigel", section 4 (the format rows of its results).
+ *     "Rigel", section 4 (the format rows of its results); the 6-bit types of the same OCP
+ *     microscaling family (E2M3, E3M2) follow the OCP MX v1.0 specification, which the pages
+ *     do not cover.
  *
  * Conventions shared by every entry point:
  *   - Storage is row-major.  Element (r, c) of a stored matrix X with leading dimension ldX is
@@ -28,11 +30,16 @@
  *     stored K x N (ldb >= N) or, with transB, N x K (ldb >= K); C is M x N (ldc >= N).
  *     Leading dimensions and sizes are counted in elements.
  *   - Supported (A, B, C) type tuples: (F32,F32,F32), (F16,F16,F16), (BF16,BF16,BF16),
- *     (X,Y,BF16) for X, Y in {E4M3, E5M2}, and (E2M1,E2M1,BF16).  E4M3 and E5M2 are the OCP
- *     8-bit floats (E4M3: bias 7, max 448, no infinities; E5M2: bias 15, max 57344, IEEE-style
- *     infinities and NaN).  E2M1 is the OCP 4-bit float (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4,
- *     6), stored two per byte along each stored row: element c of a row sits in byte c / 2,
- *     in the low nibble when c is even.  Any other tuple returns GEMM_ERR_UNSUPPORTED.
+ *     (X,Y,BF16) for X, Y in {E4M3, E5M2}, (E2M1,E2M1,BF16), and (X,Y,BF16) for X, Y in
+ *     {E2M3, E3M2}.  E4M3 and E5M2 are the OCP 8-bit floats (E4M3: bias 7, max 448, no
+ *     infinities; E5M2: bias 15, max 57344, IEEE-style infinities and NaN).  E2M1 is the OCP
+ *     4-bit float (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), stored two per byte along each
+ *     stored row: element c of a row sits in byte c / 2, in the low nibble when c is even.
+ *     E2M3 (bias 1, max 7.5) and E3M2 (bias 3, max 28) are the OCP 6-bit floats, without
+ *     infinities or NaN, stored four per three bytes along each stored row: element c of a row
+ *     occupies bits 6c .. 6c+5 of the row's bytes read as one little-endian integer.  The
+ *     6-bit types need A stored M x K and B stored N x K, and K, lda and ldb multiples of 4
+ *     (rows start on whole bytes).  Any other tuple returns GEMM_ERR_UNSUPPORTED.
  *   - Pointers A, B, C and bias are DEVICE pointers owned by the caller.  C is read (only when
  *     beta != 0) and written.  Nothing is allocated and nothing is retained after a call.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream).  They
@@ -76,7 +83,9 @@ typedef enum gemm_dtype {
   GEMM_BF16 = 2,
   GEMM_E4M3 = 3,
   GEMM_E5M2 = 4,
-  GEMM_E2M1 = 5
+  GEMM_E2M1 = 5,
+  GEMM_E2M3 = 6,
+  GEMM_E3M2 = 7
 } gemm_dtype_t;
 
 /* Epilogue bits.  BIAS adds bias[j] (fp32, length N, one value per output column, broadcast
@@ -153,12 +162,13 @@ GEMM_API gemm_status_t gemm_run_kernel(gemm_handle_t h, gemm_kernel_t kernel, vo
  *
  * sa (M rows of ldsa >= K/32 bytes) and sb (N rows of ldsb >= K/32 bytes) are DEVICE pointers
  * owned by the caller; bytes past K/32 in a row are never used.  Types: A and B in
- * {E4M3, E5M2} (MXFP8, either mix) or both E2M1 (MXFP4); C is BF16.  K must be a multiple of
- * 32.  Errors as gemm_run, plus GEMM_ERR_INVALID_VALUE for K % 32 != 0, a NULL scale array
+ * {E4M3, E5M2} (MXFP8, either mix), both E2M1 (MXFP4), or A and B in {E2M3, E3M2} (MXFP6,
+ * either mix); C is BF16.  K must be a multiple of 32.  Errors as gemm_run, plus GEMM_ERR_INVALID_VALUE for K % 32 != 0, a NULL scale array
  * when K > 0, or ldsa / ldsb < K / 32, and GEMM_ERR_ALIAS when C overlaps a scale array.
  * Matrix-core kernels additionally need 16-byte-aligned sa and sb, ldsa and ldsb multiples of
  * 16, and fewer than 2^32 scale bytes per array; E2M1 operands need A stored M x K and B
- * stored N x K with lda, ldb multiples of 32.  Other arguments take GEMM_KERNEL_SIMT. */
+ * stored N x K with lda, ldb multiples of 32; E2M3 / E3M2 operands need K a multiple of 128 and
+ * lda, ldb multiples of 64.  Other arguments take GEMM_KERNEL_SIMT. */
 GEMM_API gemm_status_t gemm_run_mx(gemm_handle_t h, void* stream, int64_t M, int64_t N,
                                    int64_t K, int transA, int transB, float alpha,
                                    const void* A, int64_t lda, const uint8_t* sa, int64_t ldsa,

@@ -96,14 +96,15 @@ def gate_sampled(p: W.Problem, got: np.ndarray, n: int = 2048, seed: int = 0,
 
 
 POISON = {"f32": np.float32(np.nan).view(np.uint32), "f16": 0xFFFF, "bf16": 0xFFFF,
-          "e4m3": 0xFF, "e5m2": 0xFF, "e2m1": 0xFF}  # e2m1 has no NaN: 0xFF is (-6, -6)
+          "e4m3": 0xFF, "e5m2": 0xFF, "e2m1": 0xFF,   # e2m1 has no NaN: 0xFF is (-6, -6)
+          "e2m3": 0xFF, "e3m2": 0xFF}                 # nor the 6-bit types: all -max
 
 
 def padded_storage(stored: np.ndarray, dtype: str, ld: int) -> np.ndarray:
     """Copy a stored matrix into rows of length ld (elements), filling the padding with NaN
-    patterns (packed E2M1 rows hold ld / 2 bytes)."""
+    patterns (packed E2M1 rows hold ld / 2 bytes, packed 6-bit rows 3 ld / 4)."""
     words = stored.view(np.uint32) if stored.dtype == np.float32 else stored
-    width = ld // 2 if dtype == "e2m1" else ld
+    width = ld // 2 if dtype == "e2m1" else (ld // 4 * 3 if dtype in W.FP6 else ld)
     out = np.full((stored.shape[0], width), POISON[dtype], dtype=words.dtype)
     out[:, :stored.shape[1]] = words
     return out.view(np.float32) if stored.dtype == np.float32 else out
@@ -122,6 +123,8 @@ def run_padded(g, p: W.Problem, ld_fn=aligned_ld, kernel: int = 0):
     lda, ldb, ldc = ld_fn(p.lda), ld_fn(p.ldb), ld_fn(p.ldc)
     if p.a_type == "e2m1":  # whole 16-byte packed rows
         lda, ldb = -(-lda // 32) * 32, -(-ldb // 32) * 32
+    if p.a_type in W.FP6:  # whole 16-byte packed rows: 64 elements are 48 bytes
+        lda, ldb = -(-lda // 64) * 64, -(-ldb // 64) * 64
     Ah = padded_storage(p.A, p.a_type, lda)
     Bh = padded_storage(p.B, p.b_type, ldb)
     Ch = padded_storage(p.C, p.c_type, ldc)

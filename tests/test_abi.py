@@ -189,6 +189,25 @@ def test_packed_fp4_byte_ranges():
     assert chk(at=E2M1, ct=BF16, M=1, K=3, lda=3, C=PA + 2) == OK
 
 
+def test_fp6_arguments():
+    """The 6-bit types: any E2M3 / E3M2 pair with BF16 out, stored K-contiguous (A M x K, B N x
+    K) with K, lda and ldb multiples of 4; rows take 3/4 of a byte per element."""
+    OK, U, AL = tmm.GEMM_OK, tmm.GEMM_ERR_UNSUPPORTED, tmm.GEMM_ERR_ALIAS
+    E2M3, E3M2 = tmm.GEMM_E2M3, tmm.GEMM_E3M2
+    for at in (E2M3, E3M2):
+        for bt in (E2M3, E3M2):
+            assert chk(at=at, bt=bt, ct=BF16, tb=1) == OK
+            assert chk_mx(at=at, bt=bt, tb=1) == OK
+    assert chk(at=E2M3, ct=E2M3, tb=1) == U and chk(at=E2M3, ct=F32, tb=1) == U
+    assert chk(at=E2M3, bt=E4M3, ct=BF16, tb=1) == U and chk(at=E2M1, bt=E3M2, ct=BF16, tb=1) == U
+    assert chk(at=E2M3, ct=BF16, tb=0) == U and chk(at=E2M3, ct=BF16, ta=1, tb=1) == U
+    assert chk(at=E2M3, ct=BF16, tb=1, K=30, lda=32, ldb=32) == U   # K % 4
+    assert chk(at=E2M3, ct=BF16, tb=1, lda=34) == U                 # lda % 4
+    # A: 64 rows x 32 elements (lda 32) = 64 * 24 bytes
+    assert chk(at=E2M3, ct=BF16, tb=1, C=PA + 64 * 24 - 1) == AL
+    assert chk(at=E2M3, ct=BF16, tb=1, C=PA + 64 * 24) == OK
+
+
 def test_mx_arguments():
     OK, V, U, AL = (tmm.GEMM_OK, tmm.GEMM_ERR_INVALID_VALUE, tmm.GEMM_ERR_UNSUPPORTED,
                     tmm.GEMM_ERR_ALIAS)

@@ -1,6 +1,6 @@
-"""GPU parity for the 8- and 4-bit paths beyond E4M3 with per-tensor scales: OCP E5M2, mixed
-E4M3 x E5M2, packed fp4 (E2M1), and the OCP microscaling (MX) block-scaled formats, all through
-the C ABI against the float64 oracle.  Bars as in test_gpu_parity: bit-exact where the
+"""GPU parity for the 8-, 6- and 4-bit paths beyond E4M3 with per-tensor scales: OCP E5M2, mixed
+E4M3 x E5M2, packed fp4 (E2M1), packed 6-bit E2M3 / E3M2, and the OCP microscaling (MX)
+block-scaled formats, all through the C ABI against the float64 oracle.  Bars as in test_gpu_parity: bit-exact where the
 arithmetic is exact, the normalised-error gate K*2^-23 + u_out elsewhere."""
 import itertools
 import zlib
@@ -141,7 +141,7 @@ def test_mx_scale_of_each_block_and_row(g):
         assert pad_ok and np.array_equal(got, Cref), kernel
 
 
-@pytest.mark.parametrize("name", ["e5m2_4096", "mxfp8_4096", "mxfp4_4096"])
+@pytest.mark.parametrize("name", ["e5m2_4096", "mxfp8_4096", "mxfp4_4096", "mxfp6_4096"])
 def test_full_size_sampled(g, name):
     p = getattr(W, name)()
     _, got = H.run(g, p)
@@ -164,3 +164,79 @@ def test_fp4_other_layouts_use_simt(g):
     assert e.value.status == tmm.GEMM_ERR_UNSUPPORTED
     _, got = H.run(g, p, 0, d)
     assert np.array_equal(got, oracle.gemm(p)[0])
+
+
+# ---------------------------------------------------------------------- 6-bit formats --
+
+FP6_PAIRS = [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e2m3", "e3m2"), ("e3m2", "e2m3")]
+
+
+@pytest.mark.parametrize("kernel", list(KERNELS))
+def test_fp6_codes_are_ocp(g, kernel):
+    """Codes that name the 6-bit formats, through every kernel family: E2M3 0x1F = 7.5,
+    0x01 = 1/8, 0x21 = -1/8, 0x08 = 1, 0x10 = 2; E3M2 0x1F = 28, 0x01 = 1/16, 0x0C = 1,
+    0x10 = 2; packed four per three bytes, element i at bits 6i (k = 5 straddles a byte)."""
+    M, N, K = 32, 32, 128
+    cases = (("e2m3", 0x08, 0x10, [7.5, 0.125, -0.125]),
+             ("e3m2", 0x0C, 0x10, [28.0, 0.0625, -0.0625]))
+    for t, one, two, expect in cases:
+        A = np.zeros((M, K), np.uint8)
+        A[0, 0], A[1, 0], A[2, 0] = 0x1F, 0x01, 0x21
+        A[3, 5] = one
+        B = np.zeros((N, K), np.uint8)  # stored N x K
+        B[:, 0] = one
+        B[:, 5] = two
+        p = W.Problem(f"{t}_probe", M, N, K, False, True, 1.0, 0.0, t, t, "bf16", 0,
+                      W.pack_fp6(A), W.pack_fp6(B), np.zeros((M, N), np.uint16), None)
+        _, got = H.run(g, p, KERNELS[kernel])
+        assert list(got[:3, 0]) == expect and (got[:3] == got[:3, :1]).all(), (t, got[:4, :4])
+        assert (got[3] == 2.0).all() and (got[4:] == 0).all(), t
+
+
+@pytest.mark.parametrize("pair,kernel", [(pr, k) for pr in FP6_PAIRS for k in KERNELS])
+def test_mx_fp6_gate(g, pair, kernel):
+    """Block-scaled 6-bit operands (A stored M x K, B stored N x K), K = 384 (three 128-element
+    K tiles), ragged M and N, padded rows (poisoned) and scale rows padded with NaN scales,
+    alpha, beta and the full epilogue."""
+    at, bt = pair
+    M, N, K = 200, 264, 384
+    seed = zlib.crc32(f"mx6/{at}/{bt}/{kernel}".encode()) & 0xFFFF
+    p = W.make_problem(M, N, K, a_type=at, b_type=bt, trans_a=False, trans_b=True, seed=seed,
+                       mx=True, dist_a=("normal", 1.0), dist_b=("normal", 1.0), alpha=0.75,
+                       beta=-0.5, epilogue=W.EPI_BIAS | W.EPI_GELU)
+    got, kname, pad_ok = H.run_padded(g, p, kernel=KERNELS[kernel])
+    res = H.gate_full(p, got)
+    _report(f"mx {at}x{bt} {kernel}", res)
+    assert pad_ok and res.ok, res
+
+
+@pytest.mark.parametrize("pair,kernel", [(pr, k) for pr in FP6_PAIRS[:3] for k in KERNELS])
+def test_fp6_per_tensor_gate(g, pair, kernel):
+    """Per-tensor scaled 6-bit operands (scale max|x| -> the format's largest value)."""
+    at, bt = pair
+    M, N, K = 130, 96, 256
+    seed = zlib.crc32(f"fp6/{at}/{bt}/{kernel}".encode()) & 0xFFFF
+    p = W.make_problem(M, N, K, a_type=at, b_type=bt, trans_a=False, trans_b=True, seed=seed,
+                       dist_a=("normal", 1.0), dist_b=("normal", 1.0), alpha=1.25)
+    got, kname, pad_ok = H.run_padded(g, p, kernel=KERNELS[kernel])
+    res = H.gate_full(p, got)
+    _report(f"fp6 {at}x{bt} {kernel}", res)
+    assert pad_ok and res.ok, res
+
+
+def test_fp6_partial_k_tile_uses_simt(g):
+    """K not a whole number of 128-element tiles (352 = 11 blocks): the scalar kernel serves it,
+    and forcing a matrix-core family is refused."""
+    import tiled_matrix_multiply_amd as tmm
+    M, N, K = 64, 96, 352
+    p = W.make_problem(M, N, K, a_type="e2m3", trans_b=True, seed=12, mx=True,
+                       dist_a=("normal", 1.0), dist_b=("normal", 1.0))
+    d = H.Device(p)
+    assert tmm.select_kernel(g.handle, M, N, K, trans_b=True, a_type="e2m3", A=d.A, B=d.B,
+                             C=d.C) == "simt"
+    with pytest.raises(tmm.GemmError) as e:
+        H.run(g, p, KERNELS["mfma64"], d)
+    assert e.value.status == tmm.GEMM_ERR_UNSUPPORTED
+    _, got = H.run(g, p, 0, d)
+    res = H.gate_full(p, got)
+    assert res.ok, res

@@ -28,9 +28,10 @@ GEMM_ERR_NO_MEMORY = -7
 
 # gemm_dtype_t
 GEMM_F32, GEMM_F16, GEMM_BF16, GEMM_E4M3, GEMM_E5M2, GEMM_E2M1 = 0, 1, 2, 3, 4, 5
+GEMM_E2M3, GEMM_E3M2 = 6, 7
 DTYPE = {"f32": GEMM_F32, "f16": GEMM_F16, "bf16": GEMM_BF16, "e4m3": GEMM_E4M3,
-         "e5m2": GEMM_E5M2, "e2m1": GEMM_E2M1}
-LOWP = ("e4m3", "e5m2", "e2m1")  # output bf16
+         "e5m2": GEMM_E5M2, "e2m1": GEMM_E2M1, "e2m3": GEMM_E2M3, "e3m2": GEMM_E3M2}
+LOWP = ("e4m3", "e5m2", "e2m1", "e2m3", "e3m2")  # output bf16
 
 # epilogue bits
 GEMM_EPI_NONE, GEMM_EPI_BIAS, GEMM_EPI_GELU = 0, 1, 2
@@ -249,8 +250,9 @@ def run(handle, A, B, C, *, M, N, K, trans_a=False, trans_b=False, alpha=1.0, be
         scale_b=1.0, lda=None, ldb=None, ldc=None, sa_blk=None, sb_blk=None, ldsa=None,
         ldsb=None, kernel=GEMM_KERNEL_AUTO, stream=None):
     """GEMM on device tensors holding storage words (A, B, C contiguous row-major unless ld*
-    is given; E2M1 holds two elements per byte).  With sa_blk / sb_blk (device uint8 tensors
-    of E8M0 scales, M x ldsa and N x ldsb) the call is block-scaled (gemm_run_mx).  Raises
+    is given; E2M1 holds two elements per byte, E2M3 / E3M2 four per three bytes).  With
+    sa_blk / sb_blk (device uint8 tensors of E8M0 scales, M x ldsa and N x ldsb) the call is
+    block-scaled (gemm_run_mx).  Raises
     GemmError on a negative status.  Asynchronous on `stream` (default: torch's current
     stream)."""
     b_type = b_type or a_type

@@ -32,6 +32,14 @@ TGEMM_F8_LAUNCHER(mx_e4m3_e5m2)
 TGEMM_F8_LAUNCHER(mx_e5m2_e4m3)
 TGEMM_F8_LAUNCHER(e2m1)
 TGEMM_F8_LAUNCHER(mx_e2m1)
+TGEMM_F8_LAUNCHER(e2m3)
+TGEMM_F8_LAUNCHER(e3m2)
+TGEMM_F8_LAUNCHER(e2m3_e3m2)
+TGEMM_F8_LAUNCHER(e3m2_e2m3)
+TGEMM_F8_LAUNCHER(mx_e2m3)
+TGEMM_F8_LAUNCHER(mx_e3m2)
+TGEMM_F8_LAUNCHER(mx_e2m3_e3m2)
+TGEMM_F8_LAUNCHER(mx_e3m2_e2m3)
 #undef TGEMM_F8_LAUNCHER
 hipError_t launch_bias_gelu(void* C, int64_t ldc, int M, int N, int c_type, const float* bias,
                             uint32_t epi, int cu_count, hipStream_t s);
@@ -62,7 +70,7 @@ struct Args {
   int64_t ldsb;
 };
 
-// Storage bits per element (E2M1 packs two per byte).
+// Storage bits per element (E2M1 packs two per byte, E2M3 / E3M2 four per three bytes).
 int ebits(gemm_dtype_t t) {
   switch (t) {
     case GEMM_F32: return 32;
@@ -71,14 +79,18 @@ int ebits(gemm_dtype_t t) {
     case GEMM_E4M3: return 8;
     case GEMM_E5M2: return 8;
     case GEMM_E2M1: return 4;
+    case GEMM_E2M3: return 6;
+    case GEMM_E3M2: return 6;
     default: return 0;
   }
 }
 
 bool is_fp8(gemm_dtype_t t) { return t == GEMM_E4M3 || t == GEMM_E5M2; }
+bool is_fp6(gemm_dtype_t t) { return t == GEMM_E2M3 || t == GEMM_E3M2; }
 
 bool supported_tuple(gemm_dtype_t a, gemm_dtype_t b, gemm_dtype_t c) {
   if (is_fp8(a) && is_fp8(b)) return c == GEMM_BF16;
+  if (is_fp6(a) && is_fp6(b)) return c == GEMM_BF16;
   if (a != b) return false;
   switch (a) {
     case GEMM_F32: return c == GEMM_F32;
@@ -108,7 +120,11 @@ gemm_status_t check(const Args& a) {
   if (a.epi & ~(GEMM_EPI_BIAS | GEMM_EPI_GELU)) return GEMM_ERR_INVALID_VALUE;
   if (!ebits(a.at) || !ebits(a.bt) || !ebits(a.ct)) return GEMM_ERR_UNSUPPORTED;
   if (!supported_tuple(a.at, a.bt, a.ct)) return GEMM_ERR_UNSUPPORTED;
-  if (a.mx && !(is_fp8(a.at) || a.at == GEMM_E2M1)) return GEMM_ERR_UNSUPPORTED;
+  if (a.mx && !(is_fp8(a.at) || a.at == GEMM_E2M1 || is_fp6(a.at))) return GEMM_ERR_UNSUPPORTED;
+  // 6-bit operands: stored K-contiguous, rows starting on whole bytes
+  if (is_fp6(a.at) && (a.transA != 0 || a.transB != 1 || a.K % 4 != 0 || a.lda % 4 != 0 ||
+                       a.ldb % 4 != 0))
+    return GEMM_ERR_UNSUPPORTED;
   if (a.M > kMaxDim || a.N > kMaxDim || a.K > kMaxDim) return GEMM_ERR_UNSUPPORTED;
   if (a.M == 0 || a.N == 0) return GEMM_OK;  // nothing to compute
   if (!a.C) return GEMM_ERR_INVALID_VALUE;
@@ -143,6 +159,10 @@ bool mfma_aligned(const Args& a) {
   if (a.at == GEMM_E2M1) {
     // packed fp4 is staged as bytes along K: A stored M x K, B stored N x K, whole bytes
     if (a.transA != 0 || a.transB != 1 || a.K % 2 != 0) return false;
+  }
+  if (is_fp6(a.at)) {
+    // packed 6-bit rows are staged as bytes along K in whole 96-byte (128-element) K tiles
+    if (a.K % 128 != 0) return false;
   }
   if (a.K > 0) {
     if (!al16(a.A) || !al16(a.B)) return false;
@@ -251,6 +271,17 @@ using Launcher = hipError_t (*)(const tgemm::GemmParams&, int, bool, bool, hipSt
 Launcher f8_launcher(gemm_dtype_t at, gemm_dtype_t bt, bool mx) {
   using namespace tgemm;
   if (at == GEMM_E2M1) return mx ? launch_mfma_mx_e2m1 : launch_mfma_e2m1;
+  if (is_fp6(at)) {
+    const bool a3 = at == GEMM_E3M2, b3 = bt == GEMM_E3M2;
+    if (mx) {
+      if (!a3 && !b3) return launch_mfma_mx_e2m3;
+      if (a3 && b3) return launch_mfma_mx_e3m2;
+      return a3 ? launch_mfma_mx_e3m2_e2m3 : launch_mfma_mx_e2m3_e3m2;
+    }
+    if (!a3 && !b3) return launch_mfma_e2m3;
+    if (a3 && b3) return launch_mfma_e3m2;
+    return a3 ? launch_mfma_e3m2_e2m3 : launch_mfma_e2m3_e3m2;
+  }
   const bool a5 = at == GEMM_E5M2, b5 = bt == GEMM_E5M2;
   if (mx) {
     if (!a5 && !b5) return launch_mfma_mx_e4m3;
@@ -314,6 +345,11 @@ gemm_status_t run_impl(gemm_handle_t h, gemm_kernel_t kernel, void* stream, cons
       p.K = (int)(a.K / 2);
       p.lda = a.lda / 2;
       p.ldb = a.ldb / 2;
+    } else if (is_fp6(a.at)) {
+      // the same for packed 6-bit rows: three bytes per four elements
+      p.K = (int)(a.K / 4 * 3);
+      p.lda = a.lda / 4 * 3;
+      p.ldb = a.ldb / 4 * 3;
     }
     // Storage contiguous along M (A stored K x M) or along N (B stored K x N).
     const bool a_mn = a.transA != 0, b_mn = a.transB == 0;
@@ -325,7 +361,9 @@ gemm_status_t run_impl(gemm_handle_t h, gemm_kernel_t kernel, void* stream, cons
       case GEMM_BF16: err = tgemm::launch_mfma_bf16(p, tile, a_mn, b_mn, s, ks); break;
       case GEMM_E4M3:
       case GEMM_E5M2:
-      case GEMM_E2M1: err = f8_launcher(a.at, a.bt, a.mx)(p, tile, a_mn, b_mn, s); break;
+      case GEMM_E2M1:
+      case GEMM_E2M3:
+      case GEMM_E3M2: err = f8_launcher(a.at, a.bt, a.mx)(p, tile, a_mn, b_mn, s); break;
       default: return GEMM_ERR_UNSUPPORTED;
     }
   } else {

@@ -8,7 +8,7 @@ namespace tgemm {
 
 // E2M1 is OCP fp4: two elements per byte along the storage row, the even element in the
 // low nibble.
-enum DType : int { F32 = 0, F16 = 1, BF16 = 2, E4M3 = 3, E5M2 = 4, E2M1 = 5 };
+enum DType : int { F32 = 0, F16 = 1, BF16 = 2, E4M3 = 3, E5M2 = 4, E2M1 = 5, E2M3 = 6, E3M2 = 7 };
 enum : uint32_t { EPI_BIAS = 1u, EPI_GELU = 2u };
 
 // Arguments every GEMM kernel receives (by value, in the kernel-argument segment).
@@ -45,8 +45,11 @@ template <> struct DTypeInfo<F16> { static constexpr int bytes = 2; };
 template <> struct DTypeInfo<BF16> { static constexpr int bytes = 2; };
 template <> struct DTypeInfo<E4M3> { static constexpr int bytes = 1; };
 template <> struct DTypeInfo<E5M2> { static constexpr int bytes = 1; };
-// The matrix-core kernels see packed fp4 rows as bytes (two elements each).
+// The matrix-core kernels see packed fp4 rows as bytes (two elements each), and packed 6-bit
+// rows as bytes too (four elements per three).
 template <> struct DTypeInfo<E2M1> { static constexpr int bytes = 1; };
+template <> struct DTypeInfo<E2M3> { static constexpr int bytes = 1; };
+template <> struct DTypeInfo<E3M2> { static constexpr int bytes = 1; };
 
 // ------------------------------------------------------------------ element conversions --
 
@@ -87,6 +90,32 @@ __device__ __forceinline__ float e2m1_bits_to_float(uint32_t q) {
   return s ? -v : v;
 }
 
+// OCP 6-bit floats (MX v1.0), no infinities or NaN, exact in fp32:
+//   E2M3: 1 sign, 2 exponent (bias 1), 3 mantissa bits, subnormals m * 2^-3;
+//   E3M2: 1 sign, 3 exponent (bias 3), 2 mantissa bits, subnormals m * 2^-4.
+__device__ __forceinline__ float e2m3_bits_to_float(uint32_t q) {
+  const uint32_t s = (q >> 5) & 1u, e = (q >> 3) & 3u, m = q & 7u;
+  const float v = e == 0 ? 0.125f * (float)m : __uint_as_float(((e + 126u) << 23) | (m << 20));
+  return s ? -v : v;
+}
+__device__ __forceinline__ float e3m2_bits_to_float(uint32_t q) {
+  const uint32_t s = (q >> 5) & 1u, e = (q >> 2) & 7u, m = q & 3u;
+  const float v = e == 0 ? 0.0625f * (float)m : __uint_as_float(((e + 124u) << 23) | (m << 21));
+  return s ? -v : v;
+}
+
+// Element idx of packed 6-bit storage: bits 6 idx .. 6 idx + 5 of the little-endian byte
+// string; the following byte is read only when the element reaches into it (an element never
+// crosses its group of three bytes).
+__device__ __forceinline__ uint32_t fp6_code(const void* base, int64_t idx) {
+  const uint8_t* b = reinterpret_cast<const uint8_t*>(base);
+  const int64_t bit = 6 * idx, by = bit >> 3;
+  const uint32_t sh = (uint32_t)(bit & 7);
+  uint32_t v = (uint32_t)b[by] >> sh;
+  if (sh > 2u) v |= (uint32_t)b[by + 1] << (8u - sh);
+  return v & 63u;
+}
+
 // OCP E8M0 block scale 2^(e - 127) (e = 255 is NaN), exact in fp32: 2^-126 and up are
 // normal numbers (exponent field e), 2^-127 is the subnormal 0x00400000.
 __device__ __forceinline__ float e8m0_to_float(uint32_t e) {
@@ -109,6 +138,8 @@ __device__ __forceinline__ float load_as_float(const void* base, int64_t idx) {
   else if constexpr (DT == BF16) return bf16_bits_to_float(reinterpret_cast<const uint16_t*>(base)[idx]);
   else if constexpr (DT == E4M3) return e4m3_bits_to_float(reinterpret_cast<const uint8_t*>(base)[idx]);
   else if constexpr (DT == E5M2) return e5m2_bits_to_float(reinterpret_cast<const uint8_t*>(base)[idx]);
+  else if constexpr (DT == E2M3) return e2m3_bits_to_float(fp6_code(base, idx));
+  else if constexpr (DT == E3M2) return e3m2_bits_to_float(fp6_code(base, idx));
   else return e2m1_bits_to_float((reinterpret_cast<const uint8_t*>(base)[idx >> 1] >> (4 * (idx & 1))) & 15u);
 }
 

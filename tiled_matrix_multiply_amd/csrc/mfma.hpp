@@ -141,20 +141,29 @@ template <> struct MmaOp<F32> {
   }
 };
 
-// 8- and 4-bit inputs (OCP E4M3, E5M2, E2M1): the 32x32x64 f8f6f4 op with a format code per
-// operand and one E8M0 scale per lane and operand.  A lane holds 32 consecutive k of its row,
-// which is exactly one 32-element block of the OCP microscaling (MX) formats, so the lane's
-// scale byte is its block's scale; per-tensor scaling passes 2^0 (code 127) and folds the
-// scales into alpha.  XT is the type of the first operand (the B fragment), YT of the second.
-// KG counts staged bytes per k-group: 64 for 8-bit elements, 32 for packed fp4 (64 elements).
+// 8-, 6- and 4-bit inputs (OCP E4M3, E5M2, E2M3, E3M2, E2M1): the 32x32x64 f8f6f4 op with a
+// format code per operand and one E8M0 scale per lane half and operand: lanes 32h .. 32h+31
+// give the scale of the k-group's block h (its k 32h .. 32h+31), which with per-tensor scaling
+// is 2^0 (code 127, the scales folded into alpha).  XT is the type of the first operand (the B
+// fragment), YT of the second.  KG counts staged bytes per k-group of 64 elements: 64 (8-bit),
+// 48 (packed 6-bit), 32 (packed 4-bit).  Where each element sits in a lane differs by width (an
+// in-bounds one-instruction probe): an 8-bit lane half h holds k 16h .. 16h+15 and
+// 32+16h .. 32+16h+15 (bytes 0-15 and 16-31), a 6- or 4-bit lane half h holds k 32h .. 32h+31 in
+// order, element i at bits 6i (4i) of its 6 (4) registers.  So 6-bit pairs only with 6-bit and
+// 4-bit with 4-bit.
 template <int DT>
-constexpr int f8f6f4_format() { return DT == E4M3 ? 0 : (DT == E5M2 ? 1 : 4); }
+constexpr int f8f6f4_format() {
+  return DT == E4M3 ? 0 : DT == E5M2 ? 1 : DT == E2M3 ? 2 : DT == E3M2 ? 3 : 4;
+}
+template <int DT>
+constexpr bool is_fp6() { return DT == E2M3 || DT == E3M2; }
 
 template <int XT, int YT>
 struct MmaScaled {
   static_assert((XT == E2M1) == (YT == E2M1), "fp4 pairs only with fp4");
-  static constexpr bool FP4 = XT == E2M1;
-  static constexpr int KG = FP4 ? 32 : 64, CPL = FP4 ? 1 : 2;
+  static_assert(is_fp6<XT>() == is_fp6<YT>(), "6-bit pairs only with 6-bit");
+  static constexpr bool FP4 = XT == E2M1, FP6 = is_fp6<XT>();
+  static constexpr int KG = FP4 ? 32 : (FP6 ? 48 : 64), CPL = FP4 ? 1 : 2;
   using Frag = typename std::conditional<FP4, u32x4, u32x8>::type;
   __device__ static __forceinline__ i32x8 widen(const Frag& x) {
     if constexpr (FP4) return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
@@ -168,7 +177,7 @@ struct MmaScaled {
 };
 
 template <int DT>
-constexpr bool is_f8f6f4() { return DT == E4M3 || DT == E5M2 || DT == E2M1; }
+constexpr bool is_f8f6f4() { return DT == E4M3 || DT == E5M2 || DT == E2M1 || is_fp6<DT>(); }
 
 // ----------------------------------------------------------------------- configuration --
 
@@ -179,7 +188,7 @@ constexpr bool is_f8f6f4() { return DT == E4M3 || DT == E5M2 || DT == E2M1; }
 template <int TILE>
 constexpr int default_stages() { return TILE == 128 ? 3 : 2; }
 
-// DT_ / BT_: types of A and B (they differ only within the 8-bit family); MX_: OCP
+// DT_ / BT_: types of A and B (they differ only within the 8-bit or the 6-bit family); MX_: OCP
 // microscaling, one E8M0 scale per 32 k of each row of op(A) and column of op(B).
 // QB_: B is given as affine group-quantized codes of QB_ bits (4 or 8; 0 = B is plain data),
 // dequantised into the 16-bit type of A as it is staged (the B tile then looks exactly like a
@@ -202,16 +211,21 @@ struct MfmaCfg {
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 accumulators per wave
   static constexpr int ES = DTypeInfo<DT_>::bytes;
-  static constexpr int BKE = 128 / ES;                 // K elements per staged tile (128 bytes)
+  static constexpr bool FP6 = is_fp6<DT_>();
+  // K elements per staged tile: 128 bytes of each row, or for packed 6-bit rows 96 bytes (128
+  // elements, two k-groups) in the 128-byte LDS row; the copies still move the row's 128 bytes
+  // from the tile start, and the fragment reads never touch the last 32.
+  static constexpr int BKE = FP6 ? 96 : 128 / ES;
   static constexpr bool A_MN = A_MN_, B_MN = B_MN_;    // operand stored contiguous along M/N
+  static_assert(!FP6 || (!A_MN_ && !B_MN_), "packed 6-bit operands are staged K-contiguous");
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;  // one staged K tile
   static constexpr int S = S_;  // LDS buffers per operand: K tiles kt .. kt+S-1 are resident or in flight
   static constexpr int QB = QB_;
   static_assert(QB_ == 0 || ((QB_ == 4 || QB_ == 8) && !B_MN_ && !MX_ && S_ == 2 &&
                              (DT_ == BF16 || DT_ == F16)),
                 "quantized B: K-contiguous codes, 16-bit A, two stages");
-  // MX scales: a staged K tile covers BPT 32-element blocks (4 for 8-bit elements, 8 for
-  // packed fp4); each row's 16 consecutive scale bytes (TPC = 16 / BPT tiles) are copied as one
+  // MX scales: a staged K tile covers BPT 32-element blocks (4 for 8- and 6-bit elements, 8
+  // for packed fp4); each row's 16 consecutive scale bytes (TPC = 16 / BPT tiles) are copied as one
   // piece into a double-buffered region of (BM + BN) rows x 16 bytes after the data stages.
   static constexpr int BPT = (DT_ == E2M1) ? 8 : 4, TPC = 16 / BPT;
   static constexpr int GS = S * (A_BYTES + B_BYTES);  // one K group's stages
@@ -480,13 +494,40 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
     asm volatile("" : "+v"(v));
     return v;
   };
+  // Packed 6-bit K-contiguous tiles: piece t of k-group g is the 8 bytes at row byte
+  // 48 g + 24 lhalf + 8 t, i.e. logical chunk c = that / 16 at byte (that % 16) of it, held at
+  // position c ^ kswz(row); for even-parity fragment rows kswz(row) = s_lane, and odd ones flip
+  // bit 2 of the position (offset ^ 64), as for the other widths.
+  int k6[C::FP6 ? 6 : 1];
+  if constexpr (C::FP6) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const int rb = 48 * g + 24 * lhalf + 8 * t;
+        int v = lrow * 128 + (((rb >> 4) ^ s_lane) << 4) + (rb & 15);
+        asm volatile("" : "+v"(v));
+        k6[3 * g + t] = v;
+      }
+  }
   // Fragment f of an operand for k-group g, from the operand buffer at byte offset `boff`
   // (uniform) past the operand's first buffer.
   auto read_frag = [&](uint32_t boff, auto opnd, int wbase, int f, int g, const int* kb,
                        const int* mb, Frag& out) {
     using O = decltype(opnd);
     const uint8_t* s = gsm + O::LDS_OFF + boff;
-    if constexpr (!O::MN) {
+    if constexpr (!O::MN && C::FP6) {
+      // the lane half's 32 elements: bytes 48 g + 24 h .. + 23 of the row, three 8-byte pieces
+      // (each inside one 16-byte chunk) into registers 0..5; registers 6 and 7 stay zero
+      const int par = ((wbase >> 5) + f) & 1;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const int off = (wbase + f * 32) * 128 + (k6[3 * g + t] ^ (64 * par));
+        const u32x2 v = *reinterpret_cast<const u32x2*>(s + off);
+        out[2 * t] = v[0];
+        out[2 * t + 1] = v[1];
+      }
+    } else if constexpr (!O::MN) {
       const int par = ((wbase >> 5) + f) & 1;
 #pragma unroll
       for (int x = 0; x < Op::CPL; ++x) {
@@ -556,6 +597,16 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   constexpr int AS = GROUPED ? C::FM : 1;   // A fragments per register set
   constexpr int BS = GROUPED ? 2 : 1;       // B register sets
   Frag af[2][AS], bf[BS][C::FN];
+  if constexpr (C::FP6) {  // registers 6 and 7 of a 6-bit fragment are never loaded
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < AS; ++j) af[i][j] = Frag{};
+#pragma unroll
+    for (int i = 0; i < BS; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) bf[i][j] = Frag{};
+  }
   // MX: the E8M0 scale byte of each fragment lane's 32-element block, read from the staged
   // scale rows next to the fragment itself (scA / scB mirror af / bf); 127 (2^0) otherwise.
   // Blocks past K (the last tile's zero-filled tail) take 2^0 whatever the padding holds.
@@ -1005,13 +1056,14 @@ hipError_t launch_mfma_cfg(GemmParams p, hipStream_t s) {
 
 // Tile families: 0 -> 64x64 (2x2 waves of 32x32), 1 -> 128x128 (2x2 waves of 64x64),
 // 2 -> 256x256 (2x4 waves of 128x64).  BT: type of B (differs from A only in the 8-bit
-// family); MX: block-scaled.  Packed fp4 is staged K-contiguous only (A stored M x K, B stored
-// N x K): the other layouts return an error (the host never routes them here).
+// family); MX: block-scaled.  Packed fp4 and 6-bit operands are staged K-contiguous only (A
+// stored M x K, B stored N x K): the other layouts return an error (the host never routes them
+// here).
 template <int DT, int TILE, int WM, int WN, int BT, bool MX, int KS = 1>
 hipError_t launch_mfma_layout(const GemmParams& p, bool a_mn, bool b_mn, hipStream_t s) {
   constexpr int S = default_stages<TILE>();
   if (!a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, false, S, BT, MX, 0, KS>>(p, s);
-  if constexpr (DT == E2M1) {
+  if constexpr (DT == E2M1 || is_fp6<DT>()) {
     return hipErrorInvalidValue;
   } else {
     if (!a_mn && b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, true, S, BT, MX, 0, KS>>(p, s);

@@ -74,6 +74,10 @@ hipError_t launch_simt(const GemmParams& p, int a_type, int b_type, int transA, 
     case E5M2 * 8 + E4M3: return launch<E5M2, E4M3, BF16>(p, transA, transB, s);
     case E5M2 * 8 + E5M2: return launch<E5M2, E5M2, BF16>(p, transA, transB, s);
     case E2M1 * 8 + E2M1: return launch<E2M1, E2M1, BF16>(p, transA, transB, s);
+    case E2M3 * 8 + E2M3: return launch<E2M3, E2M3, BF16>(p, transA, transB, s);
+    case E2M3 * 8 + E3M2: return launch<E2M3, E3M2, BF16>(p, transA, transB, s);
+    case E3M2 * 8 + E2M3: return launch<E3M2, E2M3, BF16>(p, transA, transB, s);
+    case E3M2 * 8 + E3M2: return launch<E3M2, E3M2, BF16>(p, transA, transB, s);
     default: return hipErrorInvalidValue;
   }
 }

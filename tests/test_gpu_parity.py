@@ -310,3 +310,30 @@ def test_k_split_paths(g, dtype):
         got, kname, pad_ok = H.run_padded(g, p, kernel=KERNELS["mfma64"])
         res = H.gate_full(p, got)
         assert res.ok and pad_ok, f"{dtype} {M}x{N}x{K}: {res}"
+
+
+# ------------------------------------------------------------------- large extents --
+
+@pytest.mark.parametrize("case", ["long_k", "tall", "wide", "long_rows"])
+def test_large_extents(g, case):
+    """Sizes far from the square workloads: K = 2^17 (the bound K * 2^-23 at its largest
+    tested value, and the K split), 2^18 rows or columns (4096 tiles, one workgroup per tile
+    and beyond 65535 tiles of the scalar kernel's grid.y would be), and rows of 2^21 elements
+    (4 MiB: the staging copies' 32-bit offsets span 63 such rows)."""
+    if case == "long_k":
+        p = W.make_problem(64, 96, 1 << 17, a_type="bf16", seed=70, dist_a=("normal", 1.0),
+                           dist_b=("normal", 1.0), epilogue=W.EPI_BIAS | W.EPI_GELU)
+        got, kname, pad_ok = H.run_padded(g, p)
+    elif case in ("tall", "wide"):
+        M, N = (1 << 18, 16) if case == "tall" else (16, 1 << 18)
+        p = W.make_problem(M, N, 64, a_type="f16", seed=71, dist_a=("normal", 1.0),
+                           dist_b=("normal", 1.0), beta=0.5, alpha=-1.0)
+        got, kname, pad_ok = H.run_padded(g, p)
+    else:
+        p = W.make_problem(64, 80, 96, a_type="bf16", seed=72, dist_a=("normal", 1.0),
+                           dist_b=("normal", 1.0), trans_b=True)
+        got, kname, pad_ok = H.run_padded(g, p, ld_fn=lambda w: w if w == p.N else 1 << 21)
+    res = H.gate_full(p, got)
+    print(f"[large] {case} {p.M}x{p.N}x{p.K} {kname}: {res}", flush=True)
+    assert kname != "simt", kname
+    assert pad_ok and res.ok, res

@@ -282,12 +282,19 @@ def counter_pass(g, reps: int, copy_bytes: int) -> None:
         print(f"[counter-pass] copied {copy_bytes} bytes 3 times", file=sys.stderr, flush=True)
 
 
+def recipe_hash(recipe: dict) -> str:
+    """Hash of a workload's input recipe (sizes, types, distributions, seed, RNG, draw order)."""
+    blob = json.dumps(recipe, sort_keys=True, default=str).encode()
+    return hashlib.sha256(blob).hexdigest()[:16]
+
+
 def summarize(name, cell: Cell, ms: np.ndarray, dtype: str) -> dict:
     p = cell.p
     med = float(np.median(ms))
     lo, hi = bootstrap_ci(ms)
     tf = p.flops / (med * 1e-3) / 1e12
     row = {"cell": name, "kernel": cell.kernel, "M": p.M, "N": p.N, "K": p.K, "dtype": dtype,
+           "seed": p.recipe.get("seed"), "recipe_hash": recipe_hash(p.recipe),
            "reps": int(len(ms)), "median_us": round(med * 1e3, 3),
            "ci95_us": [round(hi_ * 1e3, 3) for hi_ in (lo, hi)],
            "tflops": round(tf, 2),
@@ -498,7 +505,8 @@ def main():
         "data": "synthetic (seeded numpy draws: A~N(0,1), B~N(0,1/K), bias~N(0,0.01); bf16 RNE)",
         "config": {"workload": "bf16 GEMM + bias + erf-GELU fused, M=N=K=4096, row-major NN, "
                                "fp32 accumulate, bf16 out",
-                   "M": 4096, "N": 4096, "K": 4096, "kernel": head.kernel},
+                   "M": 4096, "N": 4096, "K": 4096, "kernel": head.kernel,
+                   "seed": head_p.recipe["seed"], "recipe_hash": recipe_hash(head_p.recipe)},
         "pct_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
         "median_tflops": head_row["tflops"],
         "ci95_tflops": head_row["tflops_ci95"],

@@ -232,7 +232,7 @@ GEMM_API gemm_status_t gemm_bias_gelu(gemm_handle_t h, void* stream, int64_t M, 
  * Errors: as gemm_run (C overlapping X, Wq, scales, offsets or bias is GEMM_ERR_ALIAS), plus
  * GEMM_ERR_INVALID_VALUE for bits not 4 or 8, group < 1, K % group != 0, an odd K with 4-bit
  * codes, or ldx / ldw / ldg too small; GEMM_ERR_UNSUPPORTED for an x_type other than F16 / BF16.
- * Kernel choice (AUTO): GEMM_KERNEL_QGEMV for M <= 4 when its staged activations fit 64 KiB
+ * Kernel choice (AUTO): GEMM_KERNEL_QGEMV for M <= 4 when its staged activations fit 80 KiB
  * of LDS, GEMM_KERNEL_QMFMA otherwise, each when its alignment needs hold (below), else
  * GEMM_KERNEL_SIMT (one output per thread, any alignment). */
 GEMM_API gemm_status_t gemm_run_q(gemm_handle_t h, void* stream, int64_t M, int64_t N,

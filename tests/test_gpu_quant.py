@@ -70,6 +70,8 @@ def test_qgemv_parity(g, M, bits, G, x_type):
     (2, 50, 2112, 4, 64),   # 33 groups (odd), one unit
     (1, 40, 8320, 4, 32),   # 260 groups: per-lane scales and offsets, three units
     (1, 33, 8192, 8, 64),   # 8-bit: four units
+    (4, 77, 8192, 4, 64),   # 68 KiB of staged activations: more than 64 KiB of dynamic LDS
+    (3, 50, 6144, 4, 64),   # three rows (the four-row kernel, one masked)
 ])
 def test_qgemv_unit_shapes(g, M, N, K, bits, G):
     """Row blocks that take several units of chunks, ragged last units, and both forms of the
@@ -98,6 +100,10 @@ def test_q_auto_choices(g):
               offsets=0x40000000, C=0x50000000)
     assert g.select_kernel_q(1, 64, 256, **kw) == "qgemv"
     assert g.select_kernel_q(4, 64, 256, **kw) == "qgemv"
+    # four rows of K = 8192 stage 68 KiB of activations (over 64 KiB, within the 80 KiB the
+    # kernel takes); K = 10240 needs 85 KiB: the matrix-core kernel
+    assert g.select_kernel_q(4, 64, 8192, **kw) == "qgemv"
+    assert g.select_kernel_q(4, 64, 10240, **kw) == "qmfma"
     # group 8 is not a whole number of 16-byte chunks: the scalar kernel
     assert g.select_kernel_q(1, 64, 256, **dict(kw, group=8)) == "simt"
     # a code row stride that is not a multiple of 16 bytes

@@ -17,7 +17,7 @@ namespace {
 
 constexpr int64_t kMaxDim = 0x7fffffff;
 constexpr int64_t kQgemvMaxRows = 4;
-constexpr int64_t kQgemvMaxLds = 64 * 1024;
+constexpr int64_t kQgemvMaxLds = 80 * 1024;  // two workgroups still fit a compute unit's 160 KiB
 
 struct QArgs {
   int64_t M, N, K;
@@ -78,7 +78,7 @@ gemm_status_t check_q(const QArgs& a) {
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Needs of the matrix-vector kernel: 16-byte code chunks that never straddle a group, the
-// staged activations within 64 KiB of LDS, and 32-bit chunk counts.
+// staged activations within 80 KiB of LDS, and 32-bit chunk counts.
 bool qgemv_ok(const QArgs& a) {
   const int ch = a.bits == 4 ? 32 : 16;
   if (a.M > kQgemvMaxRows) return false;

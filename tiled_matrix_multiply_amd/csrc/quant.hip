@@ -407,18 +407,37 @@ inline bool qgemv_shared_so(const QParams& p) {
          ((reinterpret_cast<uintptr_t>(p.S) | reinterpret_cast<uintptr_t>(p.O)) & 3u) == 0;
 }
 
-template <int XT, int BITS, int MT>
-hipError_t launch_qgemv_t(const QParams& p, int cu_count, hipStream_t s) {
+// One launch of the persistent matrix-vector kernel: as many workgroups per compute unit as
+// are resident at once (registers and LDS decide it: the runtime's occupancy query, at most
+// QGEMV_WG_PER_CU), so that no workgroup waits for a slot and the row blocks are shared evenly.
+// More than 64 KiB of dynamic LDS (four activation rows of K = 8192) is declared first.
+template <class Kernel>
+hipError_t launch_qgemv_kernel(Kernel kernel, const QParams& p, int cu_count, size_t lds,
+                               hipStream_t s) {
+  if (lds > 64 * 1024) {
+    const hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 64 * QGEMV_WAVES, lds) !=
+          hipSuccess || occ < 1)
+    occ = 1;
+  if (occ > QGEMV_WG_PER_CU) occ = QGEMV_WG_PER_CU;
   const int64_t rows_per_wg = (int64_t)QGEMV_WAVES * QGEMV_ROWS;
   const int64_t blocks = (p.N + rows_per_wg - 1) / rows_per_wg;
-  const int64_t cap = (int64_t)cu_count * QGEMV_WG_PER_CU;
+  const int64_t cap = (int64_t)cu_count * occ;
   const unsigned grid = (unsigned)(blocks < cap ? blocks : cap);
-  const size_t lds = (size_t)qgemv_lds_bytes(p.M, p.K, BITS);
-  if (qgemv_shared_so(p))
-    hipLaunchKernelGGL((qgemv_kernel<XT, BITS, MT, true>), dim3(grid), dim3(64 * QGEMV_WAVES), lds, s, p);
-  else
-    hipLaunchKernelGGL((qgemv_kernel<XT, BITS, MT, false>), dim3(grid), dim3(64 * QGEMV_WAVES), lds, s, p);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * QGEMV_WAVES), lds, s, p);
   return hipGetLastError();
+}
+
+template <int XT, int BITS, int MT>
+hipError_t launch_qgemv_t(const QParams& p, int cu_count, hipStream_t s) {
+  const size_t lds = (size_t)qgemv_lds_bytes(p.M, p.K, BITS);
+  if (qgemv_shared_so(p)) return launch_qgemv_kernel(qgemv_kernel<XT, BITS, MT, true>, p, cu_count, lds, s);
+  return launch_qgemv_kernel(qgemv_kernel<XT, BITS, MT, false>, p, cu_count, lds, s);
 }
 
 template <int XT, int BITS>
@@ -428,7 +447,7 @@ hipError_t launch_qgemv_b(const QParams& p, int cu_count, hipStream_t s) {
   return launch_qgemv_t<XT, BITS, 4>(p, cu_count, s);
 }
 
-// The host has checked: 1 <= M <= 4, LDS need <= 64 KiB, alignment and group divisibility.
+// The host has checked: 1 <= M <= 4, LDS need <= 80 KiB, alignment and group divisibility.
 hipError_t launch_qgemv(const QParams& p, int x_type, int cu_count, hipStream_t s) {
   if (x_type == BF16)
     return p.bits == 4 ? launch_qgemv_b<BF16, 4>(p, cu_count, s) : launch_qgemv_b<BF16, 8>(p, cu_count, s);

@@ -90,6 +90,28 @@ def test_integer_inputs_bit_exact(g, dtype, kernel, ta, tb):
     assert bad.size == 0, f"{bad.shape[0]} mismatches, first at {bad[0]}: got {got[tuple(bad[0])]} want {expect[tuple(bad[0])]}"
 
 
+@pytest.mark.parametrize("dtype,K,ta,tb",
+                         [(d, k, ta, tb) for d in ("f16", "bf16") for k in (1, 40, 64, 100, 128, 150, 192, 264)
+                          for ta, tb in ((False, False), (True, True))] +
+                         [(d, 150, ta, tb) for d in ("f16", "bf16") for ta, tb in ((False, True), (True, False))])
+def test_short_k_256_tile_bit_exact(g, dtype, K, ta, tb):
+    """The 256 x 256 tile over 1 .. 5 K tiles of 64: the K loop's first, second and last tiles
+    take the special cases (tile 1 partly copied ahead, copies past the end of K, a partial
+    last tile rewritten before its barrier).  Integer inputs: exact in any summation order."""
+    M, N = 300, 264
+    seed = zlib.crc32(f"short/{dtype}/{K}/{ta}/{tb}".encode()) & 0xFFFF
+    p = W.make_problem(M, N, K, a_type=dtype, trans_a=ta, trans_b=tb, seed=seed,
+                       dist_a=("int", (-4, 4)), dist_b=("int", (-4, 4)), fp8_scaled=False,
+                       alpha=1.0, beta=-1.0, dist_c=("int", (-8, 8)), epilogue=W.EPI_BIAS)
+    p.bias = np.round(p.bias * 30).astype(np.float32)
+    got, kname, pad_ok = H.run_padded(g, p, kernel=KERNELS["mfma256"])
+    Cref, _ = oracle.gemm(p)
+    expect = oracle.decode(p.c_type, _rne(Cref, p.c_type))
+    bad = np.argwhere(got != expect)
+    assert pad_ok
+    assert bad.size == 0, f"{bad.shape[0]} mismatches, first at {bad[0]}: got {got[tuple(bad[0])]} want {expect[tuple(bad[0])]}"
+
+
 def test_identity_and_permutation_bit_exact(g):
     rng = np.random.default_rng(3)
     n = 320

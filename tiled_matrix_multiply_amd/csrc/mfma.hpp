@@ -169,10 +169,12 @@ struct MmaScaled {
     if constexpr (FP4) return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
     else return __builtin_bit_cast(i32x8, x);
   }
+  // OS: which byte of the scale registers sx and sy the op reads (its op_sel field)
+  template <int OS = 0>
   __device__ static __forceinline__ f32x16 run(const Frag& x, const Frag& y, f32x16 c, int sx,
                                                int sy) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-        widen(x), widen(y), c, f8f6f4_format<XT>(), f8f6f4_format<YT>(), 0, sx, 0, sy);
+        widen(x), widen(y), c, f8f6f4_format<XT>(), f8f6f4_format<YT>(), OS, sx, OS, sy);
   }
 };
 
@@ -607,35 +609,68 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) bf[i][j] = Frag{};
   }
-  // MX: the E8M0 scale byte of each fragment lane's 32-element block, read from the staged
-  // scale rows next to the fragment itself (scA / scB mirror af / bf); 127 (2^0) otherwise.
-  // Blocks past K (the last tile's zero-filled tail) take 2^0 whatever the padding holds.
-  int scA[2][AS] = {}, scB[BS][C::FN] = {};
-  int sclane = lrow * 16 + lhalf;  // this lane's byte within a 16-byte scale row
-  asm volatile("" : "+v"(sclane));
-  auto read_scale = [&](auto opnd, int wbase, int f, int g, int kt) -> int {
+  // MX: the E8M0 scales of a fragment lane for every k-group of a K tile, read once per tile
+  // and fragment (one 8- or 4-byte read of the staged scale row): lane half h's scale for
+  // k-group g is block 2g + h of the tile, held at byte OPS(g) of one register, and the
+  // multiply of k-group g selects that byte with its op_sel field.  scAc / scBc serve the tile
+  // being multiplied; scAn / scBn are read with the next tile's first fragments and take over
+  // at the top of the next iteration.  Blocks past K (the last tile's zero-filled tail) take
+  // 2^0 (code 127) whatever the padding holds.
+  auto OPS = [](int g) { return C::BPT == 8 ? g : 2 * g; };
+  uint32_t scAc[C::FM], scBc[C::FN], scAn[C::FM], scBn[C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) scAc[i] = scAn[i] = 0x7F7F7F7Fu;
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) scBc[j] = scBn[j] = 0x7F7F7F7Fu;
+  int scrow = lrow * 16;  // this lane's 16-byte scale row within a fragment's 32 rows
+  asm volatile("" : "+v"(scrow));
+  auto read_scales = [&](auto opnd, int wbase, int f, int kt, uint32_t fix) -> uint32_t {
     using O = decltype(opnd);
     constexpr int ROW0 = std::is_same<O, OA>::value ? 0 : C::BM;  // A rows, then B rows
-    const int blk = kt * C::BPT + 2 * g;                           // block of lane half 0
-    const uint8_t v = smem[C::SC_OFF + ((kt / C::TPC) & 1) * C::SC_BUF +
-                           (ROW0 + wbase + 32 * f) * 16 + (kt % C::TPC) * C::BPT + 2 * g + sclane];
-    return blk + lhalf < p.kblocks ? (int)v : 127;
+    const uint8_t* row = smem + C::SC_OFF + ((kt / C::TPC) & 1) * C::SC_BUF + (ROW0 + wbase + 32 * f) * 16 +
+                         (kt % C::TPC) * C::BPT + scrow;
+    uint32_t v;
+    if constexpr (C::BPT == 8) {  // blocks 0..7 of the tile: this lane half's four
+      const u32x2 d = *reinterpret_cast<const u32x2*>(row);
+      v = __builtin_amdgcn_perm(d[1], d[0], lhalf ? 0x07050301u : 0x06040200u);
+    } else {                      // blocks 0..3: this lane half's two at bytes 0 and 2
+      v = *reinterpret_cast<const uint32_t*>(row) >> (8 * lhalf);
+    }
+    return (v & ~fix) | (0x7F7F7F7Fu & fix);
   };
-  auto load_a = [&](int kt, uint32_t aoff, int g, int i, Frag& dst, int& sdst) {
-    read_frag(aoff, OA{}, wm * C::WTM, i, g, kbA, mbA, dst);
-    if constexpr (C::MX) sdst = read_scale(OA{}, wm * C::WTM, i, g, kt);
-  };
-  auto load_b = [&](int kt, uint32_t boff, int g, int set) {
+  auto read_tile_scales = [&](int kt) {
+    if constexpr (C::MX) {
+      uint32_t fix = 0;  // bytes of blocks past K
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      read_frag(boff, OB{}, wn * C::WTN, j, g, kbB, mbB, bf[set][j]);
-      if constexpr (C::MX) scB[set][j] = read_scale(OB{}, wn * C::WTN, j, g, kt);
+      for (int g = 0; g < G; ++g)
+        if (kt * C::BPT + 2 * g + lhalf >= p.kblocks) fix |= 0xFFu << (8 * OPS(g));
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) scAn[i] = read_scales(OA{}, wm * C::WTM, i, kt, fix);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) scBn[j] = read_scales(OB{}, wn * C::WTN, j, kt, fix);
     }
   };
+  auto next_tile_scales = [&]() {
+    if constexpr (C::MX) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) scAc[i] = scAn[i];
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) scBc[j] = scBn[j];
+    }
+  };
+  auto load_a = [&](uint32_t aoff, int g, int i, Frag& dst) {
+    read_frag(aoff, OA{}, wm * C::WTM, i, g, kbA, mbA, dst);
+  };
+  auto load_b = [&](uint32_t boff, int g, int set) {
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) read_frag(boff, OB{}, wn * C::WTN, j, g, kbB, mbB, bf[set][j]);
+  };
+  // k-group g of tile kt; with g = 0 also the tile's scales
   auto load_group = [&](int kt, uint32_t aoff, uint32_t boff, int g, int set) {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) load_a(kt, aoff, g, i, af[set][i], scA[set][i]);
-    load_b(kt, boff, g, set);
+    for (int i = 0; i < C::FM; ++i) load_a(aoff, g, i, af[set][i]);
+    load_b(boff, g, set);
+    if (g == 0) read_tile_scales(kt);
   };
   // D = op(B)-fragment x op(A)-fragment: rows of D are n, columns are m, so each lane ends up
   // holding 4 consecutive n of one m (vector stores along the C row).  With the 256 x 256 tile
@@ -645,18 +680,29 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   // schedules are built to save.  Smaller grids keep their accumulators in AccVGPRs, which a
   // VGPR operand constraint would force out and back on every step, so they are not pinned.
   constexpr bool PIN = C::FM * C::FN >= 8;
-  auto mma = [&](int i, const Frag& a, int sa_v, int bset) {
+  // multiplies of A fragment a (row i of the accumulator grid) in k-group g
+  auto mma = [&](int i, const Frag& a, int g, int bset) {
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
-      if constexpr (C::MX) acc[i][j] = Op::run(bf[bset][j], a, acc[i][j], scB[bset][j], sa_v);
-      else if constexpr (C::F8) acc[i][j] = Op::run(bf[bset][j], a, acc[i][j], 127, 127);
-      else acc[i][j] = Op::run(bf[bset][j], a, acc[i][j]);
+      if constexpr (C::MX) {
+        const int sb = (int)scBc[j], sa = (int)scAc[i];
+        switch (OPS(g)) {  // g is a constant once the loops are unrolled
+          case 0: acc[i][j] = Op::template run<0>(bf[bset][j], a, acc[i][j], sb, sa); break;
+          case 1: acc[i][j] = Op::template run<1>(bf[bset][j], a, acc[i][j], sb, sa); break;
+          case 2: acc[i][j] = Op::template run<2>(bf[bset][j], a, acc[i][j], sb, sa); break;
+          default: acc[i][j] = Op::template run<3>(bf[bset][j], a, acc[i][j], sb, sa); break;
+        }
+      } else if constexpr (C::F8) {
+        acc[i][j] = Op::run(bf[bset][j], a, acc[i][j], 127, 127);
+      } else {
+        acc[i][j] = Op::run(bf[bset][j], a, acc[i][j]);
+      }
       if constexpr (PIN) asm volatile("" : "+v"(acc[i][j]));
     }
   };
-  auto mma_group = [&](int set) {
+  auto mma_group = [&](int g) {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) mma(i, af[set][i], scA[set][i], set);
+    for (int i = 0; i < C::FM; ++i) mma(i, af[g & 1][i], g, g & 1);
   };
   constexpr int S = G * C::FM;
   static_assert(G % 2 == 0 && S % 2 == 0, "register-set parities carry across tiles");
@@ -812,6 +858,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   if constexpr (GROUPED) {
     if (KT > 0) load_group(0, 0, 0, 0, 0);
     for (int kt = 0; kt < NI; ++kt) {
+      next_tile_scales();
       const bool work = C::KS == 1 || kt < KT;  // a split group may have one tile fewer
       const uint32_t aoff = abuf * C::A_BYTES, boff = abuf * C::B_BYTES;
       const int anext = abuf + 1 == C::S ? 0 : abuf + 1;
@@ -826,7 +873,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
           // those instantiations)
           if constexpr (C::KS == 1) __builtin_amdgcn_iglp_opt(1);
           load_group(kt, aoff, boff, g + 1, (g + 1) & 1);
-          mma_group(g & 1);
+          mma_group(g);
         }
         if constexpr (C::QB != 0)
           if (kt + 1 < KT) qstore_part(qcur, anext, g);
@@ -843,31 +890,36 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
       tile_boundary(kt, abuf, anext);
       if constexpr (C::QB != 0) qnext = qload(kt + 3);
       if (kt + 1 < KT) load_group(kt + 1, anext * C::A_BYTES, anext * C::B_BYTES, 0, 0);
-      if (work) mma_group((G - 1) & 1);
+      if (work) mma_group(G - 1);
       abuf = anext;
     }
   } else {
     static_assert(C::KS == 1, "K split with the grouped schedule only");
     if (KT > 0) {
-      load_b(0, 0, 0, 0);
-      load_a(0, 0, 0, 0, af[0][0], scA[0][0]);
+      load_b(0, 0, 0);
+      load_a(0, 0, 0, af[0][0]);
+      read_tile_scales(0);
     }
     for (int kt = 0; kt < KT; ++kt) {
+      next_tile_scales();
       const uint32_t aoff = abuf * C::A_BYTES, boff = abuf * C::B_BYTES;
       const int anext = abuf + 1 == C::S ? 0 : abuf + 1;
 #pragma unroll
       for (int st = 0; st < S; ++st) {
         const int g = st / C::FM, i = st % C::FM;
-        if (i == 0 && g > 0) load_b(kt, boff, g, 0);
+        if (i == 0 && g > 0) load_b(boff, g, 0);
         if (st + 1 < S) {
-          load_a(kt, aoff, (st + 1) / C::FM, (st + 1) % C::FM, af[(st + 1) & 1][0], scA[(st + 1) & 1][0]);
-          mma(i, af[st & 1][0], scA[st & 1][0], 0);
+          load_a(aoff, (st + 1) / C::FM, (st + 1) % C::FM, af[(st + 1) & 1][0]);
+          mma(i, af[st & 1][0], g, 0);
         } else {
           tile_boundary(kt, abuf, anext);
-          if (kt + 1 < KT) load_a(kt + 1, anext * C::A_BYTES, 0, 0, af[0][0], scA[0][0]);
-          mma(i, af[st & 1][0], scA[st & 1][0], 0);
+          if (kt + 1 < KT) {
+            load_a(anext * C::A_BYTES, 0, 0, af[0][0]);
+            read_tile_scales(kt + 1);
+          }
+          mma(i, af[st & 1][0], g, 0);
           // the single B set is still read by the last step: refill it only afterwards
-          if (kt + 1 < KT) load_b(kt + 1, anext * C::B_BYTES, 0, 0);
+          if (kt + 1 < KT) load_b(anext * C::B_BYTES, 0, 0);
         }
       }
       abuf = anext;

@@ -612,50 +612,59 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   // MX: the E8M0 scales of a fragment lane for every k-group of a K tile, read once per tile
   // and fragment (one 8- or 4-byte read of the staged scale row): lane half h's scale for
   // k-group g is block 2g + h of the tile, held at byte OPS(g) of one register, and the
-  // multiply of k-group g selects that byte with its op_sel field.  scAc / scBc serve the tile
-  // being multiplied; scAn / scBn are read with the next tile's first fragments and take over
-  // at the top of the next iteration.  Blocks past K (the last tile's zero-filled tail) take
-  // 2^0 (code 127) whatever the padding holds.
+  // multiply of k-group g selects that byte with its op_sel field.  The words read with the
+  // next tile's first fragments (rAn / rBn) are only rearranged into scAc / scBc at the top of
+  // that tile: any arithmetic on them before the current tile's last multiplies would make
+  // those multiplies wait for the reads.  Blocks past K (the last tile's zero-filled tail)
+  // take 2^0 (code 127) whatever the padding holds.
   auto OPS = [](int g) { return C::BPT == 8 ? g : 2 * g; };
-  uint32_t scAc[C::FM], scBc[C::FN], scAn[C::FM], scBn[C::FN];
+  constexpr int RW = C::MX ? C::BPT / 4 : 1;  // words read per fragment and tile
+  uint32_t scAc[C::FM], scBc[C::FN], rAn[C::FM][RW] = {}, rBn[C::FN][RW] = {};
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) scAc[i] = scAn[i] = 0x7F7F7F7Fu;
+  for (int i = 0; i < C::FM; ++i) scAc[i] = 0x7F7F7F7Fu;
 #pragma unroll
-  for (int j = 0; j < C::FN; ++j) scBc[j] = scBn[j] = 0x7F7F7F7Fu;
+  for (int j = 0; j < C::FN; ++j) scBc[j] = 0x7F7F7F7Fu;
   int scrow = lrow * 16;  // this lane's 16-byte scale row within a fragment's 32 rows
   asm volatile("" : "+v"(scrow));
-  auto read_scales = [&](auto opnd, int wbase, int f, int kt, uint32_t fix) -> uint32_t {
+  auto read_scales = [&](auto opnd, int wbase, int f, int kt, uint32_t (&dst)[RW]) {
     using O = decltype(opnd);
     constexpr int ROW0 = std::is_same<O, OA>::value ? 0 : C::BM;  // A rows, then B rows
     const uint8_t* row = smem + C::SC_OFF + ((kt / C::TPC) & 1) * C::SC_BUF + (ROW0 + wbase + 32 * f) * 16 +
                          (kt % C::TPC) * C::BPT + scrow;
-    uint32_t v;
-    if constexpr (C::BPT == 8) {  // blocks 0..7 of the tile: this lane half's four
+    if constexpr (RW == 2) {
       const u32x2 d = *reinterpret_cast<const u32x2*>(row);
-      v = __builtin_amdgcn_perm(d[1], d[0], lhalf ? 0x07050301u : 0x06040200u);
-    } else {                      // blocks 0..3: this lane half's two at bytes 0 and 2
-      v = *reinterpret_cast<const uint32_t*>(row) >> (8 * lhalf);
+      dst[0] = d[0];
+      dst[RW - 1] = d[1];
+    } else {
+      dst[0] = *reinterpret_cast<const uint32_t*>(row);
     }
-    return (v & ~fix) | (0x7F7F7F7Fu & fix);
   };
   auto read_tile_scales = [&](int kt) {
+    if constexpr (C::MX) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) read_scales(OA{}, wm * C::WTM, i, kt, rAn[i]);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) read_scales(OB{}, wn * C::WTN, j, kt, rBn[j]);
+    }
+  };
+  // the scales of tile kt (read by read_tile_scales(kt)) into the registers the multiplies use
+  auto next_tile_scales = [&](int kt) {
     if constexpr (C::MX) {
       uint32_t fix = 0;  // bytes of blocks past K
 #pragma unroll
       for (int g = 0; g < G; ++g)
         if (kt * C::BPT + 2 * g + lhalf >= p.kblocks) fix |= 0xFFu << (8 * OPS(g));
+      auto pack = [&](const uint32_t (&w)[RW]) {
+        // 8 blocks: this lane half's four (bytes h, 2+h, 4+h, 6+h); 4 blocks: its two, to
+        // bytes 0 and 2
+        const uint32_t v = RW == 2 ? __builtin_amdgcn_perm(w[RW - 1], w[0], lhalf ? 0x07050301u : 0x06040200u)
+                                   : w[0] >> (8 * lhalf);
+        return (v & ~fix) | (0x7F7F7F7Fu & fix);
+      };
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) scAn[i] = read_scales(OA{}, wm * C::WTM, i, kt, fix);
+      for (int i = 0; i < C::FM; ++i) scAc[i] = pack(rAn[i]);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) scBn[j] = read_scales(OB{}, wn * C::WTN, j, kt, fix);
-    }
-  };
-  auto next_tile_scales = [&]() {
-    if constexpr (C::MX) {
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) scAc[i] = scAn[i];
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) scBc[j] = scBn[j];
+      for (int j = 0; j < C::FN; ++j) scBc[j] = pack(rBn[j]);
     }
   };
   auto load_a = [&](uint32_t aoff, int g, int i, Frag& dst) {
@@ -858,7 +867,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   if constexpr (GROUPED) {
     if (KT > 0) load_group(0, 0, 0, 0, 0);
     for (int kt = 0; kt < NI; ++kt) {
-      next_tile_scales();
+      next_tile_scales(kt);
       const bool work = C::KS == 1 || kt < KT;  // a split group may have one tile fewer
       const uint32_t aoff = abuf * C::A_BYTES, boff = abuf * C::B_BYTES;
       const int anext = abuf + 1 == C::S ? 0 : abuf + 1;
@@ -901,7 +910,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
       read_tile_scales(0);
     }
     for (int kt = 0; kt < KT; ++kt) {
-      next_tile_scales();
+      next_tile_scales(kt);
       const uint32_t aoff = abuf * C::A_BYTES, boff = abuf * C::B_BYTES;
       const int anext = abuf + 1 == C::S ? 0 : abuf + 1;
 #pragma unroll

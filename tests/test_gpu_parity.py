@@ -190,6 +190,45 @@ def test_bf16_bias_gelu_unfused(g, n):
     assert res.ok
 
 
+@pytest.mark.parametrize("c_type", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("M,N,ldc", [(37, 24, 24), (37, 24, 40), (5, 13, 13), (1, 8, 8),
+                                     (300001, 8, 8), (9, 2056, 2056)])
+@pytest.mark.parametrize("epi", [W.EPI_BIAS | W.EPI_GELU, W.EPI_GELU, W.EPI_BIAS])
+def test_unfused_bias_gelu_pass(g, c_type, M, N, ldc, epi):
+    """The separate elementwise pass on its own: C = GELU(C + bias) in place, on vector-path
+    shapes (N and ldc multiples of 8, rows past the 65535 x 4 the launch covers in one pass)
+    and scalar-path shapes, against the oracle's erf-GELU of the same stored values.  One
+    rounding to the output type (relative, or half a step among subnormals); the approximation
+    adds at most 1e-6 of |x + b|.  The padding
+    of a row (ldc > N) must come back untouched."""
+    import torch
+    rng = np.random.default_rng(M * 7 + N * 3 + ldc + epi)
+    x = rng.normal(0.0, 3.0, size=(M, ldc))
+    stored = W.encode(x, c_type)
+    bias = rng.normal(0.0, 0.5, size=N).astype(np.float32)
+    Cd, bd = H.to_device(stored), H.to_device(bias)
+    g.bias_gelu(Cd, bd, M=M, N=N, ldc=ldc, c_type=c_type, epilogue=epi)
+    torch.cuda.synchronize()
+    raw = H.from_device(Cd, c_type)
+    assert np.array_equal(raw[:, N:], stored[:, N:])
+    got = oracle.decode(c_type, raw[:, :N])
+    xin = oracle.decode(c_type, stored[:, :N])
+    t = xin + (bias.astype(np.float64) if epi & W.EPI_BIAS else 0.0)
+    if epi & W.EPI_GELU:
+        from scipy.special import erfc
+        want = 0.5 * t * erfc(-t / np.sqrt(2.0))  # x Phi(x), vectorised
+        few = t.ravel()[:64]
+        assert np.allclose([oracle.gelu(v) for v in few], want.ravel()[:64], rtol=1e-14, atol=0)
+    else:
+        want = t
+    u = {"f32": 2.0 ** -23, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[c_type]
+    sub = {"f32": 2.0 ** -150, "f16": 2.0 ** -25, "bf16": 2.0 ** -134}[c_type]  # half a subnormal step
+    tol = u * np.abs(want) + 1e-6 * np.abs(t) + sub
+    err = np.abs(got - want)
+    bad = ~(err <= tol)
+    assert not bad.any(), f"{bad.sum()} elements, first at {np.argwhere(bad)[0]}: got {got[bad][0]} want {want[bad][0]}"
+
+
 @pytest.mark.parametrize("n", [512, 4096])
 def test_fp8_e4m3(g, n):
     p = W.fp8_4096(n)

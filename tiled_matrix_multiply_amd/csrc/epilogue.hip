@@ -6,48 +6,75 @@
 
 namespace tgemm {
 
-// Vector path: each thread handles 8 consecutive elements of one row (16 bytes of a 16-bit C,
-// 32 bytes of fp32 C); requires N % 8 == 0, ldc % 8 == 0 and a 16-byte-aligned C.
-template <int CT>
+// Vector path: a workgroup is TX x (256 / TX) threads.  Thread (x, y) of workgroup (bx, by)
+// owns the 8 consecutive elements of column chunk c = TX bx + x (16 bytes of a 16-bit C, 32 of
+// fp32 C) in the R rows R (by (256 / TX) + y) ..  + R-1, then the rows gridDim.y (256 / TX) R
+// further on.  Its R loads are issued before any GELU, so each thread keeps R reads in flight,
+// and no index is divided.  The chunk's bias values are read once.  Requires N % 8 == 0,
+// ldc % 8 == 0 and a 16-byte-aligned C.
+// For 16-bit outputs with GELU the elementwise work is the fused epilogue's: y = (x + b) / 2
+// (one fma with the bias halved; halving is exact) and gelu_as7128_half(y).
+template <int CT, int R>
 __global__ __launch_bounds__(256) void bias_gelu_vec_kernel(void* C, int64_t ldc, int M, int N,
-                                                            const float* bias, uint32_t epi) {
-  const int per_row = N / 8;
-  const int64_t total = (int64_t)M * per_row;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    const int m = (int)(t / per_row), n = (int)(t % per_row) * 8;
-    const int64_t idx = (int64_t)m * ldc + n;
-    float v[8];
-    if constexpr (CT == F32) {
-      const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(C) + idx);
-      const float4 a = src[0], b = src[1];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-      const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(C) + idx);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+                                                            const float* bias, uint32_t epi, int TX) {
+  const int ty = threadIdx.x / TX, tx = threadIdx.x % TX, TY = 256 / TX;
+  const int c = blockIdx.x * TX + tx;
+  if (c >= N / 8) return;
+  const int n = 8 * c;
+  const bool half = CT != F32 && (epi & EPI_GELU);
+  const float hs = half ? 0.5f : 1.0f;
+  float bj[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t h = (ws[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-        v[e] = (CT == F16) ? f16_bits_to_float(h) : bf16_bits_to_float(h);
+  for (int e = 0; e < 8; ++e) bj[e] = (epi & EPI_BIAS) ? hs * bias[n + e] : 0.0f;
+  typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+  for (int64_t m0 = ((int64_t)blockIdx.y * TY + ty) * R; m0 < M; m0 += (int64_t)gridDim.y * TY * R) {
+    u32x8 w[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (m0 + r >= M) break;
+      const int64_t idx = (m0 + r) * ldc + n;
+      if constexpr (CT == F32) {
+        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(C) + idx);
+        const uint4 a = src[0], b = src[1];
+        w[r] = u32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      } else {
+        const uint4 h = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(C) + idx);
+        w[r] = u32x8{h.x, h.y, h.z, h.w, 0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = v[e];
-      if (epi & EPI_BIAS) x += bias[n + e];
-      if (epi & EPI_GELU) x = gelu_out<CT>(x);
-      v[e] = x;
-    }
-    if constexpr (CT == F32) {
-      float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(C) + idx);
-      dst[0] = float4{v[0], v[1], v[2], v[3]};
-      dst[1] = float4{v[4], v[5], v[6], v[7]};
-    } else {
-      uint32_t h[8];
+    for (int r = 0; r < R; ++r) {
+      if (m0 + r >= M) break;
+      const int64_t idx = (m0 + r) * ldc + n;
+      float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = (CT == F16) ? float_to_f16_bits(v[e]) : float_to_bf16_bits(v[e]);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(C) + idx) =
-          uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      for (int e = 0; e < 8; ++e) {
+        float x;
+        if constexpr (CT == F32) {
+          x = __uint_as_float(w[r][e]);
+        } else {
+          const uint32_t h = (w[r][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+          x = (CT == F16) ? f16_bits_to_float(h) : bf16_bits_to_float(h);
+        }
+        if (half) {
+          v[e] = gelu_as7128_half(fmaf(0.5f, x, bj[e]));
+        } else {
+          x += bj[e];
+          if (epi & EPI_GELU) x = gelu_out<CT>(x);
+          v[e] = x;
+        }
+      }
+      if constexpr (CT == F32) {
+        float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(C) + idx);
+        dst[0] = float4{v[0], v[1], v[2], v[3]};
+        dst[1] = float4{v[4], v[5], v[6], v[7]};
+      } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (CT == F16) ? float_to_f16_bits(v[e]) : float_to_bf16_bits(v[e]);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(C) + idx) =
+            uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      }
     }
   }
 }
@@ -71,14 +98,31 @@ __global__ __launch_bounds__(256) void bias_gelu_scalar_kernel(void* C, int64_t 
 template <int CT>
 static hipError_t launch_ct(void* C, int64_t ldc, int M, int N, const float* bias, uint32_t epi,
                             bool vec, int cu_count, hipStream_t s) {
-  const int64_t items = vec ? (int64_t)M * (N / 8) : (int64_t)M * N;
-  const int64_t want = (items + 255) / 256;
-  const int64_t cap = (int64_t)cu_count * 16;  // enough resident waves to saturate HBM
-  const unsigned grid = (unsigned)(want < cap ? (want > 0 ? want : 1) : cap);
-  if (vec)
-    hipLaunchKernelGGL((bias_gelu_vec_kernel<CT>), dim3(grid), dim3(256), 0, s, C, ldc, M, N, bias, epi);
-  else
+  if (vec) {
+    // TX threads across the row's chunks (a power of two from 64 to 256), 256 / TX rows; R rows
+    // per thread once the problem has more than 2048 chunks per compute unit (a full
+    // complement of resident threads), else one: small passes want every chunk in its own
+    // thread, large ones several loads in flight per thread.
+    const int chunks = N / 8;
+    int tx = 64;
+    while (tx < 256 && tx < chunks) tx *= 2;
+    const int64_t items = (int64_t)M * chunks, full = (int64_t)cu_count * 2048;
+    const int r = items >= 4 * full ? 4 : items >= 2 * full ? 2 : 1;
+    const unsigned gx = (unsigned)((chunks + tx - 1) / tx);
+    const int64_t gy = ((int64_t)M + (int64_t)(256 / tx) * r - 1) / ((int64_t)(256 / tx) * r);
+    const dim3 grid(gx, (unsigned)(gy < 65535 ? gy : 65535));
+    if (r == 4)
+      hipLaunchKernelGGL((bias_gelu_vec_kernel<CT, 4>), grid, dim3(256), 0, s, C, ldc, M, N, bias, epi, tx);
+    else if (r == 2)
+      hipLaunchKernelGGL((bias_gelu_vec_kernel<CT, 2>), grid, dim3(256), 0, s, C, ldc, M, N, bias, epi, tx);
+    else
+      hipLaunchKernelGGL((bias_gelu_vec_kernel<CT, 1>), grid, dim3(256), 0, s, C, ldc, M, N, bias, epi, tx);
+  } else {
+    const int64_t want = ((int64_t)M * N + 255) / 256;
+    const int64_t cap = (int64_t)cu_count * 16;  // enough resident waves to saturate HBM
+    const unsigned grid = (unsigned)(want < cap ? (want > 0 ? want : 1) : cap);
     hipLaunchKernelGGL((bias_gelu_scalar_kernel<CT>), dim3(grid), dim3(256), 0, s, C, ldc, M, N, bias, epi);
+  }
   return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@ bf16 at 4096^3.  Each cell: warm up for >= 200 ms, then R timed reps with one HI
 per rep on the stream the kernel runs on; median and a percentile-bootstrap 95% CI
 (10^4 resamples, seed 0), as "Rigel" (arXiv 2606.12765), section 3 reports its cells.
 
-Prints ONE JSON line.  Only --gpus 1 is supported: this build runs on a single GPU.
+Prints ONE JSON line.  Only --gpus 1 is supported: the library runs on a single GPU.
 """
 from __future__ import annotations
 
@@ -400,7 +400,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: --gpus {args.gpus} (WORLD_SIZE={world}) requested, but this build is a "
+        print(f"bench.py: --gpus {args.gpus} (WORLD_SIZE={world}) requested, but the library is a "
               f"single-GPU GEMM: there is no sharded path and no collective. Run --gpus 1.",
               file=sys.stderr)
         sys.exit(2)

@@ -1,6 +1,6 @@
 """Builds oracle/liboracle.so (plain C, float64, OpenMP) with gcc.
 
-The oracle is test infrastructure: this script only compiles the checker.
+The oracle is test infrastructure: this script only compiles it.
 """
 import os
 import subprocess

@@ -110,12 +110,13 @@ class Cell:
         bias_gelu = tmm.library().gemm_bias_gelu
         post = (h, s, p.M, p.N, self.C.data_ptr(), p.ldc, dt[p.c_type], args[-1], p.epilogue)
 
-        def step():
-            st = run(h, s, *args)
+        def step(stream=None):
+            sh = s if stream is None else stream
+            st = run(h, sh, *args)
             if st != 0:
                 raise RuntimeError(f"gemm_run: {tmm.gemm_status_string(st)}")
             if unfused:
-                st = bias_gelu(*post)
+                st = bias_gelu(h, sh, *post[2:])
                 if st != 0:
                     raise RuntimeError(f"gemm_bias_gelu: {tmm.gemm_status_string(st)}")
         self.step = step
@@ -205,8 +206,9 @@ class QCell:
                       xt, q.epilogue, bptr) for w in self.W]
         self.i = 0
 
-        def step():
-            st = run(*self.args[self.i])
+        def step(stream=None):
+            a = self.args[self.i]
+            st = run(a[0], a[1] if stream is None else stream, *a[2:])
             self.i = (self.i + 1) % len(self.args)
             if st != 0:
                 raise RuntimeError(f"gemm_run_q: {tmm.gemm_status_string(st)}")
@@ -286,6 +288,41 @@ def recipe_hash(recipe: dict) -> str:
     """Hash of a workload's input recipe (sizes, types, distributions, seed, RNG, draw order)."""
     blob = json.dumps(recipe, sort_keys=True, default=str).encode()
     return hashlib.sha256(blob).hexdigest()[:16]
+
+
+def graph_time(cell, per_graph: int = 20, replays: int = 20):
+    """Per-step period (ms) with `per_graph` steps captured in one HIP graph and replayed
+    `replays` times between one event pair: the GPU's own launch-to-launch period, without the
+    host's per-call cost, which bounds the back-to-back loop of the small cells.  None if the
+    capture fails (the timed results stand without it)."""
+    import torch
+    try:
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # a launch off the default stream before capture
+            cell.step(side.cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cs = torch.cuda.current_stream().cuda_stream
+            for _ in range(per_graph):
+                cell.step(cs)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (replays * per_graph)
+        del graph
+        return ms
+    except RuntimeError as e:
+        print(f"[bench] graph timing unavailable: {e}", file=sys.stderr, flush=True)
+        return None
 
 
 def summarize(name, cell: Cell, ms: np.ndarray, dtype: str) -> dict:
@@ -474,6 +511,11 @@ def main():
         for name, dtype, make in sweep_cells():
             c = make(g)
             row = summarize(name, c, c.time(args.reps), dtype)
+            gms = graph_time(c)
+            row["graph_us"] = round(gms * 1e3, 3) if gms is not None else None
+            if gms is not None:
+                print(f"[bench] {'':34s} {row['graph_us']:.2f} us per step in a HIP graph",
+                      file=sys.stderr, flush=True)
             if isinstance(c, QCell) and c.p.M <= 4:
                 row["pct_hbm"] = round(100 * row["gbs"] / PEAK_HBM_GBS, 2)
                 print(f"[bench] {'':34s} {row['pct_hbm']:.1f}% of HBM peak "

@@ -106,8 +106,12 @@ typedef enum gemm_kernel {
   GEMM_KERNEL_MFMA_256 = 4, /* matrix-core kernel, 256x256 workgroup tile, 8 wavefronts */
   GEMM_KERNEL_QGEMV = 5,    /* gemm_run_q only: matrix-vector kernel for a few activation rows,
                                bound by the bandwidth of the weight codes */
-  GEMM_KERNEL_QMFMA = 6     /* gemm_run_q only: matrix-core kernel that dequantises the codes
+  GEMM_KERNEL_QMFMA = 6,    /* gemm_run_q only: matrix-core kernel that dequantises the codes
                                in registers (prefill) */
+  GEMM_KERNEL_MFMA_32 = 7   /* matrix-core kernel, 32x32 workgroup tile, 4 wavefronts that
+                               split the K loop four ways; fp32, fp16 and bf16 only (other
+                               types return GEMM_ERR_UNSUPPORTED).  AUTO takes it when 64x64
+                               tiles would leave three quarters of the compute units idle */
 } gemm_kernel_t;
 
 typedef struct gemm_handle* gemm_handle_t;

@@ -19,7 +19,8 @@ import gemm_harness as H
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = {"simt": 1, "mfma64": 2, "mfma128": 3, "mfma256": 4}
+KERNELS = {"simt": 1, "mfma64": 2, "mfma128": 3, "mfma256": 4, "mfma32": 7}
+WIDE = ("f32", "f16", "bf16")  # the types the 32 x 32 kernel takes
 
 
 @pytest.fixture(scope="module")
@@ -67,8 +68,9 @@ def _rne(x: np.ndarray, c_type: str) -> np.ndarray:
 
 
 @pytest.mark.parametrize("dtype,kernel,ta,tb",
-                         list(itertools.product(["f32", "f16", "bf16", "e4m3"], KERNELS,
-                                                [False, True], [False, True])))
+                         [c for c in itertools.product(["f32", "f16", "bf16", "e4m3"], KERNELS,
+                                                       [False, True], [False, True])
+                          if c[1] != "mfma32" or c[0] in WIDE])
 def test_integer_inputs_bit_exact(g, dtype, kernel, ta, tb):
     """Integer inputs in [-4, 4]: every partial sum is an integer below 2^24, so any fp32
     accumulation order is exact and the result must equal the exact value rounded once."""
@@ -110,6 +112,14 @@ def test_short_k_256_tile_bit_exact(g, dtype, K, ta, tb):
     bad = np.argwhere(got != expect)
     assert pad_ok
     assert bad.size == 0, f"{bad.shape[0]} mismatches, first at {bad[0]}: got {got[tuple(bad[0])]} want {expect[tuple(bad[0])]}"
+
+
+def test_mfma32_refuses_8_bit_inputs(g):
+    import tiled_matrix_multiply_amd as tmm
+    p = W.make_problem(64, 64, 128, a_type="e4m3", seed=5)
+    with pytest.raises(tmm.GemmError) as e:
+        H.run(g, p, KERNELS["mfma32"])
+    assert e.value.status == tmm.GEMM_ERR_UNSUPPORTED
 
 
 def test_identity_and_permutation_bit_exact(g):
@@ -251,6 +261,10 @@ def test_kernel_selection(g):
     assert g.select_kernel(4096, 4096, 4096, a_type="bf16", **ptrs) == "mfma256"
     assert g.select_kernel(2048, 2048, 2048, a_type="bf16", **ptrs) == "mfma128"
     assert g.select_kernel(1024, 1024, 1024, a_type="f16", **ptrs) == "mfma64"
+    # 64 x 64 tiles would fill a quarter of the compute units or less: 32 x 32, K split 4 ways
+    assert g.select_kernel(512, 512, 512, a_type="bf16", **ptrs) == "mfma32"
+    assert g.select_kernel(256, 256, 256, a_type="f32", **ptrs) == "mfma32"
+    assert g.select_kernel(512, 512, 512, a_type="e4m3", **ptrs) == "mfma64"
     assert g.select_kernel(1000, 1000, 1000, a_type="f32", **ptrs) == "mfma64"
     assert g.select_kernel(1000, 1000, 1000, a_type="f32", A=(1 << 40) + 4, B=2 << 40,
                            C=3 << 40) == "simt"
@@ -262,8 +276,10 @@ SHAPES = [(1, 1, 1), (31, 33, 17), (64, 64, 64), (65, 63, 129), (257, 255, 1), (
           (1000, 777, 333), (130, 1030, 40)]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "e4m3"])
-@pytest.mark.parametrize("kernel", ["auto", "simt", "mfma64", "mfma128", "mfma256"])
+@pytest.mark.parametrize("dtype,kernel",
+                         [(d, k) for d in ("f32", "f16", "bf16", "e4m3")
+                          for k in ("auto", "simt", "mfma64", "mfma128", "mfma256", "mfma32")
+                          if k != "mfma32" or d in WIDE])
 def test_edge_shapes(g, dtype, kernel):
     """Ragged shapes with leading dimensions padded to 16-byte multiples (padding poisoned
     with NaN): every kernel family must mask its loads and stores at every edge."""

@@ -44,8 +44,9 @@ GEMM_KERNEL_MFMA_128 = 3
 GEMM_KERNEL_MFMA_256 = 4
 GEMM_KERNEL_QGEMV = 5
 GEMM_KERNEL_QMFMA = 6
+GEMM_KERNEL_MFMA_32 = 7
 KERNEL_NAME = {0: "auto", 1: "simt", 2: "mfma64", 3: "mfma128", 4: "mfma256", 5: "qgemv",
-               6: "qmfma"}
+               6: "qmfma", 7: "mfma32"}
 
 # Every symbol include/gemm.h declares.
 EXPORTS = ("gemm_create", "gemm_destroy", "gemm_check_args", "gemm_run", "gemm_run_kernel",

@@ -198,6 +198,10 @@ int k_split(const Args& a, int cu_count) {
 // Largest tile that still gives every compute unit at least one workgroup.
 gemm_kernel_t auto_kernel(const Args& a, int cu_count) {
   if (!mfma_aligned(a)) return GEMM_KERNEL_SIMT;
+  // 64 x 64 tiles would leave three quarters of the compute units idle: 32 x 32 tiles with the
+  // K loop split four ways (16- and 32-bit inputs)
+  if ((a.at == GEMM_F32 || a.at == GEMM_F16 || a.at == GEMM_BF16) && 4 * tiles(a.M, a.N, 64) <= cu_count)
+    return GEMM_KERNEL_MFMA_32;
   if (tiles(a.M, a.N, 256) >= cu_count) return GEMM_KERNEL_MFMA_256;
   if (tiles(a.M, a.N, 128) >= cu_count) return GEMM_KERNEL_MFMA_128;
   return GEMM_KERNEL_MFMA_64;
@@ -331,10 +335,13 @@ gemm_status_t run_impl(gemm_handle_t h, gemm_kernel_t kernel, void* stream, cons
     p.tiles_n = (int)((a.N + 15) / 16);
     DeviceGuard g(h->device);
     err = tgemm::launch_simt(p, a.at, a.bt, a.transA, a.transB, s);
-  } else if (kernel >= GEMM_KERNEL_MFMA_64 && kernel <= GEMM_KERNEL_MFMA_256) {
+  } else if ((kernel >= GEMM_KERNEL_MFMA_64 && kernel <= GEMM_KERNEL_MFMA_256) ||
+             kernel == GEMM_KERNEL_MFMA_32) {
     if (!mfma_aligned(a)) return GEMM_ERR_UNSUPPORTED;
-    const int tile = kernel - GEMM_KERNEL_MFMA_64;
-    const int t = 64 << tile;
+    if (kernel == GEMM_KERNEL_MFMA_32 && a.at != GEMM_F32 && a.at != GEMM_F16 && a.at != GEMM_BF16)
+      return GEMM_ERR_UNSUPPORTED;
+    const int tile = kernel == GEMM_KERNEL_MFMA_32 ? 3 : kernel - GEMM_KERNEL_MFMA_64;
+    const int t = kernel == GEMM_KERNEL_MFMA_32 ? 32 : 64 << tile;
     const int64_t tm = (a.M + t - 1) / t, tn = (a.N + t - 1) / t;
     if (tm * tn > kMaxDim) return GEMM_ERR_UNSUPPORTED;
     p.tiles_m = (int)tm;

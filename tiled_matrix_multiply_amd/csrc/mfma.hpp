@@ -268,7 +268,7 @@ struct Operand {
   __device__ static __forceinline__ int kswz(int r) { return (r ^ (r >> 3)) & 7; }
   __device__ static __forceinline__ int mswz(int k) {
     if constexpr (ES == 4) return 0;  // 32 lanes read one k-row: never conflicts
-    else if constexpr (ES == 2) return (k & 3) << (CPR >= 16 ? 2 : 1);
+    else if constexpr (ES == 2) return CPR >= 16 ? (k & 3) << 2 : CPR >= 8 ? (k & 3) << 1 : 0;
     else if constexpr (CPR >= 16) return (k & 7) << 1;
     else if constexpr (CPR == 8) return k & 7;
     else return (k >> 1) & 3;
@@ -1140,6 +1140,12 @@ hipError_t launch_mfma_dtype(const GemmParams& p, int tile, bool a_mn, bool b_mn
                              int ks = 1) {
   if constexpr (DT == F32 || DT == F16 || DT == BF16) {
     if (tile == 0 && ks == 2) return launch_mfma_layout<DT, 64, 2, 2, BT, MX, 2>(p, a_mn, b_mn, s);
+  }
+  if (tile == 3) {  // 32 x 32, one wave per K group, four groups (small products)
+    if constexpr ((DT == F32 || DT == F16 || DT == BF16) && !MX)
+      return launch_mfma_layout<DT, 32, 1, 1, BT, MX, 4>(p, a_mn, b_mn, s);
+    else
+      return hipErrorInvalidValue;
   }
   if (ks != 1) return hipErrorInvalidValue;
   switch (tile) {

@@ -184,9 +184,11 @@ constexpr bool is_f8f6f4() { return DT == E4M3 || DT == E5M2 || DT == E2M1 || is
 // ----------------------------------------------------------------------- configuration --
 
 // LDS stages (K tiles resident or in flight per operand) by tile size, from a sweep over
-// n = 512 .. 2048 (fp16, random operands): the 128 x 128 tile gains 12% at 2048 from a third
-// stage (its four waves cannot hide one copy's latency); the 64 x 64 tile loses from any more
-// (fewer workgroups fit a compute unit); the 256 x 256 tile fills 128 of the 160 KB with two.
+// n = 512 .. 2048 (fp16, random operands): the 128 x 128 tile with one group of four waves
+// gains 12% at 2048 from a third stage (its four waves cannot hide one copy's latency; the 16-
+// and 32-bit types now split its K loop between two groups of two stages instead, which is
+// faster still); the 64 x 64 tile loses from any more (fewer workgroups fit a compute unit);
+// the 256 x 256 tile fills 128 of the 160 KB with two.
 template <int TILE>
 constexpr int default_stages() { return TILE == 128 ? 3 : 2; }
 
@@ -1115,14 +1117,16 @@ hipError_t launch_mfma_cfg(GemmParams p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile families: 0 -> 64x64 (2x2 waves of 32x32), 1 -> 128x128 (2x2 waves of 64x64),
-// 2 -> 256x256 (2x4 waves of 128x64).  BT: type of B (differs from A only in the 8-bit
+// Tile families: 0 -> 64x64 (2x2 waves of 32x32), 1 -> 128x128 (2x2 waves of 64x64; two such
+// groups splitting K for 16- and 32-bit inputs), 2 -> 256x256 (2x4 waves of 128x64), 3 -> 32x32
+// (four one-wave groups splitting K; 16- and 32-bit inputs).  BT: type of B (differs from A only in the 8-bit
 // family); MX: block-scaled.  Packed fp4 and 6-bit operands are staged K-contiguous only (A
 // stored M x K, B stored N x K): the other layouts return an error (the host never routes them
 // here).
 template <int DT, int TILE, int WM, int WN, int BT, bool MX, int KS = 1>
 hipError_t launch_mfma_layout(const GemmParams& p, bool a_mn, bool b_mn, hipStream_t s) {
-  constexpr int S = default_stages<TILE>();
+  // a K split gives each group its own stages: two each
+  constexpr int S = KS > 1 ? 2 : default_stages<TILE>();
   if (!a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, false, S, BT, MX, 0, KS>>(p, s);
   if constexpr (DT == E2M1 || is_fp6<DT>()) {
     return hipErrorInvalidValue;
@@ -1150,7 +1154,13 @@ hipError_t launch_mfma_dtype(const GemmParams& p, int tile, bool a_mn, bool b_mn
   if (ks != 1) return hipErrorInvalidValue;
   switch (tile) {
     case 0: return launch_mfma_layout<DT, 64, 2, 2, BT, MX>(p, a_mn, b_mn, s);
-    case 1: return launch_mfma_layout<DT, 128, 2, 2, BT, MX>(p, a_mn, b_mn, s);
+    case 1:
+      // 16- and 32-bit inputs: two groups of four waves split the K loop (two waves per SIMD,
+      // so that one covers the other's waits)
+      if constexpr ((DT == F32 || DT == F16 || DT == BF16) && !MX)
+        return launch_mfma_layout<DT, 128, 2, 2, BT, MX, 2>(p, a_mn, b_mn, s);
+      else
+        return launch_mfma_layout<DT, 128, 2, 2, BT, MX>(p, a_mn, b_mn, s);
     case 2: return launch_mfma_layout<DT, 256, 2, 4, BT, MX>(p, a_mn, b_mn, s);
     default: return hipErrorInvalidValue;
   }

@@ -260,6 +260,9 @@ def test_kernel_selection(g):
     ptrs = dict(A=1 << 40, B=2 << 40, C=3 << 40)   # aligned, disjoint; never dereferenced
     assert g.select_kernel(4096, 4096, 4096, a_type="bf16", **ptrs) == "mfma256"
     assert g.select_kernel(2048, 2048, 2048, a_type="bf16", **ptrs) == "mfma128"
+    # beyond two rounds of 128 x 128 workgroups the 256 x 256 tile is faster
+    assert g.select_kernel(2816, 2816, 2816, a_type="bf16", **ptrs) == "mfma128"
+    assert g.select_kernel(3072, 3072, 3072, a_type="bf16", **ptrs) == "mfma256"
     assert g.select_kernel(1024, 1024, 1024, a_type="f16", **ptrs) == "mfma64"
     # 64 x 64 tiles would fill a quarter of the compute units or less: 32 x 32, K split 4 ways
     assert g.select_kernel(512, 512, 512, a_type="bf16", **ptrs) == "mfma32"

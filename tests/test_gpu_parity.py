@@ -264,6 +264,8 @@ def test_kernel_selection(g):
     assert g.select_kernel(2816, 2816, 2816, a_type="bf16", **ptrs) == "mfma128"
     assert g.select_kernel(3072, 3072, 3072, a_type="bf16", **ptrs) == "mfma256"
     assert g.select_kernel(1024, 1024, 1024, a_type="f16", **ptrs) == "mfma64"
+    assert g.select_kernel(1792, 1792, 1792, a_type="bf16", **ptrs) == "mfma128"
+    assert g.select_kernel(1280, 1280, 1280, a_type="bf16", **ptrs) == "mfma64"
     # 64 x 64 tiles would fill a quarter of the compute units or less: 32 x 32, K split 4 ways
     assert g.select_kernel(512, 512, 512, a_type="bf16", **ptrs) == "mfma32"
     assert g.select_kernel(256, 256, 256, a_type="f32", **ptrs) == "mfma32"

@@ -207,7 +207,10 @@ gemm_kernel_t auto_kernel(const Args& a, int cu_count) {
   // 256 x 256 ones (bf16 + bias + GELU: 3072^3 80 vs 98 us, 3584^3 101 vs 146 us; at two
   // rounds or fewer the 128 tile wins, 2816^3 65 vs 73 us, 4096 x 2048 x 4096 85 vs 99 us).
   if (tiles(a.M, a.N, 128) > 2 * (int64_t)cu_count) return GEMM_KERNEL_MFMA_256;
-  if (tiles(a.M, a.N, 128) >= cu_count) return GEMM_KERNEL_MFMA_128;
+  // The 128 tile (its K loop split between two wave groups for 16- and 32-bit types) also
+  // beats 64 x 64 tiles with some compute units idle, from about 9/16 of them busy: 1792^3
+  // 25.0 vs 28.8 us, 1536 x 1536 x 4096 42.2 vs 47.8 us; below, 1280^3 18.3 vs 14.9 us.
+  if (16 * tiles(a.M, a.N, 128) >= 9 * (int64_t)cu_count) return GEMM_KERNEL_MFMA_128;
   return GEMM_KERNEL_MFMA_64;
 }
 

@@ -256,6 +256,17 @@ def test_bf16_twin_4096(g):
     assert res.ok
 
 
+@pytest.mark.parametrize("M,N,K", [(1280, 1280, 1280), (1024, 2048, 2048)])
+def test_k_split_beyond_one_round(g, M, N, K):
+    """The 64 x 64 tile with its K loop split, on more tiles than compute units."""
+    p = W.make_problem(M, N, K, a_type="bf16", seed=17, dist_a=("normal", 1.0),
+                       dist_b=("normal", 1.0 / np.sqrt(K)), epilogue=W.EPI_BIAS | W.EPI_GELU)
+    _, got = H.run(g, p)
+    res = H.gate_sampled(p, got)
+    _report(f"bf16+bias+GELU {M}x{N}x{K} (64 tile, K split)", res)
+    assert res.ok
+
+
 def test_kernel_selection(g):
     ptrs = dict(A=1 << 40, B=2 << 40, C=3 << 40)   # aligned, disjoint; never dereferenced
     assert g.select_kernel(4096, 4096, 4096, a_type="bf16", **ptrs) == "mfma256"

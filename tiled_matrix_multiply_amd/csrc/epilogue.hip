@@ -99,15 +99,15 @@ template <int CT>
 static hipError_t launch_ct(void* C, int64_t ldc, int M, int N, const float* bias, uint32_t epi,
                             bool vec, int cu_count, hipStream_t s) {
   if (vec) {
-    // TX threads across the row's chunks (a power of two from 64 to 256), 256 / TX rows; R rows
-    // per thread once the problem has more than 2048 chunks per compute unit (a full
-    // complement of resident threads), else one: small passes want every chunk in its own
-    // thread, large ones several loads in flight per thread.
+    // TX threads across the row's chunks (a power of two from 64 to 256), 256 / TX rows; R = 4
+    // rows per thread once the pass has 2048 chunks per compute unit (a full complement of
+    // resident threads), 2 from half that, else one: small passes want every chunk in its own
+    // thread, large ones several loads in flight per thread (bf16 2048^2: 9 -> 6 us with 4).
     const int chunks = N / 8;
     int tx = 64;
     while (tx < 256 && tx < chunks) tx *= 2;
     const int64_t items = (int64_t)M * chunks, full = (int64_t)cu_count * 2048;
-    const int r = items >= 4 * full ? 4 : items >= 2 * full ? 2 : 1;
+    const int r = items >= full ? 4 : items >= full / 2 ? 2 : 1;
     const unsigned gx = (unsigned)((chunks + tx - 1) / tx);
     const int64_t gy = ((int64_t)M + (int64_t)(256 / tx) * r - 1) / ((int64_t)(256 / tx) * r);
     const dim3 grid(gx, (unsigned)(gy < 65535 ? gy : 65535));

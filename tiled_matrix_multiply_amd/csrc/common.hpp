@@ -181,69 +181,52 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * erfcf(x * -0.70710678118654752f);
 }
 
-// GELU for 16-bit outputs, x Phi(x) with the error function from the approximation of
-// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.28:
-//   erf(y) = 1 - (1 + a1 y + a2 y^2 + ... + a6 y^6)^-16 + eps,  |eps| <= 3e-7,  y >= 0.
-// Written without a branch on the sign: with z = |x|,
-//   x Phi(x) = (x + |x|) / 2 - z erfc(z / sqrt 2) / 2,
-// that is x - x erfc(x / sqrt 2) / 2 for x >= 0 and x erfc(-x / sqrt 2) / 2 for x < 0.  The
-// 1/sqrt(2) is folded into the coefficients (b_k = a_k 2^(-k/2)), so the cost is six FMAs,
-// four squarings and one reciprocal.  In fp32 the result is within 1e-6 |x| of x Phi(x), under
-// a thousandth of a bf16 and a hundredth of an fp16 unit in the last place.  z is clamped at
-// 30, where erfc is 0 in fp32, so that +inf maps to +inf; NaN propagates through x + |x|.
-__device__ __forceinline__ float gelu_as7128(float x) {
-  constexpr double R = 0.70710678118654752;  // 1 / sqrt 2
-  constexpr float b1 = (float)(0.0705230784 * R), b2 = (float)(0.0422820123 * R * R);
-  constexpr float b3 = (float)(0.0092705272 * R * R * R), b4 = (float)(0.0001520143 * R * R * R * R);
-  constexpr float b5 = (float)(0.0002765672 * R * R * R * R * R);
-  constexpr float b6 = (float)(0.0000430638 * R * R * R * R * R * R);
-  const float z = fminf(fabsf(x), 30.0f);
-  float h = fmaf(b6, z, b5);
-  h = fmaf(h, z, b4);
-  h = fmaf(h, z, b3);
-  h = fmaf(h, z, b2);
-  h = fmaf(h, z, b1);
-  h = fmaf(h, z, 1.0f);
-  h *= h;
-  h *= h;
-  h *= h;
-  h *= h;                                    // (1 + ...)^16
-  const float e = __builtin_amdgcn_rcpf(h);  // erfc(z / sqrt 2)
-  return 0.5f * fmaf(-z, e, x + fabsf(x));
+// GELU for 16-bit outputs, x Phi(x) with a complementary error function that keeps a bounded
+// relative error over the whole line, so that the negative tail, where x Phi(x) is tiny, is as
+// accurate as the rest.  Hastings' form (the one of Abramowitz & Stegun 7.1.26), refitted for
+// relative error (erfc_fit.py beside this file regenerates the constants):
+//   erfc(z) = t P(t) exp(-z^2),  t = 1 / (1 + p z),  z >= 0,
+// P of degree 7 fitted minimax in relative terms to exp(z^2) erfc(z) / t (6.5e-7), p = 0.46.
+// The function takes y = x / 2, which the GEMM epilogue produces directly by halving alpha,
+// beta and the bias (exact: a power-of-two scaling).  With w = |y| and z = |x| / sqrt 2 = sqrt 2 w,
+//   x Phi(x) = (x + |x|) / 2 - |x| erfc(z) / 2 = (y + |y|) - w erfc(sqrt 2 w),
+// which is x - x erfc(x / sqrt 2) / 2 for x >= 0 and x erfc(-x / sqrt 2) / 2 for x < 0, with no
+// branch on the sign.  exp(-z^2) is 2^a with a = -2 log2(e) w^2 + 32: the extra 2^32 keeps the
+// hardware exponential's result a normal number until x Phi(x) is below the fp32 range, and
+// 2^-32 is folded into P's coefficients.  In fp32 (an emulation of this operation order over
+// x in [-14.5, 14.5]) the result is within 1.9e-6 relative of x Phi(x) for x in [-6, 3] and
+// within 1e-5 wherever x Phi(x) is a normal fp32 number; the far tail's error is the rounding
+// of a.  That is under 1/390 of a bf16 and 1/48 of an fp16 unit roundoff.  w is clamped at 15
+// (x at 30): exp(-z^2) is 0 there, so +inf maps to +inf; NaN propagates through y + |y|.
+__device__ __forceinline__ float gelu16_half(float y) {
+  constexpr float kp = (float)(0.46 * 1.41421356237309505);  // p sqrt 2
+  constexpr float ka = (float)(-2.0 * 1.44269504088896341);  // -2 log2(e)
+  constexpr float g0 = 2.5952709021e-01f * 0x1p-32f, g1 = 2.5955513782e-01f * 0x1p-32f;
+  constexpr float g2 = 2.3121260461e-01f * 0x1p-32f, g3 = 1.8668765607e-01f * 0x1p-32f;
+  constexpr float g4 = 5.3007917024e-02f * 0x1p-32f, g5 = 1.6868148381e-01f * 0x1p-32f;
+  constexpr float g6 = -2.2630292169e-01f * 0x1p-32f, g7 = 6.7631682811e-02f * 0x1p-32f;
+  const float w = fminf(fabsf(y), 15.0f);
+  const float t = __builtin_amdgcn_rcpf(fmaf(w, kp, 1.0f));
+  float h = fmaf(g7, t, g6);
+  h = fmaf(h, t, g5);
+  h = fmaf(h, t, g4);
+  h = fmaf(h, t, g3);
+  h = fmaf(h, t, g2);
+  h = fmaf(h, t, g1);
+  h = fmaf(h, t, g0);
+  const float e = __builtin_amdgcn_exp2f(fmaf(w * w, ka, 32.0f));  // 2^32 exp(-z^2)
+  return fmaf(-w, (t * h) * e, y + fabsf(y));
 }
 
-// The same GELU evaluated from y = x / 2, which the GEMM epilogue produces directly by
-// halving alpha, beta and the bias (exact: a power-of-two scaling).  With w = |y|,
-//   x Phi(x) = (y + |y|) - w erfc(sqrt(2) w),
-// and erfc(sqrt(2) w) = (1 + c1 w + ... + c6 w^6)^-16 with c_k = a_k 2^(k/2) (formula 7.1.28
-// again).  This drops the final halving and the pre-scaling of the argument: 15 instructions
-// per element instead of 17.  w is clamped at 15 (x at 30) as above.
-__device__ __forceinline__ float gelu_as7128_half(float y) {
-  constexpr double Q = 1.41421356237309505;  // sqrt 2
-  constexpr float c1 = (float)(0.0705230784 * Q), c2 = (float)(0.0422820123 * Q * Q);
-  constexpr float c3 = (float)(0.0092705272 * Q * Q * Q), c4 = (float)(0.0001520143 * Q * Q * Q * Q);
-  constexpr float c5 = (float)(0.0002765672 * Q * Q * Q * Q * Q);
-  constexpr float c6 = (float)(0.0000430638 * Q * Q * Q * Q * Q * Q);
-  const float w = fminf(fabsf(y), 15.0f);
-  float h = fmaf(c6, w, c5);
-  h = fmaf(h, w, c4);
-  h = fmaf(h, w, c3);
-  h = fmaf(h, w, c2);
-  h = fmaf(h, w, c1);
-  h = fmaf(h, w, 1.0f);
-  h *= h;
-  h *= h;
-  h *= h;
-  h *= h;
-  return fmaf(-w, __builtin_amdgcn_rcpf(h), y + fabsf(y));
-}
+// The same GELU from x itself.
+__device__ __forceinline__ float gelu16(float x) { return gelu16_half(0.5f * x); }
 
 // GELU at the precision the output type can hold: the device erfc for fp32 outputs, the
-// branch-free approximation above for fp16 / bf16 outputs.
+// branch-free form above for fp16 / bf16 outputs.
 template <int CT>
 __device__ __forceinline__ float gelu_out(float x) {
   if constexpr (CT == F32) return gelu_erf(x);
-  else return gelu_as7128(x);
+  else return gelu16(x);
 }
 
 // alpha*acc (+ beta*c_in) (+ bias) then GELU: the fused epilogue applied in registers.

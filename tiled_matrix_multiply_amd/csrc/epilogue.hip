@@ -13,7 +13,7 @@ namespace tgemm {
 // and no index is divided.  The chunk's bias values are read once.  Requires N % 8 == 0,
 // ldc % 8 == 0 and a 16-byte-aligned C.
 // For 16-bit outputs with GELU the elementwise work is the fused epilogue's: y = (x + b) / 2
-// (one fma with the bias halved; halving is exact) and gelu_as7128_half(y).
+// (one fma with the bias halved; halving is exact) and gelu16_half(y).
 template <int CT, int R>
 __global__ __launch_bounds__(256) void bias_gelu_vec_kernel(void* C, int64_t ldc, int M, int N,
                                                             const float* bias, uint32_t epi, int TX) {
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void bias_gelu_vec_kernel(void* C, int64_t ldc
           x = (CT == F16) ? f16_bits_to_float(h) : bf16_bits_to_float(h);
         }
         if (half) {
-          v[e] = gelu_as7128_half(fmaf(0.5f, x, bj[e]));
+          v[e] = gelu16_half(fmaf(0.5f, x, bj[e]));
         } else {
           x += bj[e];
           if (epi & EPI_GELU) x = gelu_out<CT>(x);

@@ -988,7 +988,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
     // specialised on (beta != 0, GELU) so that it carries no branches: this loop runs on the
     // vector ALUs after the last multiply, so every instruction in it is paid in full.
     // With GELU and a 16-bit output the element loop computes y = x / 2 (alpha, beta and the
-    // bias halved, an exact scaling) and gelu_as7128_half(y).
+    // bias halved, an exact scaling) and gelu16_half(y).
     const bool half = C::CT != F32 && (epi & EPI_GELU);
     const float hs = half ? 0.5f : 1.0f;
     float bj[C::FN][4][4];
@@ -1051,7 +1051,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
               if constexpr (HB) x = fmaf(beta_e, cin[j][rg][e], x);
               if constexpr (HG) {
                 if constexpr (C::CT == F32) x = gelu_out<C::CT>(x);
-                else x = gelu_as7128_half(x);
+                else x = gelu16_half(x);
               }
               v[e] = x;
             }

@@ -2,8 +2,11 @@
 
 Bars: bit-exact where the arithmetic is exact (integer-valued inputs, identity/permutation
 operands, the fp8 format probe); otherwise the normalised-error gate
-max |C - Cref| / (sum_k |a b| + |beta C_in|) <= K * 2^-23 + u_out, checked on every entry at sizes
-the oracle finishes in seconds and on sampled entries at the full 2048/4096 sizes.
+max |C - Cref| / (sum_k |a b| + |beta C_in|) <= K * 2^-23 + u_out, checked on every output entry,
+the full 2048^3 and 4096^3 workloads included (the float64 oracle runs 4096^3 in seconds on the
+host's cores); the headline workload is also checked on sampled entries each recomputed on its
+own (a second path through the oracle).  The 16-bit GELU is checked in relative terms over the
+whole line, its negative tail included.
 """
 import itertools
 import zlib
@@ -169,7 +172,7 @@ def test_fp32_1000_nn_vs_tn_report(g):
 def test_fp16_square(g, n):
     p = W.fp16_square(n)
     _, got = H.run(g, p)
-    res = H.gate_full(p, got) if n <= 1024 else H.gate_sampled(p, got)
+    res = H.gate_full(p, got)
     _report(f"fp16 {n}^3", res)
     assert res.ok
 
@@ -178,9 +181,14 @@ def test_fp16_square(g, n):
 def test_bf16_bias_gelu_fused(g, n):
     p = W.bf16_bias_gelu(n)
     _, got = H.run(g, p)
-    res = H.gate_full(p, got) if n <= 1024 else H.gate_sampled(p, got)
+    res = H.gate_full(p, got, cache=True)
     _report(f"bf16+bias+GELU fused {n}^3", res)
     assert res.ok
+    if n == 4096:
+        # the headline workload: sampled entries too, each recomputed on its own by the oracle
+        res = H.gate_sampled(p, got)
+        _report(f"bf16+bias+GELU fused {n}^3 (sampled, per-entry oracle)", res)
+        assert res.ok
 
 
 @pytest.mark.parametrize("n", [512, 1024, 2048, 4096])
@@ -194,8 +202,7 @@ def test_bf16_bias_gelu_unfused(g, n):
     g.bias_gelu(d.C, d.bias, M=p.M, N=p.N, c_type="bf16")
     torch.cuda.synchronize()
     got = oracle.decode("bf16", H.from_device(d.C, "bf16"))
-    res = (H.gate_full(p, got, roundings=2) if n <= 1024
-           else H.gate_sampled(p, got, roundings=2))
+    res = H.gate_full(p, got, roundings=2, cache=True)
     _report(f"bf16 GEMM then bias+GELU (unfused) {n}^3", res)
     assert res.ok
 
@@ -207,10 +214,10 @@ def test_bf16_bias_gelu_unfused(g, n):
 def test_unfused_bias_gelu_pass(g, c_type, M, N, ldc, epi):
     """The separate elementwise pass on its own: C = GELU(C + bias) in place, on vector-path
     shapes (N and ldc multiples of 8, rows past the 65535 x 4 the launch covers in one pass)
-    and scalar-path shapes, against the oracle's erf-GELU of the same stored values.  One
-    rounding to the output type (relative, or half a step among subnormals); the approximation
-    adds at most 1e-6 of |x + b|.  The padding
-    of a row (ldc > N) must come back untouched."""
+    and scalar-path shapes, against the oracle's erf-GELU of the same stored values.  Inputs
+    ~ N(0, 3^2), so the negative tail down to about -14 is exercised.  The bound is relative:
+    one rounding to the output type plus the GELU's own error (EPS_GELU), or half a step among
+    subnormals.  The padding of a row (ldc > N) must come back untouched."""
     import torch
     rng = np.random.default_rng(M * 7 + N * 3 + ldc + epi)
     x = rng.normal(0.0, 3.0, size=(M, ldc))
@@ -225,25 +232,71 @@ def test_unfused_bias_gelu_pass(g, c_type, M, N, ldc, epi):
     xin = oracle.decode(c_type, stored[:, :N])
     t = xin + (bias.astype(np.float64) if epi & W.EPI_BIAS else 0.0)
     if epi & W.EPI_GELU:
-        from scipy.special import erfc
-        want = 0.5 * t * erfc(-t / np.sqrt(2.0))  # x Phi(x), vectorised
+        want = _gelu64(t)
         few = t.ravel()[:64]
         assert np.allclose([oracle.gelu(v) for v in few], want.ravel()[:64], rtol=1e-14, atol=0)
     else:
         want = t
-    u = {"f32": 2.0 ** -23, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[c_type]
-    sub = {"f32": 2.0 ** -150, "f16": 2.0 ** -25, "bf16": 2.0 ** -134}[c_type]  # half a subnormal step
-    tol = u * np.abs(want) + 1e-6 * np.abs(t) + sub
-    err = np.abs(got - want)
-    bad = ~(err <= tol)
+    # The bias add is one fp32 rounding of t (relative 2^-24) ahead of GELU, whose relative
+    # sensitivity d log(x Phi(x)) / d log x = 1 + x phi(x) / Phi(x) stays below 1 + x^2.
+    eps = 0.0
+    if epi & W.EPI_GELU:
+        eps = EPS_GELU + ((1.0 + t * t) * 2.0 ** -24 if epi & W.EPI_BIAS else 0.0)
+    elif epi & W.EPI_BIAS:
+        eps = 2.0 ** -24
+    bad = ~(np.abs(got - want) <= (U_OUT[c_type] + eps) * np.abs(want) + SUB[c_type])
     assert not bad.any(), f"{bad.sum()} elements, first at {np.argwhere(bad)[0]}: got {got[bad][0]} want {want[bad][0]}"
+
+
+# Relative error of the library's GELU: the 16-bit outputs' erfc approximation is within 1e-5
+# of x Phi(x) wherever x Phi(x) is a normal fp32 number (1.9e-6 on [-6, 3]); the fp32 outputs'
+# device erfcf loses up to about 2 z^2 fp32 roundings to its argument z = -x / sqrt 2 in the
+# tail (1.2e-5 at x = -14).  2^-16 = 1.5e-5 covers both.
+EPS_GELU = 2.0 ** -16
+U_OUT = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}   # unit roundoff
+# Absolute allowance: half a subnormal step of the 16-bit outputs; for fp32 outputs 8 subnormal
+# steps, since past x = -13 the device erfcf is itself an fp32 subnormal, each of its roundings
+# up to half a step, and the result scales it by |x| / 2 <= 7.
+SUB = {"f32": 2.0 ** -146, "f16": 2.0 ** -25, "bf16": 2.0 ** -134}
+
+
+def _gelu64(t):
+    """x Phi(x) in float64, vectorised (the oracle's formula, 0.5 x erfc(-x / sqrt 2))."""
+    from scipy.special import erfc
+    return 0.5 * t * erfc(-t / np.sqrt(2.0))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("kernel", ["simt", "mfma32", "mfma64", "mfma128", "mfma256"])
+def test_gelu_tail_fused_k1(g, dtype, kernel):
+    """The fused epilogue's GELU in relative terms over [-14, 4]: with K = 1 every accumulator
+    is one exact product (a 16-bit value times a power of two), so the pre-activation is known
+    exactly and the output must be x Phi(x) rounded once, to within EPS_GELU.  The shape has
+    full and edge tiles for every kernel family."""
+    M, N = 520, 264
+    rng = np.random.default_rng(zlib.crc32(f"gelu/{dtype}/{kernel}".encode()))
+    x = W.encode(rng.uniform(-7.0, 2.0, size=(M, 1)), dtype)
+    scales = rng.choice([2.0, 1.0, 0.5, -0.5, 1.0, 2.0], size=(1, N))
+    p = W.Problem("gelu_tail", M, N, 1, False, False, 1.0, 0.0, dtype, dtype, dtype,
+                  W.EPI_GELU, x, W.encode(scales, dtype), np.zeros((M, N), W.STORAGE[dtype]),
+                  None)
+    got, kname, pad_ok = H.run_padded(g, p, kernel=KERNELS[kernel])
+    t = oracle.decode(dtype, x) * scales
+    want = _gelu64(t)
+    Cref, _ = oracle.gemm(p)
+    assert np.allclose(Cref, want, rtol=1e-13, atol=1e-300)
+    assert t.min() < -13.0 and t.max() > 3.5
+    bad = ~(np.abs(got - want) <= (U_OUT[dtype] + EPS_GELU) * np.abs(want) + SUB[dtype])
+    assert pad_ok
+    assert not bad.any(), (f"{kname}: {bad.sum()} elements, first at {np.argwhere(bad)[0]}: "
+                           f"x={t[bad][0]!r} got {got[bad][0]!r} want {want[bad][0]!r}")
 
 
 @pytest.mark.parametrize("n", [512, 4096])
 def test_fp8_e4m3(g, n):
     p = W.fp8_4096(n)
     _, got = H.run(g, p)
-    res = H.gate_full(p, got) if n <= 1024 else H.gate_sampled(p, got)
+    res = H.gate_full(p, got)
     _report(f"fp8 E4M3 {n}^3 (sa={p.scale_a:.4g}, sb={p.scale_b:.4g})", res)
     assert res.ok
 
@@ -251,7 +304,7 @@ def test_fp8_e4m3(g, n):
 def test_bf16_twin_4096(g):
     p = W.bf16_twin_of_fp8(4096)
     _, got = H.run(g, p)
-    res = H.gate_sampled(p, got)
+    res = H.gate_full(p, got)
     _report("bf16 4096^3 (fp8 twin)", res)
     assert res.ok
 
@@ -262,7 +315,7 @@ def test_k_split_beyond_one_round(g, M, N, K):
     p = W.make_problem(M, N, K, a_type="bf16", seed=17, dist_a=("normal", 1.0),
                        dist_b=("normal", 1.0 / np.sqrt(K)), epilogue=W.EPI_BIAS | W.EPI_GELU)
     _, got = H.run(g, p)
-    res = H.gate_sampled(p, got)
+    res = H.gate_full(p, got)
     _report(f"bf16+bias+GELU {M}x{N}x{K} (64 tile, K split)", res)
     assert res.ok
 
@@ -429,4 +482,20 @@ def test_large_extents(g, case):
     res = H.gate_full(p, got)
     print(f"[large] {case} {p.M}x{p.N}x{p.K} {kname}: {res}", flush=True)
     assert kname != "simt", kname
+    assert pad_ok and res.ok, res
+
+
+@pytest.mark.parametrize("trans_a", [False, True])
+def test_tall_unaligned_takes_simt(g, trans_a):
+    """M = 2^20 + 3 rows with an odd leading dimension: the matrix-core kernels cannot take the
+    layout, so AUTO uses the scalar kernel, which must take any M (its workgroups stride over
+    the tiles; there is no per-dimension grid limit)."""
+    M, N, K = (1 << 20) + 3, 5, 40
+    p = W.make_problem(M, N, K, a_type="f32", trans_a=trans_a, seed=73, alpha=0.5, beta=-1.0,
+                       dist_a=("normal", 1.0), dist_b=("normal", 1.0), dist_c=("normal", 1.0),
+                       epilogue=W.EPI_BIAS | W.EPI_GELU)
+    got, kname, pad_ok = H.run_padded(g, p, ld_fn=lambda w: w + 1 if w % 2 == 0 else w + 2)
+    res = H.gate_full(p, got)
+    print(f"[large] tall unaligned {M}x{N}x{K} trans_a={trans_a} {kname}: {res}", flush=True)
+    assert kname == "simt", kname
     assert pad_ok and res.ok, res

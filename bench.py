@@ -8,7 +8,12 @@ that problem with every input already resident in HBM.  Throughput is 2*M*N*K pe
 fp16 n^3, bf16 fused versus unfused n^3 for n in {512, 1024, 2048, 4096}, and fp8-E4M3 versus
 bf16 at 4096^3.  Each cell: warm up for >= 200 ms, then R timed reps with one HIP event pair
 per rep on the stream the kernel runs on; median and a percentile-bootstrap 95% CI
-(10^4 resamples, seed 0), as "Rigel" (arXiv 2606.12765), section 3 reports its cells.
+(10^4 resamples, seed 0), as "Rigel" (arXiv 2606.12765), section 3 reports its cells.  The
+headline's timed steps come after a time-based settle (--settle-seconds of back-to-back steps)
+and the --warmup steps.  The shader clock is sampled during every timed region and printed
+beside its fraction of peak ("Rigel" section 3: the clock state decides small-size results),
+and a measured device-copy bandwidth stands beside the 8 TB/s HBM figure as the practical
+ceiling of the bandwidth-bound cells ("Case Study: The Tiled GEMM", its bandwidth roofline).
 
 Prints ONE JSON line.  Only --gpus 1 is supported: the library runs on a single GPU.
 """
@@ -66,6 +71,75 @@ def bootstrap_ci(x: np.ndarray, n_boot: int = 10000, seed: int = 0):
     return float(np.percentile(meds, 2.5)), float(np.percentile(meds, 97.5))
 
 
+class ClockProbe:
+    """The shader clock a timed region left the chip at, read in-kernel: gemm_probe_clock
+    enqueued on the same stream right behind the region's last launch, `workgroups` one-wave
+    workgroups each timing `us` microseconds of the constant-rate counter against the
+    shader-clock cycle counter.  The published peaks assume 2.4 GHz; under sustained
+    matrix-core load the clock is held lower by power, so every fraction of peak is quoted
+    beside this reading."""
+
+    def __init__(self, g, workgroups: int = 256, us: int = 40):
+        import torch
+        import tiled_matrix_multiply_amd as tmm
+        self.tmm = tmm
+        self.h = g.handle
+        self.wg, self.us = workgroups, us
+        self.buf = torch.zeros(4 * workgroups, dtype=torch.int64, device="cuda:0")
+        self.khz = tmm.gemm_wall_clock_khz(self.h)
+
+    def enqueue(self, stream):
+        st = self.tmm.gemm_probe_clock(self.h, stream, self.buf.data_ptr(), self.wg, self.us)
+        if st != 0:
+            raise RuntimeError(f"gemm_probe_clock: {self.tmm.gemm_status_string(st)}")
+
+    def read(self):
+        """After a synchronisation: mean, min and max over the workgroups (MHz)."""
+        v = self.buf.cpu().numpy().reshape(-1, 4).astype(np.float64)
+        mhz = (v[:, 2] - v[:, 0]) / (v[:, 3] - v[:, 1]) * self.khz / 1000.0
+        return {"mean": round(float(mhz.mean()), 1), "min": round(float(mhz.min()), 1),
+                "max": round(float(mhz.max()), 1), "workgroups": int(mhz.size),
+                "source": "s_memtime / s_memrealtime probe right after the timed launches"}
+
+
+def hbm_ceiling(g, nbytes: int = 1 << 30, reps: int = 20) -> dict:
+    """Measured HBM ceiling with the library's bandwidth probe over `nbytes` (4x the 256 MB
+    last-level cache, so every rep streams from HBM): a read-only stream and a copy, each timed
+    with one event pair around `reps` launches after a warm-up.  GB/s counts bytes read (plus
+    bytes written for the copy)."""
+    import torch
+    import tiled_matrix_multiply_amd as tmm
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    s = torch.cuda.current_stream()
+    out = {"bytes": nbytes, "reps": reps, "kind": "library bandwidth probe: 16-byte loads, "
+                                                   "4 in flight per thread"}
+    for mode, d, moved in (("read", None, nbytes), ("copy", dst.data_ptr(), 2 * nbytes)):
+        def launch():
+            st = tmm.gemm_probe_bandwidth(g.handle, s.cuda_stream, src.data_ptr(), d, nbytes,
+                                          sink.data_ptr())
+            if st != 0:
+                raise RuntimeError(f"gemm_probe_bandwidth: {tmm.gemm_status_string(st)}")
+        for _ in range(3):
+            launch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            launch()
+        e1.record(s)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"{mode}_gbs"] = round(moved / (ms * 1e-3) / 1e9, 1)
+        out[f"{mode}_us"] = round(ms * 1e3, 2)
+        print(f"[bench] HBM {mode} probe over {nbytes >> 20} MiB: {ms * 1e3:.1f} us, "
+              f"{out[f'{mode}_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 class Cell:
     """Device-resident operands of one workload and the call that runs it."""
 
@@ -121,18 +195,27 @@ class Cell:
                     raise RuntimeError(f"gemm_bias_gelu: {tmm.gemm_status_string(st)}")
         self.step = step
 
-    def time(self, reps: int, warmup_s: float = 0.2, warmup_min: int = 3):
-        """Per-rep durations (ms) from HIP event pairs on the kernel's stream."""
+    def settle(self, seconds: float, min_steps: int = 3) -> int:
+        """Back-to-back steps for at least `seconds` of wall time (clocks and power settle);
+        returns the number of steps run."""
         import torch
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         n = 0
-        while n < warmup_min or time.perf_counter() - t0 < warmup_s:
+        while n < min_steps or time.perf_counter() - t0 < seconds:
             self.step()
             n += 1
             if n % 16 == 0:
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
+        return n
+
+    def time(self, reps: int, warmup_s: float = 0.2, warmup_min: int = 3, clock=None):
+        """Per-rep durations (ms) from HIP event pairs on the kernel's stream, after a time-based
+        warm-up; `clock` (a ClockProbe) is queued right behind the timed launches, its reading
+        kept in self.sclk."""
+        import torch
+        self.settle(warmup_s, warmup_min)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]
         for s, e in ev:
@@ -149,8 +232,11 @@ class Cell:
         for _ in range(reps):
             self.step()
         e1.record(self.stream)
+        if clock is not None:
+            clock.enqueue(self.stream.cuda_stream)
         torch.cuda.synchronize()
         self.b2b_ms = e0.elapsed_time(e1) / reps
+        self.sclk = clock.read() if clock is not None else None
         return ms
 
     def algorithmic_bytes(self) -> int:
@@ -214,6 +300,7 @@ class QCell:
                 raise RuntimeError(f"gemm_run_q: {tmm.gemm_status_string(st)}")
         self.step = step
 
+    settle = Cell.settle
     time = Cell.time
 
     def algorithmic_bytes(self) -> int:
@@ -339,10 +426,12 @@ def summarize(name, cell: Cell, ms: np.ndarray, dtype: str) -> dict:
                            round(p.flops / (lo * 1e-3) / 1e12, 2)],
            "pct_peak": round(100 * tf / PEAK_TFLOPS[dtype], 2),
            "gbs": round(cell.algorithmic_bytes() / (med * 1e-3) / 1e9, 1),
-           "back_to_back_us": round(getattr(cell, "b2b_ms", float("nan")) * 1e3, 3)}
+           "back_to_back_us": round(getattr(cell, "b2b_ms", float("nan")) * 1e3, 3),
+           "sclk_mhz": getattr(cell, "sclk", None)}
     print(f"[bench] {name:34s} {cell.kernel:8s} {row['median_us']:10.2f} us  "
           f"{row['tflops']:8.1f} TFLOP/s  {row['pct_peak']:5.1f}% of {dtype} peak  "
-          f"{row['gbs']:8.1f} GB/s  (back to back {row['back_to_back_us']:.2f} us)",
+          f"{row['gbs']:8.1f} GB/s  (back to back {row['back_to_back_us']:.2f} us)"
+          f"{'' if row['sclk_mhz'] is None else '  sclk %.0f MHz' % row['sclk_mhz']['mean']}",
           file=sys.stderr, flush=True)
     return row
 
@@ -417,8 +506,11 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300, help="timed steps (headline)")
-    ap.add_argument("--warmup", type=int, default=2000,
-                    help="untimed warmup steps (headline; the default runs ~0.25 s so clocks settle)")
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed warm-up steps (headline), run after the time-based settle")
+    ap.add_argument("--settle-seconds", type=float, default=0.3,
+                    help="back-to-back headline steps for at least this long before the warm-up "
+                         "steps, whatever --warmup says (clocks and power settle)")
     ap.add_argument("--reps", type=int, default=300, help="timed reps per sweep cell")
     ap.add_argument("--no-sweeps", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -484,10 +576,15 @@ def main():
             print(f"[bench] copied {args.copy_bytes} bytes 3 times", file=sys.stderr)
         return
 
-    # Headline: W untimed steps, then exactly K back-to-back steps between two
-    # synchronisations, with one HIP event pair around them on the launch stream (the
-    # average launch duration for the roofline).  A second pass times each step with its own
-    # event pair for the median and its bootstrap CI.
+    # Headline.  A time-based settle (>= --settle-seconds of back-to-back steps, whatever
+    # --warmup says: the clock and power state need wall time, not a step count), then the W
+    # untimed warm-up steps, then exactly K back-to-back steps between two synchronisations,
+    # with one HIP event pair around them on the launch stream: their period is the average
+    # launch period (launch to launch), from which the roofline's achieved rate is taken.  The
+    # shader clock is sampled over the end of the settle and the timed steps.  A second pass
+    # times each step with its own event pair for the median and its bootstrap CI.
+    clock = ClockProbe(g)
+    settle_steps = head.settle(args.settle_seconds)
     for _ in range(args.warmup):
         head.step()
     torch.cuda.synchronize()
@@ -499,18 +596,30 @@ def main():
     e1.record(head.stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the clock right behind a second, identical run of K steps (not inside the timed region)
+    for _ in range(args.steps):
+        head.step()
+    clock.enqueue(head.stream.cuda_stream)
+    torch.cuda.synchronize()
+    head_sclk = clock.read()
     ms_per_step = wall * 1e3 / args.steps
     value = head_p.flops / (ms_per_step * 1e-3) / 1e12
-    mean_ms = e0.elapsed_time(e1) / args.steps
-    achieved = head_p.flops / (mean_ms * 1e-3) / 1e12
-    ms = head.time(args.steps, warmup_s=0.05)
+    period_ms = e0.elapsed_time(e1) / args.steps
+    achieved = head_p.flops / (period_ms * 1e-3) / 1e12
+    print(f"[bench] headline: settle {settle_steps} steps ({args.settle_seconds:.2f} s), warm-up "
+          f"{args.warmup}, {args.steps} timed steps: {period_ms * 1e3:.2f} us per launch "
+          f"({achieved:.1f} TFLOP/s), wall {ms_per_step * 1e3:.2f} us per step"
+          f"{'' if head_sclk is None else ', sclk %.0f MHz' % head_sclk['mean']}",
+          file=sys.stderr, flush=True)
+    ms = head.time(max(args.steps, 30), warmup_s=0.05, clock=clock)
     head_row = summarize("bf16+bias+GELU fused 4096 (headline)", head, ms, "bf16")
 
+    hbm = None if args.no_sweeps else hbm_ceiling(g)
     sweeps = []
     if not args.no_sweeps:
         for name, dtype, make in sweep_cells():
             c = make(g)
-            row = summarize(name, c, c.time(args.reps), dtype)
+            row = summarize(name, c, c.time(args.reps, clock=clock), dtype)
             gms = graph_time(c)
             row["graph_us"] = round(gms * 1e3, 3) if gms is not None else None
             if gms is not None:
@@ -518,7 +627,11 @@ def main():
                       file=sys.stderr, flush=True)
             if isinstance(c, QCell) and c.p.M <= 4:
                 row["pct_hbm"] = round(100 * row["gbs"] / PEAK_HBM_GBS, 2)
-                print(f"[bench] {'':34s} {row['pct_hbm']:.1f}% of HBM peak "
+                if hbm is not None:
+                    row["pct_read_ceiling"] = round(100 * row["gbs"] / hbm["read_gbs"], 2)
+                    row["pct_copy_ceiling"] = round(100 * row["gbs"] / hbm["copy_gbs"], 2)
+                print(f"[bench] {'':34s} {row['pct_hbm']:.1f}% of HBM peak"
+                      f"{'' if hbm is None else ', %.1f%% of the measured read ceiling' % row['pct_read_ceiling']} "
                       f"({c.algorithmic_bytes() / 1e6:.1f} MB per launch)", file=sys.stderr,
                       flush=True)
             sweeps.append(row)
@@ -539,6 +652,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"seconds": args.settle_seconds, "steps": settle_steps},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -555,8 +669,15 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_TFLOPS["bf16"], 4), "traffic": traffic,
-                     "kernel_mean_us": round(mean_ms * 1e3, 3),
-                     "flops_per_launch": head_p.flops},
+                     "launch_period_us": round(period_ms * 1e3, 3),
+                     "flops_per_launch": head_p.flops,
+                     "sclk_mhz": head_sclk,
+                     "frac_at_measured_sclk": (round(achieved / (PEAK_TFLOPS["bf16"] * head_sclk["mean"] / 2400.0), 4)
+                                               if head_sclk else None)},
+        "sclk_mhz": head_sclk["mean"] if head_sclk else None,
+        "hbm_copy_gbs": hbm["copy_gbs"] if hbm else None,
+        "hbm_read_gbs": hbm["read_gbs"] if hbm else None,
+        "hbm_ceiling": hbm,
         "cpu_baseline": cpu,
         "sweeps": sweeps,
         "provenance": provenance(src_hash),

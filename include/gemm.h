@@ -19,8 +19,8 @@
  *     matmul2d_descriptor);
  *   - the fused GEMM + bias + GELU versus the decomposed path, and fp8 E4M3 operands:
  *     "Rigel", abstract and section 1 (contribution 7);
- *   - the other low-precision formats it lists beside fp8, block-scaled MXFP4 among them:
- *     "Rigel", section 4 (the format rows of its results); the 6-bit types of the same OCP
+ *   - the other low-precision formats it lists beside fp8, fp4 and block-scaled MXFP4:
+ *     "Rigel", section 1 (the formats Metal 4.1 adds); the 6-bit types of the same OCP
  *     microscaling family (E2M3, E3M2) follow the OCP MX v1.0 specification, which the pages
  *     do not cover.
  *
@@ -98,9 +98,10 @@ typedef enum gemm_dtype {
 /* Kernel families, for gemm_run_kernel.  AUTO picks by type, layout, alignment and size. */
 typedef enum gemm_kernel {
   GEMM_KERNEL_AUTO = 0,
-  GEMM_KERNEL_SIMT = 1,     /* LDS-tiled scalar FMA, 16x16 tile, one output per thread: the
-                               plain tiled kernel without matrix cores ("X3: Metal GEMM",
-                               section 2, translated to HIP).  Any alignment. */
+  GEMM_KERNEL_SIMT = 1,     /* LDS-tiled scalar FMA without matrix cores: a 64x64 tile per
+                               workgroup, a 4x4 register block per thread, double-buffered K
+                               slices (the shared-memory tiling of "X3: Metal GEMM", section
+                               2).  Any alignment, layout and size. */
   GEMM_KERNEL_MFMA_64 = 2,  /* matrix-core kernel, 64x64 workgroup tile, 4 wavefronts */
   GEMM_KERNEL_MFMA_128 = 3, /* matrix-core kernel, 128x128 workgroup tile, 4 wavefronts */
   GEMM_KERNEL_MFMA_256 = 4, /* matrix-core kernel, 256x256 workgroup tile, 8 wavefronts */
@@ -277,6 +278,38 @@ GEMM_API int gemm_select_kernel_q(gemm_handle_t h, int64_t M, int64_t N, int64_t
 
 /* A static, human-readable name for a status code (never NULL). */
 GEMM_API const char* gemm_status_string(gemm_status_t s);
+
+/* ---- Measurement helpers (used by the benchmark; not part of the GEMM) ----
+ *
+ * The fractions of peak a benchmark reports depend on the shader clock the chip ran at ("Rigel"
+ * (arXiv 2606.12765), section 3: clock-state effects decide its small-size results) and, for
+ * bandwidth-bound work, on the bandwidth the memory really delivers ("Case Study: The Tiled
+ * GEMM": a measured bandwidth roofline beside the product's numbers). */
+
+/* Shader clock probe.  Enqueues `workgroups` (1 .. 65536) one-wave workgroups on `stream`; each
+ * reads the shader-clock cycle counter and the constant-rate counter at its start and again
+ * once `microseconds` (1 .. 100000) of the constant clock have passed (at most 2^16 polls), and
+ * writes four uint64 to out[4 w .. 4 w + 3]: cycles at start, ticks at start, cycles at end,
+ * ticks at end.  The clock in MHz is (cycles) / (ticks) * gemm_wall_clock_khz(h) / 1000.
+ * `out` is a DEVICE pointer owned by the caller.  Queued right behind a timed run, it reads the
+ * clock that run left the chip at.  Errors: GEMM_ERR_INVALID_HANDLE, GEMM_ERR_INVALID_VALUE (null
+ * out or a count out of range), GEMM_ERR_DEVICE (no constant-rate counter rate), GEMM_ERR_LAUNCH. */
+GEMM_API gemm_status_t gemm_probe_clock(gemm_handle_t h, void* stream, uint64_t* out,
+                                        int workgroups, int microseconds);
+
+/* Rate of the constant-rate counter the clock probe reads, in kHz (100000 on MI355X), or a
+ * negative status for an invalid handle. */
+GEMM_API int gemm_wall_clock_khz(gemm_handle_t h);
+
+/* Bandwidth probe: streams `bytes` (a multiple of 16) from `src` with 16-byte loads, four in
+ * flight per thread, and writes them to `dst` (a copy; it must not overlap src) or, with dst
+ * NULL, only reads them (`sink`, a DEVICE uint32, is written only for one improbable checksum
+ * and must not be NULL then).  src and dst are 16-byte-aligned DEVICE pointers owned by the
+ * caller.  Asynchronous on `stream`.  Errors: GEMM_ERR_INVALID_HANDLE, GEMM_ERR_INVALID_VALUE
+ * (null src, misaligned pointers, bytes <= 0 or not a multiple of 16, no sink for a read),
+ * GEMM_ERR_ALIAS (dst overlaps src), GEMM_ERR_LAUNCH. */
+GEMM_API gemm_status_t gemm_probe_bandwidth(gemm_handle_t h, void* stream, const void* src,
+                                            void* dst, int64_t bytes, uint32_t* sink);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@
  * and of a column of op(B) shares one E8M0 scale 2^(e - 127) (e = 255 is NaN), so
  *   a(i,k) = dec(A ...) * 2^(sa[i*ldsa + k/32] - 127),  b(k,j) = dec(B ...) * 2^(sb[j*ldsb + k/32] - 127)
  * with the per-tensor scales then 1.  This is the plain reading of the MX formats that
- * "Rigel" (arXiv 2606.12765) lists next to fp8 (section 4, the block-scaled MXFP4 rows); the
+ * "Rigel" (arXiv 2606.12765) lists next to fp8 (section 1: fp4 and block-scaled MXFP4); the
  * 6-bit element types E2M3 and E3M2 of the same MX family are decoded as the OCP MX v1.0
  * specification defines them (the pages name no 6-bit type).
  *

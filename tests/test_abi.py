@@ -23,7 +23,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported():
     syms = declared_symbols()
-    assert len(syms) == 15, syms
+    assert len(syms) == 18, syms
     assert sorted(tmm.EXPORTS) == syms
     nm = subprocess.run(["nm", "-D", "--defined-only", tmm.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
@@ -33,6 +33,14 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(tmm.library(), s)
     # nothing but the C ABI is exported
     assert {s for s in exported if not s.startswith("gemm_")} == set(), exported
+
+
+def test_measurement_helpers_validate_without_a_gpu():
+    """The clock and bandwidth probes refuse a null handle before touching a device."""
+    assert tmm.gemm_probe_clock(None, None, 0x1000, 256, 40) == tmm.GEMM_ERR_INVALID_HANDLE
+    assert tmm.gemm_wall_clock_khz(None) == tmm.GEMM_ERR_INVALID_HANDLE
+    assert tmm.gemm_probe_bandwidth(None, None, 0x1000, None, 1 << 20,
+                                    0x2000) == tmm.GEMM_ERR_INVALID_HANDLE
 
 
 def test_status_strings():

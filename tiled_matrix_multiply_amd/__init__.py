@@ -52,7 +52,8 @@ KERNEL_NAME = {0: "auto", 1: "simt", 2: "mfma64", 3: "mfma128", 4: "mfma256", 5:
 EXPORTS = ("gemm_create", "gemm_destroy", "gemm_check_args", "gemm_run", "gemm_run_kernel",
            "gemm_run_mx", "gemm_run_mx_kernel", "gemm_check_args_mx", "gemm_select_kernel",
            "gemm_bias_gelu", "gemm_status_string", "gemm_run_q", "gemm_run_q_kernel",
-           "gemm_check_args_q", "gemm_select_kernel_q")
+           "gemm_check_args_q", "gemm_select_kernel_q", "gemm_probe_clock",
+           "gemm_wall_clock_khz", "gemm_probe_bandwidth")
 
 # libgemm.so must resolve its libamdhip64.so.7 dependency to the HIP runtime instance that owns
 # the caller's device pointers and streams.  PyTorch ships its own runtime (soname
@@ -115,6 +116,12 @@ _lib.gemm_check_args_q.argtypes = _QCHK
 _lib.gemm_check_args_q.restype = _int
 _lib.gemm_select_kernel_q.argtypes = [_vp] + _QCHK
 _lib.gemm_select_kernel_q.restype = _int
+_lib.gemm_probe_clock.argtypes = [_vp, _vp, _vp, _int, _int]
+_lib.gemm_probe_clock.restype = _int
+_lib.gemm_wall_clock_khz.argtypes = [_vp]
+_lib.gemm_wall_clock_khz.restype = _int
+_lib.gemm_probe_bandwidth.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp]
+_lib.gemm_probe_bandwidth.restype = _int
 _lib.gemm_status_string.argtypes = [_int]
 _lib.gemm_status_string.restype = ctypes.c_char_p
 
@@ -228,6 +235,18 @@ def gemm_select_kernel_q(handle, M, N, K, X, ldx, Wq, ldw, bits, group, scales, 
                          C, ldc, x_type, epilogue, bias) -> int:
     return _lib.gemm_select_kernel_q(handle, M, N, K, X, ldx, Wq, ldw, bits, group, scales,
                                      offsets, ldg, C, ldc, x_type, epilogue, bias)
+
+
+def gemm_probe_clock(handle, stream, out, workgroups, microseconds) -> int:
+    return _lib.gemm_probe_clock(handle, stream, out, workgroups, microseconds)
+
+
+def gemm_wall_clock_khz(handle) -> int:
+    return _lib.gemm_wall_clock_khz(handle)
+
+
+def gemm_probe_bandwidth(handle, stream, src, dst, nbytes, sink) -> int:
+    return _lib.gemm_probe_bandwidth(handle, stream, src, dst, nbytes, sink)
 
 
 # ----------------------------------------------------------------- tensor helpers --

@@ -43,6 +43,9 @@ TGEMM_F8_LAUNCHER(mx_e3m2_e2m3)
 #undef TGEMM_F8_LAUNCHER
 hipError_t launch_bias_gelu(void* C, int64_t ldc, int M, int N, int c_type, const float* bias,
                             uint32_t epi, int cu_count, hipStream_t s);
+hipError_t launch_clock_probe(uint64_t* out, int workgroups, uint64_t ticks, hipStream_t s);
+hipError_t launch_bandwidth_probe(const void* src, void* dst, int64_t bytes, uint32_t* sink,
+                                  int cu_count, hipStream_t s);
 }  // namespace tgemm
 
 namespace {
@@ -239,6 +242,12 @@ gemm_status_t gemm_create(gemm_handle_t* out, int device) {
   h->magic = tgemm::kHandleMagic;
   h->device = device;
   h->cu_count = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+  int wall = 0;
+  if (hipDeviceGetAttribute(&wall, hipDeviceAttributeWallClockRate, device) != hipSuccess) {
+    (void)hipGetLastError();
+    wall = 0;
+  }
+  h->wall_clock_khz = wall;
   strncpy(h->arch, prop.gcnArchName, sizeof(h->arch) - 1);
   *out = h;
   return GEMM_OK;
@@ -338,9 +347,7 @@ gemm_status_t run_impl(gemm_handle_t h, gemm_kernel_t kernel, void* stream, cons
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (kernel == GEMM_KERNEL_SIMT) {
-    if ((a.M + 15) / 16 > 65535) return GEMM_ERR_UNSUPPORTED;
-    p.tiles_m = (int)((a.M + 15) / 16);
-    p.tiles_n = (int)((a.N + 15) / 16);
+    // any M and N: the scalar kernel strides over its tiles with a bounded grid
     DeviceGuard g(h->device);
     err = tgemm::launch_simt(p, a.at, a.bt, a.transA, a.transB, s);
   } else if ((kernel >= GEMM_KERNEL_MFMA_64 && kernel <= GEMM_KERNEL_MFMA_256) ||
@@ -463,6 +470,39 @@ gemm_status_t gemm_bias_gelu(gemm_handle_t h, void* stream, int64_t M, int64_t N
   DeviceGuard g(h->device);
   const hipError_t err = tgemm::launch_bias_gelu(C, ldc, (int)M, (int)N, c_type, bias, epilogue,
                                                  h->cu_count, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+gemm_status_t gemm_probe_clock(gemm_handle_t h, void* stream, uint64_t* out, int workgroups,
+                               int microseconds) {
+  if (!valid(h)) return GEMM_ERR_INVALID_HANDLE;
+  if (!out || workgroups <= 0 || workgroups > 65536 || microseconds <= 0 || microseconds > 100000)
+    return GEMM_ERR_INVALID_VALUE;
+  if (h->wall_clock_khz <= 0) return GEMM_ERR_DEVICE;
+  const uint64_t ticks = (uint64_t)h->wall_clock_khz * (uint64_t)microseconds / 1000u;
+  DeviceGuard g(h->device);
+  const hipError_t err = tgemm::launch_clock_probe(out, workgroups, ticks ? ticks : 1,
+                                                   static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+int gemm_wall_clock_khz(gemm_handle_t h) {
+  if (!valid(h)) return GEMM_ERR_INVALID_HANDLE;
+  return h->wall_clock_khz;
+}
+
+gemm_status_t gemm_probe_bandwidth(gemm_handle_t h, void* stream, const void* src, void* dst,
+                                   int64_t bytes, uint32_t* sink) {
+  if (!valid(h)) return GEMM_ERR_INVALID_HANDLE;
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (!src || bytes <= 0 || bytes % 16 != 0 || !al16(src) || (dst && !al16(dst)))
+    return GEMM_ERR_INVALID_VALUE;
+  if (!dst && !sink) return GEMM_ERR_INVALID_VALUE;
+  if (dst && overlaps(byte_range(src, 1, bytes, bytes, 8), byte_range(dst, 1, bytes, bytes, 8)))
+    return GEMM_ERR_ALIAS;
+  DeviceGuard g(h->device);
+  const hipError_t err = tgemm::launch_bandwidth_probe(src, dst, bytes, sink, h->cu_count,
+                                                       static_cast<hipStream_t>(stream));
   return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 

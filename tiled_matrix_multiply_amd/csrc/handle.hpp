@@ -10,6 +10,7 @@ struct gemm_handle {
   uint32_t magic;
   int device;
   int cu_count;
+  int wall_clock_khz;  // rate of the constant-rate counter (s_memrealtime)
   char arch[64];
 };
 

@@ -172,6 +172,21 @@ class Cell:
             self.B.data_ptr(), p.ldb, self.C.data_ptr(), p.ldc, dt[p.a_type], dt[p.b_type],
             dt[p.c_type], epi, args[-1])]
         run = tmm.library().gemm_run
+        # A workspace, when the library would use one for these arguments (the K loop of
+        # mid-size 16-bit products split across workgroups): allocated and zeroed once, here,
+        # outside every timed region.
+        self.ws = None
+        self.ws_bytes = 0
+        if not p.mx:
+            need = tmm.gemm_workspace_bytes(h, *args[:5], args[6], args[7], args[9], args[10],
+                                            args[13], args[14], args[15], args[16], args[17],
+                                            epi, args[-1])
+            if need > 0:
+                self.ws_bytes = need
+                self.ws = torch.zeros(need // 4, dtype=torch.int32, device="cuda:0")
+                args = args + (self.ws.data_ptr(), need)
+                run = tmm.library().gemm_run_ws
+                self.kernel = "mfma256x128_sk2"
         if p.mx:
             # OCP MX block scales: one E8M0 byte per 32 k of each row of op(A) / column of op(B)
             self.sa, self.sb = dev(p.sa_blk), dev(p.sb_blk)

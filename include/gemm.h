@@ -109,10 +109,15 @@ typedef enum gemm_kernel {
                                bound by the bandwidth of the weight codes */
   GEMM_KERNEL_QMFMA = 6,    /* gemm_run_q only: matrix-core kernel that dequantises the codes
                                in registers (prefill) */
-  GEMM_KERNEL_MFMA_32 = 7   /* matrix-core kernel, 32x32 workgroup tile, 4 wavefronts that
+  GEMM_KERNEL_MFMA_32 = 7,  /* matrix-core kernel, 32x32 workgroup tile, 4 wavefronts that
                                split the K loop four ways; fp32, fp16 and bf16 only (other
                                types return GEMM_ERR_UNSUPPORTED).  AUTO takes it when 64x64
                                tiles would leave three quarters of the compute units idle */
+  GEMM_KERNEL_MFMA_256x128 = 8,     /* matrix-core kernel, 256x128 workgroup tile, 8 wavefronts
+                                       of 64x64; fp16 and bf16 only */
+  GEMM_KERNEL_MFMA_256x128_SK2 = 9  /* the 256x128 tile with its K loop split across two
+                                       workgroups that meet through a workspace: gemm_run_ws /
+                                       gemm_run_ws_kernel only; fp16 and bf16 only */
 } gemm_kernel_t;
 
 typedef struct gemm_handle* gemm_handle_t;
@@ -156,6 +161,57 @@ GEMM_API gemm_status_t gemm_run_kernel(gemm_handle_t h, gemm_kernel_t kernel, vo
                               int64_t ldb, float scale_b, float beta, void* C, int64_t ldc,
                               gemm_dtype_t a_type, gemm_dtype_t b_type, gemm_dtype_t c_type,
                               uint32_t epilogue, const float* bias);
+
+/* gemm_run with a caller-provided device workspace, for kernels that split the K loop across
+ * workgroups (the mid-size regime, fewer output tiles than compute units, where "Rigel"
+ * (arXiv 2606.12765), section 3, finds small sizes clock- and latency-bound).  The split kernel,
+ * GEMM_KERNEL_MFMA_256x128_SK2: each 256 x 128 tile's two workgroups multiply one half of K each;
+ * the first to finish writes its fp32 partial sums into the workspace and raises a per-tile
+ * flag, the second waits for that flag (a wait only ever for a workgroup already past its K
+ * loop), adds the partial sums and runs the epilogue.  The result does not depend on which
+ * finishes first (fp32 addition is commutative).  With GEMM_KERNEL_AUTO the library currently
+ * picks the split for no argument set (it measured slower than the 128 x 128 tile with its K
+ * loop split inside the workgroup at every mid size tried, 1536^3 to 2048 x 2048 x 4096), so
+ * gemm_run_ws with AUTO runs exactly as gemm_run and gemm_workspace_bytes reports 0; the split
+ * kernel is taken when named (gemm_run_ws_kernel).
+ *   workspace: DEVICE memory owned by the caller, 256-byte aligned, workspace_bytes long
+ *     (gemm_workspace_bytes gives the size a call needs; NULL with 0 bytes is allowed).  It must
+ *     be zero-filled before its first use; every call leaves it ready for the next (its
+ *     per-tile counters even, its flags at half the counters), so it is filled once, not per
+ *     call.  Calls that share a workspace must not overlap (one stream, or synchronised);
+ *     overlapping calls race on it.
+ * Errors as gemm_run, plus GEMM_ERR_INVALID_VALUE for a negative workspace_bytes, a NULL
+ * workspace with workspace_bytes > 0, or a workspace not aligned to 256 bytes. */
+GEMM_API gemm_status_t gemm_run_ws(gemm_handle_t h, void* stream, int64_t M, int64_t N,
+                                   int64_t K, int transA, int transB, float alpha,
+                                   const void* A, int64_t lda, float scale_a, const void* B,
+                                   int64_t ldb, float scale_b, float beta, void* C, int64_t ldc,
+                                   gemm_dtype_t a_type, gemm_dtype_t b_type, gemm_dtype_t c_type,
+                                   uint32_t epilogue, const float* bias, void* workspace,
+                                   int64_t workspace_bytes);
+
+/* gemm_run_ws with an explicit kernel family.  GEMM_KERNEL_MFMA_256x128_SK2 takes any M, N, K
+ * of fp16 / bf16 inputs that the matrix-core kernels accept, with a workspace of at least 8
+ * bytes per 256 x 128 output tile (rounded up to a multiple of 256) plus 131072 bytes per tile
+ * (GEMM_ERR_INVALID_VALUE otherwise); the other families ignore the workspace. */
+GEMM_API gemm_status_t gemm_run_ws_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* stream,
+                                          int64_t M, int64_t N, int64_t K, int transA,
+                                          int transB, float alpha, const void* A, int64_t lda,
+                                          float scale_a, const void* B, int64_t ldb,
+                                          float scale_b, float beta, void* C, int64_t ldc,
+                                          gemm_dtype_t a_type, gemm_dtype_t b_type,
+                                          gemm_dtype_t c_type, uint32_t epilogue,
+                                          const float* bias, void* workspace,
+                                          int64_t workspace_bytes);
+
+/* Workspace bytes gemm_run_ws (AUTO) would use for these arguments: 0 when it would not split
+ * the K loop (currently always), else 8 per 256 x 128 output tile (rounded up to 256) plus 131072
+ * per tile.  Negative status for invalid arguments (as gemm_check_args) or an invalid handle. */
+GEMM_API int64_t gemm_workspace_bytes(gemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                      int transA, int transB, const void* A, int64_t lda,
+                                      const void* B, int64_t ldb, const void* C, int64_t ldc,
+                                      gemm_dtype_t a_type, gemm_dtype_t b_type,
+                                      gemm_dtype_t c_type, uint32_t epilogue, const float* bias);
 
 /* Block-scaled GEMM in the OCP microscaling (MX) formats: every run of 32 consecutive k of a
  * row of op(A) and of a column of op(B) shares one E8M0 scale byte e, worth 2^(e - 127)

@@ -42,7 +42,8 @@ class Device:
         self.C.copy_(to_device(self.p.C, self.C.device))
 
 
-def run(g, p: W.Problem, kernel: int = 0, dev: Device | None = None, epilogue=None):
+def run(g, p: W.Problem, kernel: int = 0, dev: Device | None = None, epilogue=None,
+        workspace=None, workspace_bytes: int = 0):
     """Run on the GPU; returns (stored C bytes as numpy, decoded float64 C)."""
     import torch
     import tiled_matrix_multiply_amd as tmm
@@ -51,7 +52,8 @@ def run(g, p: W.Problem, kernel: int = 0, dev: Device | None = None, epilogue=No
             alpha=p.alpha, beta=p.beta, a_type=p.a_type, b_type=p.b_type, c_type=p.c_type,
             epilogue=p.epilogue if epilogue is None else epilogue, bias=d.bias,
             scale_a=p.scale_a, scale_b=p.scale_b, sa_blk=d.sa, sb_blk=d.sb,
-            ldsa=p.ldsa or None, ldsb=p.ldsb or None, kernel=kernel)
+            ldsa=p.ldsa or None, ldsb=p.ldsb or None, kernel=kernel, workspace=workspace,
+            workspace_bytes=workspace_bytes)
     torch.cuda.synchronize()
     raw = from_device(d.C, p.c_type)
     return raw, oracle.decode(p.c_type, raw)
@@ -131,7 +133,8 @@ def aligned_ld(width: int, mult: int = 16) -> int:
     return ((width + mult - 1) // mult) * mult + mult
 
 
-def run_padded(g, p: W.Problem, ld_fn=aligned_ld, kernel: int = 0):
+def run_padded(g, p: W.Problem, ld_fn=aligned_ld, kernel: int = 0, workspace=None,
+               workspace_bytes: int = 0):
     """Run with padded leading dimensions (padding poisoned with NaN).  Returns the decoded
     logical C, the kernel family gemm_run picked, and whether C's padding came back intact."""
     import torch
@@ -159,7 +162,8 @@ def run_padded(g, p: W.Problem, ld_fn=aligned_ld, kernel: int = 0):
     tmm.run(g.handle, A, B, C, M=p.M, N=p.N, K=p.K, trans_a=p.trans_a, trans_b=p.trans_b,
             alpha=p.alpha, beta=p.beta, a_type=p.a_type, b_type=p.b_type, c_type=p.c_type,
             epilogue=p.epilogue, bias=bias, scale_a=p.scale_a, scale_b=p.scale_b, lda=lda,
-            ldb=ldb, ldc=ldc, sa_blk=sa, sb_blk=sb, ldsa=ldsa, ldsb=ldsb, kernel=kernel)
+            ldb=ldb, ldc=ldc, sa_blk=sa, sb_blk=sb, ldsa=ldsa, ldsb=ldsb, kernel=kernel,
+            workspace=workspace, workspace_bytes=workspace_bytes)
     torch.cuda.synchronize()
     raw = from_device(C, p.c_type)
     pad_ok = bool(np.array_equal(raw.view(np.uint8).reshape(p.M, -1)[:, p.N * W.ESIZE[p.c_type]:],

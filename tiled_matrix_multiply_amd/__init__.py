@@ -45,15 +45,18 @@ GEMM_KERNEL_MFMA_256 = 4
 GEMM_KERNEL_QGEMV = 5
 GEMM_KERNEL_QMFMA = 6
 GEMM_KERNEL_MFMA_32 = 7
+GEMM_KERNEL_MFMA_256x128 = 8
+GEMM_KERNEL_MFMA_256x128_SK2 = 9
 KERNEL_NAME = {0: "auto", 1: "simt", 2: "mfma64", 3: "mfma128", 4: "mfma256", 5: "qgemv",
-               6: "qmfma", 7: "mfma32"}
+               6: "qmfma", 7: "mfma32", 8: "mfma256x128", 9: "mfma256x128_sk2"}
 
 # Every symbol include/gemm.h declares.
 EXPORTS = ("gemm_create", "gemm_destroy", "gemm_check_args", "gemm_run", "gemm_run_kernel",
            "gemm_run_mx", "gemm_run_mx_kernel", "gemm_check_args_mx", "gemm_select_kernel",
            "gemm_bias_gelu", "gemm_status_string", "gemm_run_q", "gemm_run_q_kernel",
            "gemm_check_args_q", "gemm_select_kernel_q", "gemm_probe_clock",
-           "gemm_wall_clock_khz", "gemm_probe_bandwidth")
+           "gemm_wall_clock_khz", "gemm_probe_bandwidth", "gemm_run_ws", "gemm_run_ws_kernel",
+           "gemm_workspace_bytes")
 
 # libgemm.so must resolve its libamdhip64.so.7 dependency to the HIP runtime instance that owns
 # the caller's device pointers and streams.  PyTorch ships its own runtime (soname
@@ -116,6 +119,13 @@ _lib.gemm_check_args_q.argtypes = _QCHK
 _lib.gemm_check_args_q.restype = _int
 _lib.gemm_select_kernel_q.argtypes = [_vp] + _QCHK
 _lib.gemm_select_kernel_q.restype = _int
+_lib.gemm_run_ws.argtypes = [_vp, _vp] + _RUN + [_vp, _i64]
+_lib.gemm_run_ws.restype = _int
+_lib.gemm_run_ws_kernel.argtypes = [_vp, _int, _vp] + _RUN + [_vp, _i64]
+_lib.gemm_run_ws_kernel.restype = _int
+_lib.gemm_workspace_bytes.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _i64,
+                                      _vp, _i64, _int, _int, _int, _u32, _vp]
+_lib.gemm_workspace_bytes.restype = _i64
 _lib.gemm_probe_clock.argtypes = [_vp, _vp, _vp, _int, _int]
 _lib.gemm_probe_clock.restype = _int
 _lib.gemm_wall_clock_khz.argtypes = [_vp]
@@ -237,6 +247,37 @@ def gemm_select_kernel_q(handle, M, N, K, X, ldx, Wq, ldw, bits, group, scales, 
                                      offsets, ldg, C, ldc, x_type, epilogue, bias)
 
 
+def gemm_run_ws(handle, stream, M, N, K, transA, transB, alpha, A, lda, scale_a, B, ldb,
+                scale_b, beta, C, ldc, a_type, b_type, c_type, epilogue, bias, workspace,
+                workspace_bytes) -> int:
+    """Raw entry point with a device workspace: returns the status code (no exception)."""
+    return _lib.gemm_run_ws(handle, stream, M, N, K, transA, transB, alpha, A, lda, scale_a, B,
+                            ldb, scale_b, beta, C, ldc, a_type, b_type, c_type, epilogue, bias,
+                            workspace, workspace_bytes)
+
+
+def gemm_run_ws_kernel(handle, kernel, stream, M, N, K, transA, transB, alpha, A, lda, scale_a,
+                       B, ldb, scale_b, beta, C, ldc, a_type, b_type, c_type, epilogue, bias,
+                       workspace, workspace_bytes) -> int:
+    return _lib.gemm_run_ws_kernel(handle, kernel, stream, M, N, K, transA, transB, alpha, A,
+                                   lda, scale_a, B, ldb, scale_b, beta, C, ldc, a_type, b_type,
+                                   c_type, epilogue, bias, workspace, workspace_bytes)
+
+
+def gemm_workspace_bytes(handle, M, N, K, transA, transB, A, lda, B, ldb, C, ldc, a_type,
+                         b_type, c_type, epilogue, bias) -> int:
+    return _lib.gemm_workspace_bytes(handle, M, N, K, transA, transB, A, lda, B, ldb, C, ldc,
+                                     a_type, b_type, c_type, epilogue, bias)
+
+
+def split_k_workspace_bytes(M: int, N: int) -> int:
+    """Workspace the K-split kernel (GEMM_KERNEL_MFMA_256x128_SK2) needs for an M x N output,
+    as include/gemm.h states it: 8 bytes per 256 x 128 tile rounded up to 256, plus 131072 bytes
+    per tile."""
+    t = -(-M // 256) * -(-N // 128)
+    return -(-8 * t // 256) * 256 + t * 131072
+
+
 def gemm_probe_clock(handle, stream, out, workgroups, microseconds) -> int:
     return _lib.gemm_probe_clock(handle, stream, out, workgroups, microseconds)
 
@@ -268,7 +309,7 @@ def _ptr(t):
 def run(handle, A, B, C, *, M, N, K, trans_a=False, trans_b=False, alpha=1.0, beta=0.0,
         a_type="f32", b_type=None, c_type=None, epilogue=GEMM_EPI_NONE, bias=None, scale_a=1.0,
         scale_b=1.0, lda=None, ldb=None, ldc=None, sa_blk=None, sb_blk=None, ldsa=None,
-        ldsb=None, kernel=GEMM_KERNEL_AUTO, stream=None):
+        ldsb=None, kernel=GEMM_KERNEL_AUTO, stream=None, workspace=None, workspace_bytes=0):
     """GEMM on device tensors holding storage words (A, B, C contiguous row-major unless ld*
     is given; E2M1 holds two elements per byte, E2M3 / E3M2 four per three bytes).  With
     sa_blk / sb_blk (device uint8 tensors of E8M0 scales, M x ldsa and N x ldsb) the call is
@@ -289,6 +330,13 @@ def run(handle, A, B, C, *, M, N, K, trans_a=False, trans_b=False, alpha=1.0, be
                                 DTYPE[a_type], DTYPE[b_type], DTYPE[c_type], int(epilogue),
                                 _ptr(bias))
         where = "gemm_run_mx"
+    elif workspace is not None:
+        st = gemm_run_ws_kernel(handle, kernel, _stream(stream), M, N, K, int(trans_a),
+                                int(trans_b), float(alpha), _ptr(A), lda, float(scale_a),
+                                _ptr(B), ldb, float(scale_b), float(beta), _ptr(C), ldc,
+                                DTYPE[a_type], DTYPE[b_type], DTYPE[c_type], int(epilogue),
+                                _ptr(bias), _ptr(workspace), int(workspace_bytes))
+        where = "gemm_run_ws"
     else:
         st = gemm_run_kernel(handle, kernel, _stream(stream), M, N, K, int(trans_a),
                              int(trans_b), float(alpha), _ptr(A), lda, float(scale_a), _ptr(B),

@@ -218,6 +218,30 @@ gemm_kernel_t auto_kernel(const Args& a, int cu_count) {
   return GEMM_KERNEL_MFMA_64;
 }
 
+// The K loop split across two workgroups (256 x 128 tiles, 16-bit inputs, GEMM_KERNEL_MFMA_256x128_SK2)
+// was built for mid-size products, whose 128 x 128 tiles give each compute unit one workgroup
+// walking the whole K loop.  Measured per launch (one box, back to back), against the 128 x 128
+// tile with its K loop split inside the workgroup that AUTO picks:
+//   fp16 2048^3              22.2 us   split 26.7 us   (256 x 128 unsplit, 128 workgroups: 30.6 us)
+//   bf16 + bias + GELU 2048^3 25.6 us  split 30.9 us
+//   bf16 + bias + GELU 1536^3 20.5 us  split 25.3 us
+//   bf16 + bias + GELU 2048 x 2048 x 4096   41.9 us   split 45.3 us
+//   bf16 + bias + GELU 1024 x 2048 x 2048   19.2 us   split 28.3 us
+// The hand-off of 128 KiB of partial sums per tile through device-coherent memory, plus the
+// second half's wait, costs about what the halved K loop saves, so AUTO does not take it; it
+// stays available as an explicit kernel family (gemm_run_ws_kernel).
+bool split_k_fits(const Args& a) {
+  return (a.at == GEMM_F16 || a.at == GEMM_BF16) && !a.mx;
+}
+int64_t split_k_tiles(const Args& a) { return ((a.M + 255) / 256) * ((a.N + 127) / 128); }
+bool split_k_wins(const Args&, int) { return false; }
+// Workspace of the split kernel: per tile a [counter, flag] pair of 32-bit words, then (from
+// the next 256-byte boundary) one 256 x 128 fp32 tile of partial sums.
+int64_t split_k_sync_bytes(const Args& a) { return ((8 * split_k_tiles(a) + 255) / 256) * 256; }
+int64_t split_k_ws_bytes(const Args& a) {
+  return split_k_sync_bytes(a) + split_k_tiles(a) * 256 * 128 * 4;
+}
+
 using tgemm::DeviceGuard;
 
 }  // namespace
@@ -315,12 +339,21 @@ Launcher f8_launcher(gemm_dtype_t at, gemm_dtype_t bt, bool mx) {
 }
 
 gemm_status_t run_impl(gemm_handle_t h, gemm_kernel_t kernel, void* stream, const Args& a,
-                       float alpha, float scale_a, float scale_b, float beta, void* C) {
+                       float alpha, float scale_a, float scale_b, float beta, void* C,
+                       void* ws = nullptr, int64_t ws_bytes = 0) {
   if (!valid(h)) return GEMM_ERR_INVALID_HANDLE;
   gemm_status_t st = check(a);
   if (st != GEMM_OK) return st;
+  if (ws_bytes < 0 || (ws_bytes > 0 && !ws)) return GEMM_ERR_INVALID_VALUE;
+  if (ws && (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return GEMM_ERR_INVALID_VALUE;
   if (a.M == 0 || a.N == 0) return GEMM_OK;
-  if (kernel == GEMM_KERNEL_AUTO) kernel = auto_kernel(a, h->cu_count);
+  if (kernel == GEMM_KERNEL_AUTO) {
+    kernel = auto_kernel(a, h->cu_count);
+    // with a workspace large enough, mid-size 16-bit products split K over two workgroups
+    if (ws && kernel != GEMM_KERNEL_SIMT && split_k_wins(a, h->cu_count) &&
+        ws_bytes >= split_k_ws_bytes(a))
+      kernel = GEMM_KERNEL_MFMA_256x128_SK2;
+  }
 
   tgemm::GemmParams p{};
   p.A = a.A;
@@ -351,14 +384,26 @@ gemm_status_t run_impl(gemm_handle_t h, gemm_kernel_t kernel, void* stream, cons
     DeviceGuard g(h->device);
     err = tgemm::launch_simt(p, a.at, a.bt, a.transA, a.transB, s);
   } else if ((kernel >= GEMM_KERNEL_MFMA_64 && kernel <= GEMM_KERNEL_MFMA_256) ||
-             kernel == GEMM_KERNEL_MFMA_32) {
+             kernel == GEMM_KERNEL_MFMA_32 || kernel == GEMM_KERNEL_MFMA_256x128 ||
+             kernel == GEMM_KERNEL_MFMA_256x128_SK2) {
     if (!mfma_aligned(a)) return GEMM_ERR_UNSUPPORTED;
     if (kernel == GEMM_KERNEL_MFMA_32 && a.at != GEMM_F32 && a.at != GEMM_F16 && a.at != GEMM_BF16)
       return GEMM_ERR_UNSUPPORTED;
-    const int tile = kernel == GEMM_KERNEL_MFMA_32 ? 3 : kernel - GEMM_KERNEL_MFMA_64;
-    const int t = kernel == GEMM_KERNEL_MFMA_32 ? 32 : 64 << tile;
-    const int64_t tm = (a.M + t - 1) / t, tn = (a.N + t - 1) / t;
-    if (tm * tn > kMaxDim) return GEMM_ERR_UNSUPPORTED;
+    const bool wide = kernel == GEMM_KERNEL_MFMA_256x128 || kernel == GEMM_KERNEL_MFMA_256x128_SK2;
+    if (wide && !split_k_fits(a)) return GEMM_ERR_UNSUPPORTED;
+    if (kernel == GEMM_KERNEL_MFMA_256x128_SK2) {
+      if (!ws || ws_bytes < split_k_ws_bytes(a)) return GEMM_ERR_INVALID_VALUE;
+      p.sk_sync = static_cast<uint32_t*>(ws);
+      p.sk_part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + split_k_sync_bytes(a));
+    }
+    const int tile = kernel == GEMM_KERNEL_MFMA_32 ? 3
+                     : kernel == GEMM_KERNEL_MFMA_256x128 ? 5
+                     : kernel == GEMM_KERNEL_MFMA_256x128_SK2 ? 6
+                     : kernel - GEMM_KERNEL_MFMA_64;
+    const int tmr = kernel == GEMM_KERNEL_MFMA_32 ? 32 : wide ? 256 : 64 << tile;
+    const int tnc = wide ? 128 : tmr;
+    const int64_t tm = (a.M + tmr - 1) / tmr, tn = (a.N + tnc - 1) / tnc;
+    if (tm * tn * 2 > kMaxDim) return GEMM_ERR_UNSUPPORTED;
     p.tiles_m = (int)tm;
     p.tiles_n = (int)tn;
     if (a.at == GEMM_E2M1) {
@@ -407,6 +452,45 @@ gemm_status_t gemm_run_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* strea
   const Args a{M, N, K, transA, transB, A, lda, B, ldb, C, ldc, a_type, b_type, c_type,
                epilogue, bias};
   return run_impl(h, kernel, stream, a, alpha, scale_a, scale_b, beta, C);
+}
+
+gemm_status_t gemm_run_ws_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* stream, int64_t M,
+                                 int64_t N, int64_t K, int transA, int transB, float alpha,
+                                 const void* A, int64_t lda, float scale_a, const void* B,
+                                 int64_t ldb, float scale_b, float beta, void* C, int64_t ldc,
+                                 gemm_dtype_t a_type, gemm_dtype_t b_type, gemm_dtype_t c_type,
+                                 uint32_t epilogue, const float* bias, void* workspace,
+                                 int64_t workspace_bytes) {
+  const Args a{M, N, K, transA, transB, A, lda, B, ldb, C, ldc, a_type, b_type, c_type,
+               epilogue, bias};
+  return run_impl(h, kernel, stream, a, alpha, scale_a, scale_b, beta, C, workspace,
+                  workspace_bytes);
+}
+
+gemm_status_t gemm_run_ws(gemm_handle_t h, void* stream, int64_t M, int64_t N, int64_t K,
+                          int transA, int transB, float alpha, const void* A, int64_t lda,
+                          float scale_a, const void* B, int64_t ldb, float scale_b, float beta,
+                          void* C, int64_t ldc, gemm_dtype_t a_type, gemm_dtype_t b_type,
+                          gemm_dtype_t c_type, uint32_t epilogue, const float* bias,
+                          void* workspace, int64_t workspace_bytes) {
+  return gemm_run_ws_kernel(h, GEMM_KERNEL_AUTO, stream, M, N, K, transA, transB, alpha, A, lda,
+                            scale_a, B, ldb, scale_b, beta, C, ldc, a_type, b_type, c_type,
+                            epilogue, bias, workspace, workspace_bytes);
+}
+
+int64_t gemm_workspace_bytes(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int transA,
+                             int transB, const void* A, int64_t lda, const void* B, int64_t ldb,
+                             const void* C, int64_t ldc, gemm_dtype_t a_type, gemm_dtype_t b_type,
+                             gemm_dtype_t c_type, uint32_t epilogue, const float* bias) {
+  if (!valid(h)) return GEMM_ERR_INVALID_HANDLE;
+  const Args a{M, N, K, transA, transB, A, lda, B, ldb, C, ldc, a_type, b_type, c_type,
+               epilogue, bias};
+  const gemm_status_t st = check(a);
+  if (st != GEMM_OK) return st;
+  if (a.M == 0 || a.N == 0 || auto_kernel(a, h->cu_count) == GEMM_KERNEL_SIMT ||
+      !split_k_wins(a, h->cu_count))
+    return 0;
+  return split_k_ws_bytes(a);
 }
 
 gemm_status_t gemm_run_mx_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* stream, int64_t M,

@@ -37,6 +37,10 @@ struct GemmParams {
   const void* qo;
   int64_t ldg;
   int group;
+  // K loop split across two workgroups: per tile a [counter, flag] pair of words and the
+  // first workgroup's fp32 accumulators (BM x BN floats).  Null otherwise.
+  uint32_t* sk_sync;
+  float* sk_part;
 };
 
 template <int DT> struct DTypeInfo;

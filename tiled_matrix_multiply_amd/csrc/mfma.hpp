@@ -39,6 +39,7 @@
 namespace tgemm {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -199,9 +200,13 @@ constexpr int default_stages() { return TILE == 128 ? 3 : 2; }
 // K-contiguous 16-bit B).  KS_: K split inside the workgroup: KS_ groups of WM_ x WN_ waves
 // each walk every KS_-th K tile with their own LDS stages and add their accumulators at the
 // end (small problems, whose time is the chain of K tiles rather than the multiplies).
+// BN_: tile width along N (0: square, BN = TILE_).  SK_: the K loop split across workgroups,
+// 1 or 2: with 2, two workgroups share a tile, each multiplying one half of its K tiles; the
+// first to finish hands its fp32 accumulators to the other through a workspace in device memory
+// (a pair protocol, below), and the other adds them and runs the epilogue.
 template <int DT_, int TILE_, int WM_, int WN_, bool A_MN_, bool B_MN_,
           int S_ = default_stages<TILE_>(), int BT_ = DT_, bool MX_ = false, int QB_ = 0,
-          int KS_ = 1>
+          int KS_ = 1, int BN_ = 0, int SK_ = 1>
 struct MfmaCfg {
   static constexpr int DT = DT_, BT = BT_;
   static constexpr bool F8 = is_f8f6f4<DT_>(), MX = MX_;
@@ -209,8 +214,10 @@ struct MfmaCfg {
   static_assert(!MX_ || F8, "block scales only with 8- and 4-bit inputs");
   using Op = typename std::conditional<F8, MmaScaled<BT_, DT_>, MmaOp<DT_>>::type;
   static constexpr int CT = F8 ? BF16 : DT_;
-  static constexpr int BM = TILE_, BN = TILE_;
-  static constexpr int KS = KS_;
+  static constexpr int BM = TILE_, BN = BN_ ? BN_ : TILE_;
+  static constexpr int KS = KS_, SK = SK_;
+  static_assert(SK_ == 1 || (SK_ == 2 && KS_ == 1 && !MX_ && QB_ == 0),
+                "K split across workgroups: two halves, plain inputs, no split inside");
   static constexpr int WM = WM_, WN = WN_, NW = WM_ * WN_, NT = NW * 64 * KS_;  // NW waves per K group
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 accumulators per wave
@@ -339,9 +346,15 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   // Tile order.  Workgroups are dealt to the 8 XCDs round-robin by id; renumber so each XCD
   // receives a contiguous range, then walk tiles in groups of TILE_GROUP_M tile rows so the
   // tiles on one XCD share A and B panels in that XCD's L2.
+  // With the K loop split across workgroups, the SK workgroups of a tile get consecutive ids
+  // after the renumbering, so that both halves of a tile run on one XCD and meet in its L2.
   int bid = blockIdx.x;
   const int T = p.tiles_m * p.tiles_n;
-  if ((T & 7) == 0) bid = (bid & 7) * (T >> 3) + (bid >> 3);
+  const int U = T * C::SK;  // workgroups
+  if ((U & 7) == 0) bid = (bid & 7) * (U >> 3) + (bid >> 3);
+  const int khalf = C::SK > 1 ? bid % C::SK : 0;  // which part of the K tiles this workgroup takes
+  if constexpr (C::SK > 1) bid /= C::SK;
+  const int tile_id = bid;
   const int per_group = TILE_GROUP_M * p.tiles_n;
   const int first_m = (bid / per_group) * TILE_GROUP_M;
   const int gsz = min(p.tiles_m - first_m, TILE_GROUP_M);
@@ -733,10 +746,15 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   // K tiles.  With the K loop split, group kg takes tiles kg, kg + KS, ... (KT of them) in NI
   // iterations that every group runs, so that all reach the same barriers; the loop below
   // counts iterations, which are tiles when KS = 1.
+  // With the K loop split across workgroups (SK = 2), part h takes the K tiles
+  // [h KH, min((h+1) KH, KT_ALL)), KH = ceil(KT_ALL / 2).
   const int KT_ALL = (p.K + C::BKE - 1) / C::BKE;
-  const int NI = (KT_ALL + C::KS - 1) / C::KS;
-  const int KT = C::KS == 1 ? KT_ALL : (KT_ALL - kg + C::KS - 1) / C::KS;
-  auto tile_of = [&](int i) { return C::KS == 1 ? i : i * C::KS + kg; };
+  const int KH = (KT_ALL + C::SK - 1) / C::SK;
+  const int kbeg = khalf * KH;
+  const int KT_SK = C::SK > 1 ? max(0, min(KH, KT_ALL - kbeg)) : KT_ALL;
+  const int NI = C::KS == 1 ? KT_SK : (KT_ALL + C::KS - 1) / C::KS;
+  const int KT = C::KS == 1 ? KT_SK : (KT_ALL - kg + C::KS - 1) / C::KS;
+  auto tile_of = [&](int i) { return C::KS == 1 ? kbeg + i : i * C::KS + kg; };
   const bool need_fix = (p.epi & (FIX_A | FIX_B)) != 0;
   constexpr int NL = OA::PER_WAVE + (C::QB ? 0 : OB::PER_WAVE);  // data copies per wave per K tile
   constexpr int NWL = (C::BM + C::BN) / 64;         // 64-row scale wave-loads per chunk
@@ -974,6 +992,72 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
     }
   }
 
+  if constexpr (C::SK > 1) {
+    // K split across two workgroups: the pair protocol.  Per tile, a counter and a flag in the
+    // workspace (both zero before the first call; every call leaves the counter even and the
+    // flag at counter / 2).  The counter's old value decides the roles: even, this workgroup is
+    // first and publishes its fp32 accumulators; odd, it is second, waits for the first one's
+    // flag, adds them and runs the epilogue.  The wait is only ever for a workgroup that has
+    // already left its K loop (it took the counter first), whose remaining work is its stores
+    // and its flag, so it needs nothing else to run and the wait ends: no co-residency of the
+    // grid is assumed.  The spin is bounded all the same.  fp32 addition is commutative, so the
+    // result is the same whichever workgroup arrives first.
+    // Coherence across the compute units (and the XCDs, whose L2 caches are not coherent with
+    // one another) comes from the accesses themselves: the partial sums are stored and loaded
+    // at device scope (the sc1 cache policy: no stale line in a per-CU or per-XCD cache serves
+    // them), the stores are complete (vmcnt 0) before the flag is raised, and the flag and the
+    // counter are device-scope atomics.  That avoids a release / acquire fence, which here would
+    // write the whole L2 back and invalidate it under every workgroup still at work on the XCD.
+    __shared__ uint32_t sk_old;
+    uint32_t* const sync = p.sk_sync + 2 * (int64_t)tile_id;  // [counter, flag]
+    constexpr int NF = C::FM * C::FN * 4;                      // float4 pieces per lane
+    constexpr int DEVICE_SCOPE = 16;                           // sc1 cache-policy bit
+    const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
+        p.sk_part + (int64_t)tile_id * C::BM * C::BN, (short)0, C::BM * C::BN * 4, BUFFER_FLAGS);
+    const int pbase = (wave * NF * 64 + lane) * 16;            // this lane's first piece, bytes
+    __syncthreads();  // every wave has left the K loop
+    if (tid == 0) sk_old = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint32_t old = sk_old, round = (old >> 1) + 1u;
+    if ((old & 1u) == 0u) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), part,
+                                                   pbase + ((i * C::FN + j) * 4 + q) * 64 * 16, 0, DEVICE_SCOPE);
+          }
+      wait_vmcnt<0>();  // this wave's stores are complete
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(sync + 1, round, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    if (tid == 0) {
+      for (uint32_t n = 0; n < (1u << 22); ++n) {
+        if (__hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == round) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();  // the loads below are issued after the flag was seen
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(part, pbase + ((i * C::FN + j) * 4 + q) * 64 * 16, 0,
+                                                          DEVICE_SCOPE));
+          acc[i][j][4 * q] += v[0];
+          acc[i][j][4 * q + 1] += v[1];
+          acc[i][j][4 * q + 2] += v[2];
+          acc[i][j][4 * q + 3] += v[3];
+        }
+  }
+
   // Epilogue in registers.  Lane (lrow, lhalf) of accumulator (i, j) holds rows
   // m = m0 + wm*WTM + 32 i + lrow and, in register group rg, the 4 consecutive columns
   // n = n0 + wn*WTN + 32 j + 8 rg + 4 lhalf (+0..3).
@@ -1113,7 +1197,7 @@ hipError_t launch_mfma_cfg(GemmParams p, hipStream_t s) {
   const bool fix_a = C::A_MN ? (p.M % CE != 0) : (p.K % C::BKE != 0);
   const bool fix_b = C::B_MN ? (p.N % CE != 0) : (p.K % C::BKE != 0);
   p.epi |= (fix_a ? FIX_A : 0u) | (fix_b ? FIX_B : 0u);
-  hipLaunchKernelGGL((gemm_mfma_kernel<C>), dim3((unsigned)T), dim3(C::NT), 0, s, p);
+  hipLaunchKernelGGL((gemm_mfma_kernel<C>), dim3((unsigned)(T * C::SK)), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1123,17 +1207,17 @@ hipError_t launch_mfma_cfg(GemmParams p, hipStream_t s) {
 // family); MX: block-scaled.  Packed fp4 and 6-bit operands are staged K-contiguous only (A
 // stored M x K, B stored N x K): the other layouts return an error (the host never routes them
 // here).
-template <int DT, int TILE, int WM, int WN, int BT, bool MX, int KS = 1>
+template <int DT, int TILE, int WM, int WN, int BT, bool MX, int KS = 1, int BN = 0, int SK = 1>
 hipError_t launch_mfma_layout(const GemmParams& p, bool a_mn, bool b_mn, hipStream_t s) {
-  // a K split gives each group its own stages: two each
-  constexpr int S = KS > 1 ? 2 : default_stages<TILE>();
-  if (!a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, false, S, BT, MX, 0, KS>>(p, s);
+  // a K split gives each group its own stages: two each; the 256-row tiles keep two as well
+  constexpr int S = (KS > 1 || BN) ? 2 : default_stages<TILE>();
+  if (!a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, false, S, BT, MX, 0, KS, BN, SK>>(p, s);
   if constexpr (DT == E2M1 || is_fp6<DT>()) {
     return hipErrorInvalidValue;
   } else {
-    if (!a_mn && b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, true, S, BT, MX, 0, KS>>(p, s);
-    if (a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, true, false, S, BT, MX, 0, KS>>(p, s);
-    return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, true, true, S, BT, MX, 0, KS>>(p, s);
+    if (!a_mn && b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, false, true, S, BT, MX, 0, KS, BN, SK>>(p, s);
+    if (a_mn && !b_mn) return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, true, false, S, BT, MX, 0, KS, BN, SK>>(p, s);
+    return launch_mfma_cfg<MfmaCfg<DT, TILE, WM, WN, true, true, S, BT, MX, 0, KS, BN, SK>>(p, s);
   }
 }
 
@@ -1150,6 +1234,15 @@ hipError_t launch_mfma_dtype(const GemmParams& p, int tile, bool a_mn, bool b_mn
       return launch_mfma_layout<DT, 32, 1, 1, BT, MX, 4>(p, a_mn, b_mn, s);
     else
       return hipErrorInvalidValue;
+  }
+  if (tile == 5 || tile == 6) {  // 256 x 128, 4 x 2 waves of 64 x 64; 6: K split over two workgroups
+    if constexpr ((DT == F16 || DT == BF16) && !MX) {
+      if (ks != 1) return hipErrorInvalidValue;
+      if (tile == 6) return launch_mfma_layout<DT, 256, 4, 2, BT, MX, 1, 128, 2>(p, a_mn, b_mn, s);
+      return launch_mfma_layout<DT, 256, 4, 2, BT, MX, 1, 128, 1>(p, a_mn, b_mn, s);
+    } else {
+      return hipErrorInvalidValue;
+    }
   }
   if (ks != 1) return hipErrorInvalidValue;
   switch (tile) {

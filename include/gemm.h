@@ -74,7 +74,9 @@ typedef enum gemm_status {
   GEMM_ERR_DEVICE = -5,         /* no such device, device is not gfx950, or a HIP error at
                                    gemm_create */
   GEMM_ERR_LAUNCH = -6,         /* the kernel launch itself failed (hipGetLastError) */
-  GEMM_ERR_NO_MEMORY = -7       /* host allocation of the handle failed */
+  GEMM_ERR_NO_MEMORY = -7,      /* host allocation of the handle failed */
+  GEMM_ERR_TOO_LARGE = -8       /* gemm_run_noalloc: the problem needs more scratch than the
+                                   library's static buffer holds */
 } gemm_status_t;
 
 typedef enum gemm_dtype {
@@ -203,6 +205,27 @@ GEMM_API gemm_status_t gemm_run_ws_kernel(gemm_handle_t h, gemm_kernel_t kernel,
                                           gemm_dtype_t c_type, uint32_t epilogue,
                                           const float* bias, void* workspace,
                                           int64_t workspace_bytes);
+
+/* gemm_run_ws_kernel without a workspace argument and without any allocation, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is the library's own static device array, 16 MiB +
+ * 4 KiB per device, held from the time the library's code object loads on that device until
+ * the process ends, and addressed through the handle (gemm_create takes its address).  The
+ * kernel that uses it, GEMM_KERNEL_MFMA_256x128_SK2, therefore takes outputs of at most 128
+ * tiles of 256 x 128 (for example 2048 x 2048); a larger one returns GEMM_ERR_TOO_LARGE and
+ * enqueues nothing.  AUTO and the other kernel families use no scratch and run as
+ * gemm_run_kernel.  The array needs no clearing between calls (it starts zeroed and every
+ * call leaves it as the next one needs it), but it is shared by every call on its device:
+ * calls that overlap on one device (different streams, unsynchronised) race on it.  Errors as
+ * gemm_run_ws_kernel, plus GEMM_ERR_TOO_LARGE. */
+GEMM_API gemm_status_t gemm_run_noalloc(gemm_handle_t h, gemm_kernel_t kernel, void* stream,
+                                        int64_t M, int64_t N, int64_t K, int transA,
+                                        int transB, float alpha, const void* A, int64_t lda,
+                                        float scale_a, const void* B, int64_t ldb,
+                                        float scale_b, float beta, void* C, int64_t ldc,
+                                        gemm_dtype_t a_type, gemm_dtype_t b_type,
+                                        gemm_dtype_t c_type, uint32_t epilogue,
+                                        const float* bias);
 
 /* Workspace bytes gemm_run_ws (AUTO) would use for these arguments: 0 when it would not split
  * the K loop (currently always), else 8 per 256 x 128 output tile (rounded up to 256) plus 131072

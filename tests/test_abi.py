@@ -23,7 +23,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported():
     syms = declared_symbols()
-    assert len(syms) == 21, syms
+    assert len(syms) == 22, syms
     assert sorted(tmm.EXPORTS) == syms
     nm = subprocess.run(["nm", "-D", "--defined-only", tmm.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
@@ -44,7 +44,7 @@ def test_measurement_helpers_validate_without_a_gpu():
 
 
 def test_status_strings():
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = tmm.gemm_status_string(code)
         assert s.startswith("GEMM_")
     assert tmm.gemm_status_string(-99) == "GEMM_ERR_UNKNOWN"

@@ -25,6 +25,7 @@ GEMM_ERR_ALIAS = -4
 GEMM_ERR_DEVICE = -5
 GEMM_ERR_LAUNCH = -6
 GEMM_ERR_NO_MEMORY = -7
+GEMM_ERR_TOO_LARGE = -8
 
 # gemm_dtype_t
 GEMM_F32, GEMM_F16, GEMM_BF16, GEMM_E4M3, GEMM_E5M2, GEMM_E2M1 = 0, 1, 2, 3, 4, 5
@@ -56,7 +57,7 @@ EXPORTS = ("gemm_create", "gemm_destroy", "gemm_check_args", "gemm_run", "gemm_r
            "gemm_bias_gelu", "gemm_status_string", "gemm_run_q", "gemm_run_q_kernel",
            "gemm_check_args_q", "gemm_select_kernel_q", "gemm_probe_clock",
            "gemm_wall_clock_khz", "gemm_probe_bandwidth", "gemm_run_ws", "gemm_run_ws_kernel",
-           "gemm_workspace_bytes")
+           "gemm_workspace_bytes", "gemm_run_noalloc")
 
 # libgemm.so must resolve its libamdhip64.so.7 dependency to the HIP runtime instance that owns
 # the caller's device pointers and streams.  PyTorch ships its own runtime (soname
@@ -123,6 +124,8 @@ _lib.gemm_run_ws.argtypes = [_vp, _vp] + _RUN + [_vp, _i64]
 _lib.gemm_run_ws.restype = _int
 _lib.gemm_run_ws_kernel.argtypes = [_vp, _int, _vp] + _RUN + [_vp, _i64]
 _lib.gemm_run_ws_kernel.restype = _int
+_lib.gemm_run_noalloc.argtypes = [_vp, _int, _vp] + _RUN
+_lib.gemm_run_noalloc.restype = _int
 _lib.gemm_workspace_bytes.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _i64,
                                       _vp, _i64, _int, _int, _int, _u32, _vp]
 _lib.gemm_workspace_bytes.restype = _i64
@@ -262,6 +265,15 @@ def gemm_run_ws_kernel(handle, kernel, stream, M, N, K, transA, transB, alpha, A
     return _lib.gemm_run_ws_kernel(handle, kernel, stream, M, N, K, transA, transB, alpha, A,
                                    lda, scale_a, B, ldb, scale_b, beta, C, ldc, a_type, b_type,
                                    c_type, epilogue, bias, workspace, workspace_bytes)
+
+
+def gemm_run_noalloc(handle, kernel, stream, M, N, K, transA, transB, alpha, A, lda, scale_a,
+                     B, ldb, scale_b, beta, C, ldc, a_type, b_type, c_type, epilogue,
+                     bias) -> int:
+    """Raw entry point with the library's static scratch as workspace (no allocation)."""
+    return _lib.gemm_run_noalloc(handle, kernel, stream, M, N, K, transA, transB, alpha, A, lda,
+                                 scale_a, B, ldb, scale_b, beta, C, ldc, a_type, b_type, c_type,
+                                 epilogue, bias)
 
 
 def gemm_workspace_bytes(handle, M, N, K, transA, transB, A, lda, B, ldb, C, ldc, a_type,

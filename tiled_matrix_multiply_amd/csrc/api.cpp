@@ -44,6 +44,8 @@ TGEMM_F8_LAUNCHER(mx_e3m2_e2m3)
 hipError_t launch_bias_gelu(void* C, int64_t ldc, int M, int N, int c_type, const float* bias,
                             uint32_t epi, int cu_count, hipStream_t s);
 hipError_t launch_clock_probe(uint64_t* out, int workgroups, uint64_t ticks, hipStream_t s);
+hipError_t scratch_address(void** out);
+int64_t scratch_bytes();
 hipError_t launch_bandwidth_probe(const void* src, void* dst, int64_t bytes, uint32_t* sink,
                                   int cu_count, hipStream_t s);
 }  // namespace tgemm
@@ -272,6 +274,18 @@ gemm_status_t gemm_create(gemm_handle_t* out, int device) {
     wall = 0;
   }
   h->wall_clock_khz = wall;
+  {
+    // the static scratch array's address on this device (for gemm_run_noalloc)
+    DeviceGuard g(device);
+    void* ptr = nullptr;
+    if (tgemm::scratch_address(&ptr) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      free(h);
+      return GEMM_ERR_DEVICE;
+    }
+    h->scratch = ptr;
+    h->scratch_bytes = tgemm::scratch_bytes();
+  }
   strncpy(h->arch, prop.gcnArchName, sizeof(h->arch) - 1);
   *out = h;
   return GEMM_OK;
@@ -467,6 +481,25 @@ gemm_status_t gemm_run_ws_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* st
                   workspace_bytes);
 }
 
+gemm_status_t gemm_run_noalloc(gemm_handle_t h, gemm_kernel_t kernel, void* stream, int64_t M,
+                               int64_t N, int64_t K, int transA, int transB, float alpha,
+                               const void* A, int64_t lda, float scale_a, const void* B,
+                               int64_t ldb, float scale_b, float beta, void* C, int64_t ldc,
+                               gemm_dtype_t a_type, gemm_dtype_t b_type, gemm_dtype_t c_type,
+                               uint32_t epilogue, const float* bias) {
+  if (!valid(h)) return GEMM_ERR_INVALID_HANDLE;
+  const Args a{M, N, K, transA, transB, A, lda, B, ldb, C, ldc, a_type, b_type, c_type,
+               epilogue, bias};
+  const gemm_status_t st = check(a);
+  if (st != GEMM_OK) return st;
+  // the one kernel that uses scratch: refuse what the static array cannot hold
+  if (kernel == GEMM_KERNEL_MFMA_256x128_SK2 && a.M > 0 && a.N > 0 &&
+      split_k_ws_bytes(a) > h->scratch_bytes)
+    return GEMM_ERR_TOO_LARGE;
+  return run_impl(h, kernel, stream, a, alpha, scale_a, scale_b, beta, C, h->scratch,
+                  h->scratch_bytes);
+}
+
 gemm_status_t gemm_run_ws(gemm_handle_t h, void* stream, int64_t M, int64_t N, int64_t K,
                           int transA, int transB, float alpha, const void* A, int64_t lda,
                           float scale_a, const void* B, int64_t ldb, float scale_b, float beta,
@@ -600,6 +633,8 @@ const char* gemm_status_string(gemm_status_t s) {
     case GEMM_ERR_DEVICE: return "GEMM_ERR_DEVICE: no gfx950 device";
     case GEMM_ERR_LAUNCH: return "GEMM_ERR_LAUNCH: kernel launch failed";
     case GEMM_ERR_NO_MEMORY: return "GEMM_ERR_NO_MEMORY: host allocation failed";
+    case GEMM_ERR_TOO_LARGE:
+      return "GEMM_ERR_TOO_LARGE: the problem needs more scratch than the library's static buffer holds";
     default: return "GEMM_ERR_UNKNOWN";
   }
 }

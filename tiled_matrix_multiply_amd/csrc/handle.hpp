@@ -11,6 +11,8 @@ struct gemm_handle {
   int device;
   int cu_count;
   int wall_clock_khz;  // rate of the constant-rate counter (s_memrealtime)
+  void* scratch;       // this device's copy of the library's static scratch array (device address)
+  int64_t scratch_bytes;
   char arch[64];
 };
 

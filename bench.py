@@ -442,29 +442,35 @@ def summarize(name, cell: Cell, ms: np.ndarray, dtype: str) -> dict:
            "pct_peak": round(100 * tf / PEAK_TFLOPS[dtype], 2),
            "gbs": round(cell.algorithmic_bytes() / (med * 1e-3) / 1e9, 1),
            "back_to_back_us": round(getattr(cell, "b2b_ms", float("nan")) * 1e3, 3),
-           "sclk_mhz": getattr(cell, "sclk", None)}
+           "sclk_after_run_mhz": getattr(cell, "sclk", None)}
     print(f"[bench] {name:34s} {cell.kernel:8s} {row['median_us']:10.2f} us  "
           f"{row['tflops']:8.1f} TFLOP/s  {row['pct_peak']:5.1f}% of {dtype} peak  "
           f"{row['gbs']:8.1f} GB/s  (back to back {row['back_to_back_us']:.2f} us)"
-          f"{'' if row['sclk_mhz'] is None else '  sclk %.0f MHz' % row['sclk_mhz']['mean']}",
+          f"{'' if row['sclk_after_run_mhz'] is None else '  sclk after %.0f MHz' % row['sclk_after_run_mhz']['mean']}",
           file=sys.stderr, flush=True)
     return row
 
 
-def read_traffic(src_hash: str):
-    """HBM bytes per launch from the committed counter summary, if it saw this source."""
+def read_counters(src_hash: str) -> dict:
+    """Figures from the committed counter summary of the headline kernel, if it saw this
+    source: HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size)
+    and the shader clock during the kernel (GRBM_GUI_ACTIVE cycles / 8 XCDs / duration)."""
+    out = {"traffic": None, "sclk_in_kernel_mhz": None, "mfma_busy": None}
     try:
         fields = {}
         with open(TRAFFIC_FILE) as fh:
             for line in fh:
                 if "=" in line and not line.startswith("#"):
                     k, v = line.split("=", 1)
-                    fields[k.strip()] = v.strip()
+                    fields[k.strip()] = v.split()[0] if v.split() else ""
         if fields.get("source_hash") != src_hash:
-            return None
-        return int(float(fields["hbm_bytes_per_launch"]))
+            return out
+        out["traffic"] = int(float(fields["hbm_bytes_per_launch"]))
+        out["sclk_in_kernel_mhz"] = float(fields["shader_clock_in_kernel_mhz"])
+        out["mfma_busy"] = float(fields["mfma_busy_fraction"])
     except (OSError, KeyError, ValueError):
-        return None
+        pass
+    return out
 
 
 def cpu_baseline(p, target_s: float) -> dict:
@@ -659,7 +665,8 @@ def main():
               flush=True)
         cpu = cpu_baseline(head_p, args.cpu_seconds)
 
-    traffic = read_traffic(src_hash)
+    counters = read_counters(src_hash)
+    kclk = counters["sclk_in_kernel_mhz"]
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -683,13 +690,19 @@ def main():
         "ci95_tflops": head_row["tflops_ci95"],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS["bf16"], 4), "traffic": traffic,
+                     "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": counters["traffic"],
                      "launch_period_us": round(period_ms * 1e3, 3),
                      "flops_per_launch": head_p.flops,
-                     "sclk_mhz": head_sclk,
-                     "frac_at_measured_sclk": (round(achieved / (PEAK_TFLOPS["bf16"] * head_sclk["mean"] / 2400.0), 4)
-                                               if head_sclk else None)},
-        "sclk_mhz": head_sclk["mean"] if head_sclk else None,
+                     # the clock the power controller held during the kernel (counter pass of
+                     # this source), and the frac against the peak at that clock
+                     "sclk_in_kernel_mhz": kclk,
+                     "frac_at_in_kernel_sclk": (round(achieved / (PEAK_TFLOPS["bf16"] * kclk / 2400.0), 4)
+                                                if kclk else None),
+                     "mfma_busy": counters["mfma_busy"],
+                     # a probe queued right behind a second run: the clock has recovered by then
+                     "sclk_after_run_mhz": head_sclk},
+        "sclk_after_run_mhz": head_sclk["mean"] if head_sclk else None,
         "hbm_copy_gbs": hbm["copy_gbs"] if hbm else None,
         "hbm_read_gbs": hbm["read_gbs"] if hbm else None,
         "hbm_ceiling": hbm,

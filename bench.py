@@ -75,9 +75,9 @@ class ClockProbe:
     """The shader clock a timed region left the chip at, read in-kernel: gemm_probe_clock
     enqueued on the same stream right behind the region's last launch, `workgroups` one-wave
     workgroups each timing `us` microseconds of the constant-rate counter against the
-    shader-clock cycle counter.  The published peaks assume 2.4 GHz; under sustained
-    matrix-core load the clock is held lower by power, so every fraction of peak is quoted
-    beside this reading."""
+    shader-clock cycle counter.  The clock recovers within microseconds once the matrix-core
+    load ends, so this reads the state between runs (near 2.4 GHz), not the power-held clock
+    during the kernel; that one comes from the counter summary (read_counters)."""
 
     def __init__(self, g, workgroups: int = 256, us: int = 40):
         import torch

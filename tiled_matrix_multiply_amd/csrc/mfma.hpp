@@ -219,6 +219,17 @@ struct MfmaCfg {
   static_assert(SK_ == 1 || (SK_ == 2 && KS_ == 1 && !MX_ && QB_ == 0),
                 "K split across workgroups: two halves, plain inputs, no split inside");
   static constexpr int WM = WM_, WN = WN_, NW = WM_ * WN_, NT = NW * 64 * KS_;  // NW waves per K group
+  // Waves that issue the K loop's copies.  The 256 x 256 tile runs two waves per SIMD; right
+  // after each barrier every wave would issue its copies at once, the address unit's queue
+  // fills, and both waves of a SIMD stall on it together while the matrix core idles.  So one
+  // wave per SIMD issues all of them (data and block scales), and the other keeps multiplying
+  // meanwhile: the dispatcher deals a workgroup's waves to the four SIMDs in turn, so waves
+  // 0 .. 3 sit on four different SIMDs and wave w + 4 shares wave w's (read from the hardware-ID
+  // register).  Measured at 4096 x 4096 x 8192: bf16 -1.8%, fp8 -3%, MXFP4 -3.5%, fused bf16
+  // + bias + GELU 4096^3 -2.5%; 6-bit inputs gain nothing (MXFP6 +3.5%), so they keep the copies
+  // on all waves, as does quantized B, whose code loads every thread issues.
+  static constexpr int NCW =
+      (TILE_ == 256 && BN_ == 0 && NW == 8 && KS_ == 1 && QB_ == 0 && !is_fp6<DT_>()) ? 4 : NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 accumulators per wave
   static constexpr int ES = DTypeInfo<DT_>::bytes;
@@ -252,6 +263,8 @@ struct MfmaCfg {
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is a whole number of 32x32 tiles");
 };
 
+constexpr int gcd8(int x) { return (x & 7) == 0 ? 8 : (x & 3) == 0 ? 4 : (x & 1) == 0 ? 2 : 1; }
+
 // One operand's staged tile.  LDS holds it in storage order:
 //  * K-contiguous (A not transposed, B transposed): BX rows of 128 bytes (one row per m or n),
 //    eight 16-byte chunks per row, chunk c of row r at position c ^ kswz(r);
@@ -268,10 +281,22 @@ struct Operand {
   static constexpr int RB = MN ? BX * ES : 128;     // LDS row bytes
   static constexpr int CPR = RB / 16;               // chunks per LDS row
   static constexpr int WLOADS = BX / 8;             // 1 KB wave-loads per tile (BX*128 bytes)
-  static constexpr int PER_WAVE = WLOADS / C::NW;
+  static constexpr int PER_WAVE = WLOADS / C::NCW;  // copies per copying wave
+  static constexpr int RPU = MN ? 1024 / RB : 8;     // rows (k-rows when MN) per wave-load
+  // A K-contiguous chunk's position in its row depends only on its wave-load modulo 8 (see
+  // chunk_of), so a copying wave's wave-loads i and i % VP differ by a whole number of rows, the
+  // same for every lane: the per-lane offsets of the first VP can serve them all, plus a
+  // uniform row step folded into the buffer descriptor (scalar work per copy).  Only the
+  // block-scaled fp4 kernel does so: on the 256 tile it would spill otherwise, while for the
+  // others the descriptor arithmetic costs scalar registers they are short of; they keep one
+  // offset register per copy.
+  static constexpr int SWZ_STEP = C::NCW;
+  static constexpr int VP =
+      (MN || !C::MX || C::DT != E2M1 || PER_WAVE < 8 / gcd8(SWZ_STEP)) ? PER_WAVE : 8 / gcd8(SWZ_STEP);
+  static_assert(PER_WAVE % VP == 0, "whole periods of per-lane offsets");
   static constexpr int LDS_OFF = IS_A ? 0 : C::S * C::A_BYTES;  // first buffer of the operand
   static constexpr int BUF_BYTES = IS_A ? C::A_BYTES : C::B_BYTES;
-  static_assert(WLOADS % C::NW == 0, "every wave issues the same number of loads");
+  static_assert(WLOADS % C::NCW == 0, "every copying wave issues the same number of loads");
   static_assert(!MN || (RB <= 1024 && 1024 % RB == 0), "whole k-rows per wave-load");
 
   __device__ static __forceinline__ int kswz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -366,23 +391,46 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   const uint8_t* Ag = reinterpret_cast<const uint8_t*>(p.A);
   const uint8_t* Bg = reinterpret_cast<const uint8_t*>(p.B);
 
-  // Per-lane byte offsets of the chunks this lane copies (loop invariant).
-  uint32_t voA[OA::PER_WAVE], voB[OB::PER_WAVE];
+  // Copying waves (all, or one per SIMD; see MfmaCfg::NCW) and this one's index among them.
+  const bool copier = C::NCW == C::NW || wave_u < (uint32_t)C::NCW;
+  const int cw = wave % C::NCW;
+  const uint32_t cw_u = wave_u % C::NCW;
+  // Per-lane byte offsets of the chunks this lane copies in its first VP wave-loads (loop
+  // invariant); wave-load i uses those of i % VP with the buffer moved on by a row step.
+  uint32_t voA[OA::VP], voB[OB::VP];
 #pragma unroll
-  for (int i = 0; i < OA::PER_WAVE; ++i) {
+  for (int i = 0; i < OA::VP; ++i) {
     int r, c;
-    OA::chunk_of(wave + C::NW * i, lane, r, c);
+    OA::chunk_of(cw + C::NCW * i, lane, r, c);
     voA[i] = (uint32_t)((int64_t)r * p.lda * ES + c * 16);
   }
 #pragma unroll
-  for (int i = 0; i < OB::PER_WAVE; ++i) {
+  for (int i = 0; i < OB::VP; ++i) {
     int r, c;
-    OB::chunk_of(wave + C::NW * i, lane, r, c);
+    OB::chunk_of(cw + C::NCW * i, lane, r, c);
     voB[i] = (uint32_t)((int64_t)r * p.ldb * ES + c * 16);
   }
+  // Wave-load i of a copying wave: the buffer [base, base + ext) moved on by the uniform row
+  // step between wave-loads i and i % VP (a multiple of 16 bytes, since the row stride is),
+  // its extent shortened to match, so that a chunk reads zero exactly where it did before.
+  auto copy_wave_loads = [&](auto opnd, const uint8_t* base, uint32_t ext, uint32_t row_bytes,
+                             uint32_t l, const uint32_t* vo) {
+    using O = decltype(opnd);
+#pragma unroll
+    for (int i = 0; i < O::PER_WAVE; ++i) {
+      const uint32_t step = (uint32_t)((i - i % O::VP) * C::NCW * O::RPU) * row_bytes;
+      // an opaque difference: written plainly, the compiler turns the clamp into a saturating
+      // subtract that only the vector unit has, and the descriptor leaves the scalar registers
+      uint32_t rest = ext - step;
+      asm volatile("" : "+s"(rest));
+      const i32x4 r = make_rsrc(base + step, ext > step ? rest : 0u);
+      buffer_load_lds16(r, l + C::NCW * i * 1024, vo[i % O::VP]);
+    }
+  };
 
   // Issue the direct copies of K tile kt of A (into A buffer buf) or of B (into B buffer buf).
   auto issue_a = [&](int kt, int buf) {
+    if (!copier) return;
     const int k0 = kt * C::BKE;
     const uint8_t* base;
     uint32_t ext;
@@ -393,12 +441,11 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
       base = Ag + ((int64_t)k0 * p.lda + m0) * ES;
       ext = extent_bytes(p.K, p.M, p.lda, k0, m0, ES);
     }
-    const i32x4 r = make_rsrc(base, ext);
-    const uint32_t l = (uint32_t)reinterpret_cast<uintptr_t>(gsm + OA::LDS_OFF + buf * C::A_BYTES) + wave_u * 1024;
-#pragma unroll
-    for (int i = 0; i < OA::PER_WAVE; ++i) buffer_load_lds16(r, l + C::NW * i * 1024, voA[i]);
+    const uint32_t l = (uint32_t)reinterpret_cast<uintptr_t>(gsm + OA::LDS_OFF + buf * C::A_BYTES) + cw_u * 1024;
+    copy_wave_loads(OA{}, base, ext, (uint32_t)(p.lda * ES), l, voA);
   };
   auto issue_b = [&](int kt, int buf) {
+    if (!copier) return;
     const int k0 = kt * C::BKE;
     const uint8_t* base;
     uint32_t ext;
@@ -409,16 +456,16 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
       base = Bg + ((int64_t)n0 * p.ldb + k0) * ES;
       ext = extent_bytes(p.N, p.K, p.ldb, n0, k0, ES);
     }
-    const i32x4 r = make_rsrc(base, ext);
-    const uint32_t l = (uint32_t)reinterpret_cast<uintptr_t>(gsm + OB::LDS_OFF + buf * C::B_BYTES) + wave_u * 1024;
-#pragma unroll
-    for (int i = 0; i < OB::PER_WAVE; ++i) buffer_load_lds16(r, l + C::NW * i * 1024, voB[i]);
+    const uint32_t l = (uint32_t)reinterpret_cast<uintptr_t>(gsm + OB::LDS_OFF + buf * C::B_BYTES) + cw_u * 1024;
+    copy_wave_loads(OB{}, base, ext, (uint32_t)(p.ldb * ES), l, voB);
   };
 
   // Last K tile: rewrite every chunk that reaches past K (K-contiguous operand) or past the
   // matrix edge in the final k-row (M/N-contiguous operand) with its valid elements and zeros.
-  // Runs after the tile's copies have landed and before the barrier.
+  // Runs after the tile's copies have landed and before the barrier; each copying wave fixes
+  // the chunks it copied.
   auto fixup = [&](int kt, int abuf, int bbuf) {
+    if (!copier) return;
     // An opaque copy of the lane index keeps the compiler from hoisting this rarely run code's
     // address arithmetic out of the K loop, where it would hold registers for every iteration.
     int lane = lane_id;
@@ -427,7 +474,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
     if (p.epi & FIX_A) {
 #pragma unroll
       for (int i = 0; i < OA::PER_WAVE; ++i) {
-        const int u = wave + C::NW * i;
+        const int u = cw + C::NCW * i;
         int r, c;
         OA::chunk_of(u, lane, r, c);
         uint8_t* dst = gsm + OA::LDS_OFF + abuf * C::A_BYTES + u * 1024 + lane * 16;
@@ -448,7 +495,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
     if (p.epi & FIX_B) {
 #pragma unroll
       for (int i = 0; i < OB::PER_WAVE; ++i) {
-        const int u = wave + C::NW * i;
+        const int u = cw + C::NCW * i;
         int r, c;
         OB::chunk_of(u, lane, r, c);
         uint8_t* dst = gsm + OB::LDS_OFF + bbuf * C::B_BYTES + u * 1024 + lane * 16;
@@ -756,23 +803,31 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   const int KT = C::KS == 1 ? KT_SK : (KT_ALL - kg + C::KS - 1) / C::KS;
   auto tile_of = [&](int i) { return C::KS == 1 ? kbeg + i : i * C::KS + kg; };
   const bool need_fix = (p.epi & (FIX_A | FIX_B)) != 0;
-  constexpr int NL = OA::PER_WAVE + (C::QB ? 0 : OB::PER_WAVE);  // data copies per wave per K tile
+  constexpr int NL = OA::PER_WAVE + (C::QB ? 0 : OB::PER_WAVE);  // data copies per copying wave per K tile
+  const int nl = copier ? NL : 0;                                 // ... by this wave
   constexpr int NWL = (C::BM + C::BN) / 64;         // 64-row scale wave-loads per chunk
-  static_assert(!C::MX || (NWL <= C::NW && C::NW % NWL == 0 && C::TPC + 1 >= C::S),
-                "every wave issues one scale copy per chunk; chunk buffers free in time");
+  constexpr int SPW = NWL > C::NCW ? NWL / C::NCW : 1;  // ... issued by each copying wave
+  static_assert(!C::MX || ((NWL % C::NCW == 0 || C::NCW % NWL == 0) && C::TPC + 1 >= C::S),
+                "the scale copies share evenly among the copying waves; chunk buffers free in time");
+  const int nsc = copier ? SPW : 0;                 // scale copies per chunk by this wave
   auto issue_scales = [&](int c) {
-    // wave w copies 64 rows (wave-load w % NWL; extra waves repeat a copy, writing the same
-    // bytes): row r of op(A) (then of op(B)) gives its 16 scale bytes from block 16 c on
-    const int u = (int)(wave_u % NWL);
-    const uint32_t l = (uint32_t)reinterpret_cast<uintptr_t>(smem + C::SC_OFF + (c & 1) * C::SC_BUF) + u * 1024;
-    if (64 * u < C::BM) {
-      const int64_t bytes = (int64_t)p.M * p.ldsa;
-      const i32x4 r = make_rsrc(p.sa, (uint32_t)(bytes < 0xfffffff0LL ? bytes : 0xfffffff0LL) & ~15u);
-      buffer_load_lds16(r, l, (uint32_t)((int64_t)(m0 + 64 * u + lane) * p.ldsa + 16 * c));
-    } else {
-      const int64_t bytes = (int64_t)p.N * p.ldsb;
-      const i32x4 r = make_rsrc(p.sb, (uint32_t)(bytes < 0xfffffff0LL ? bytes : 0xfffffff0LL) & ~15u);
-      buffer_load_lds16(r, l, (uint32_t)((int64_t)(n0 + 64 * u - C::BM + lane) * p.ldsb + 16 * c));
+    // copying wave w copies 64 rows per wave-load (w, w + NCW, ...; mod NWL, so extra waves
+    // repeat a copy, writing the same bytes): row r of op(A) (then of op(B)) gives its 16 scale
+    // bytes from block 16 c on
+    if (!copier) return;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int u = (int)((cw_u + C::NCW * j) % NWL);
+      const uint32_t l = (uint32_t)reinterpret_cast<uintptr_t>(smem + C::SC_OFF + (c & 1) * C::SC_BUF) + u * 1024;
+      if (64 * u < C::BM) {
+        const int64_t bytes = (int64_t)p.M * p.ldsa;
+        const i32x4 r = make_rsrc(p.sa, (uint32_t)(bytes < 0xfffffff0LL ? bytes : 0xfffffff0LL) & ~15u);
+        buffer_load_lds16(r, l, (uint32_t)((int64_t)(m0 + 64 * u + lane) * p.ldsa + 16 * c));
+      } else {
+        const int64_t bytes = (int64_t)p.N * p.ldsb;
+        const i32x4 r = make_rsrc(p.sb, (uint32_t)(bytes < 0xfffffff0LL ? bytes : 0xfffffff0LL) & ~15u);
+        buffer_load_lds16(r, l, (uint32_t)((int64_t)(n0 + 64 * u - C::BM + lane) * p.ldsb + 16 * c));
+      }
     }
   };
   auto issue = [&](int it, int buf) {  // the tile of iteration it
@@ -785,10 +840,10 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   // Copies a wave issues for tiles t0 .. t1 (each tile's data, and its chunk of scales first).
   auto copies = [&](int t0, int t1) {
     int n = 0;
-    for (int t = t0; t <= t1; ++t) n += NL + ((C::MX && t % C::TPC == 0) ? 1 : 0);
+    for (int t = t0; t <= t1; ++t) n += nl + ((C::MX && t % C::TPC == 0) ? nsc : 0);
     return n;
   };
-  constexpr int MAXC = (C::S - 1) * (NL + (C::MX ? 1 : 0));
+  constexpr int MAXC = (C::S - 1) * (NL + (C::MX ? SPW : 0));
   static_assert(MAXC < 64, "outstanding-copy counts fit the 6-bit vmcnt");
   auto tile_boundary = [&](int kt, int abuf, int anext) {
     // tiles kt+2 .. min(kt+S-1, KT-1) may stay in flight

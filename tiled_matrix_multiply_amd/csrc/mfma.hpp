@@ -845,12 +845,22 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   };
   constexpr int MAXC = (C::S - 1) * (NL + (C::MX ? SPW : 0));
   static_assert(MAXC < 64, "outstanding-copy counts fit the 6-bit vmcnt");
+  // With copying waves and the grouped schedule (16- and 32-bit inputs, two stages), a copying
+  // wave issues a tile's A copies at the boundary and its B copies only after the next tile's
+  // first k-group: the 16 copies at once kept it at the address unit for about 1060 cycles per
+  // tile (about 60 B per clock per compute unit), during which its partner was the only wave
+  // on the SIMD with multiplies to issue and could not hide its own fragment reads.  The B
+  // copies still land a good half tile before the boundary that waits for them.
+  constexpr bool DEFER_B = C::NCW < C::NW && GROUPED && !C::MX && C::QB == 0 && C::S == 2;
   auto tile_boundary = [&](int kt, int abuf, int anext) {
     // tiles kt+2 .. min(kt+S-1, KT-1) may stay in flight
     wait_vm<0, MAXC>(copies(kt + 2, min(kt + C::S - 1, KT - 1)));
     if (kt + 2 == KT && need_fix && tile_of(kt + 1) == KT_ALL - 1) fixup(tile_of(kt + 1), anext, anext);
     __syncthreads();
-    if (kt + C::S < KT) issue(kt + C::S, abuf);  // into the buffers tile kt has released
+    if (kt + C::S < KT) {  // into the buffers tile kt has released
+      if constexpr (DEFER_B) issue_a(tile_of(kt + C::S), abuf);
+      else issue(kt + C::S, abuf);
+    }
   };
   // Quantized B.  Thread t dequantises the 32 codes k0 + 32 (t % 2) .. +31 of row t / 2 of the
   // B tile (one 16-byte code chunk at 4 bits, two at 8), one group (group % 32 == 0): w =
@@ -959,6 +969,9 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
           load_group(kt, aoff, boff, g + 1, (g + 1) & 1);
           mma_group(g);
         }
+        // the deferred B copies of tile kt + 1, into the buffer tile kt - 1 released
+        if constexpr (DEFER_B)
+          if (g == 0 && kt >= 1 && kt + 1 < KT) issue_b(tile_of(kt + 1), anext);
         if constexpr (C::QB != 0)
           if (kt + 1 < KT) qstore_part(qcur, anext, g);
       }

@@ -226,10 +226,11 @@ struct MfmaCfg {
   // meanwhile: the dispatcher deals a workgroup's waves to the four SIMDs in turn, so waves
   // 0 .. 3 sit on four different SIMDs and wave w + 4 shares wave w's (read from the hardware-ID
   // register).  Measured at 4096 x 4096 x 8192: bf16 -1.8%, fp8 -3%, MXFP4 -3.5%, fused bf16
-  // + bias + GELU 4096^3 -2.5%; 6-bit inputs gain nothing (MXFP6 +3.5%), so they keep the copies
-  // on all waves, as does quantized B, whose code loads every thread issues.
+  // + bias + GELU 4096^3 -2.5%; with quantized B (whose codes every thread still loads) the
+  // 4-bit prefill 4096^3 -1.6%.  6-bit inputs gain nothing (MXFP6 +3.5%), so they keep the
+  // copies on all waves.
   static constexpr int NCW =
-      (TILE_ == 256 && BN_ == 0 && NW == 8 && KS_ == 1 && QB_ == 0 && !is_fp6<DT_>()) ? 4 : NW;
+      (TILE_ == 256 && BN_ == 0 && NW == 8 && KS_ == 1 && !is_fp6<DT_>()) ? 4 : NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 accumulators per wave
   static constexpr int ES = DTypeInfo<DT_>::bytes;

@@ -10,10 +10,12 @@ bf16 at 4096^3.  Each cell: warm up for >= 200 ms, then R timed reps with one HI
 per rep on the stream the kernel runs on; median and a percentile-bootstrap 95% CI
 (10^4 resamples, seed 0), as "Rigel" (arXiv 2606.12765), section 3 reports its cells.  The
 headline's timed steps come after a time-based settle (--settle-seconds of back-to-back steps)
-and the --warmup steps.  The shader clock is sampled during every timed region and printed
-beside its fraction of peak ("Rigel" section 3: the clock state decides small-size results),
-and a measured device-copy bandwidth stands beside the 8 TB/s HBM figure as the practical
-ceiling of the bandwidth-bound cells ("Case Study: The Tiled GEMM", its bandwidth roofline).
+and the --warmup steps.  Clock ("Rigel" section 3: the clock state decides the results): the
+headline's roofline carries the shader clock held during the kernel, from the committed
+counter summary of the same sources (GRBM_GUI_ACTIVE per dispatch time), and every timed
+region is followed by an in-kernel probe of the clock it left the chip at.  A measured
+streaming-read and copy bandwidth stands beside the 8 TB/s HBM figure as the practical ceiling
+of the bandwidth-bound cells ("Case Study: The Tiled GEMM", its bandwidth roofline).
 
 Prints ONE JSON line.  Only --gpus 1 is supported: the library runs on a single GPU.
 """

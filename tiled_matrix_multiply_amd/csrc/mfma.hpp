@@ -227,17 +227,17 @@ struct MfmaCfg {
   // 0 .. 3 sit on four different SIMDs and wave w + 4 shares wave w's (read from the hardware-ID
   // register).  Measured at 4096 x 4096 x 8192: bf16 -1.8%, fp8 -3%, MXFP4 -3.5%, fused bf16
   // + bias + GELU 4096^3 -2.5%; with quantized B (whose codes every thread still loads) the
-  // 4-bit prefill 4096^3 -1.6%.  6-bit inputs gain nothing (MXFP6 +3.5%), so they keep the
-  // copies on all waves.
-  static constexpr int NCW =
-      (TILE_ == 256 && BN_ == 0 && NW == 8 && KS_ == 1 && !is_fp6<DT_>()) ? 4 : NW;
+  // 4-bit prefill 4096^3 -1.6%; 6-bit inputs, whose copies skip the unused quarter of each row
+  // (below), about -1%.
+  static constexpr int NCW = (TILE_ == 256 && BN_ == 0 && NW == 8 && KS_ == 1) ? 4 : NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 accumulators per wave
   static constexpr int ES = DTypeInfo<DT_>::bytes;
   static constexpr bool FP6 = is_fp6<DT_>();
   // K elements per staged tile: 128 bytes of each row, or for packed 6-bit rows 96 bytes (128
-  // elements, two k-groups) in the 128-byte LDS row; the copies still move the row's 128 bytes
-  // from the tile start, and the fragment reads never touch the last 32.
+  // elements, two k-groups) in the 128-byte LDS row; the copies move the row's 128 bytes from
+  // the tile start (on the 256 tile only the first 96), and the fragment reads never touch the
+  // last 32.
   static constexpr int BKE = FP6 ? 96 : 128 / ES;
   static constexpr bool A_MN = A_MN_, B_MN = B_MN_;    // operand stored contiguous along M/N
   static_assert(!FP6 || (!A_MN_ && !B_MN_), "packed 6-bit operands are staged K-contiguous");
@@ -425,7 +425,17 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
       uint32_t rest = ext - step;
       asm volatile("" : "+s"(rest));
       const i32x4 r = make_rsrc(base + step, ext > step ? rest : 0u);
-      buffer_load_lds16(r, l + C::NCW * i * 1024, vo[i % O::VP]);
+      if constexpr (C::FP6 && !O::MN && C::BM == 256) {
+        // a 6-bit K tile is the first 96 bytes of each 128-byte row: the lanes of the last two
+        // chunks copy nothing (their LDS slots are never read).  On the 256 tile that takes a
+        // quarter off the copies' address work: MXFP6 4096^3 -4.5%, per-tensor fp6 -5.5%; on
+        // the 128 tile the masked loads measured 2% slower, so it copies whole rows
+        int row, c;
+        O::chunk_of(cw + C::NCW * i, lane, row, c);
+        if (c < 6) buffer_load_lds16(r, l + C::NCW * i * 1024, vo[i % O::VP]);
+      } else {
+        buffer_load_lds16(r, l + C::NCW * i * 1024, vo[i % O::VP]);
+      }
     }
   };
 

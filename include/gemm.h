@@ -177,11 +177,13 @@ GEMM_API gemm_status_t gemm_run_kernel(gemm_handle_t h, gemm_kernel_t kernel, vo
  * gemm_run_ws with AUTO runs exactly as gemm_run and gemm_workspace_bytes reports 0; the split
  * kernel is taken when named (gemm_run_ws_kernel).
  *   workspace: DEVICE memory owned by the caller, 256-byte aligned, workspace_bytes long
- *     (gemm_workspace_bytes gives the size a call needs; NULL with 0 bytes is allowed).  It must
- *     be zero-filled before its first use; every call leaves it ready for the next (its
- *     per-tile counters even, its flags at half the counters), so it is filled once, not per
- *     call.  Calls that share a workspace must not overlap (one stream, or synchronised);
- *     overlapping calls race on it.
+ *     (gemm_workspace_bytes gives the size a call needs; NULL with 0 bytes is allowed).  It holds
+ *     one 131328-byte slot per 256 x 128 output tile, tile t in slot t whatever the size of the
+ *     call: the tile's counter and flag, then its fp32 partial sums.  It must be zero-filled
+ *     before its first use; every call leaves each slot it used ready for the next (counter
+ *     even, flag at half the counter) and touches no other slot, so it is filled once, not per
+ *     call, and calls of different sizes may share it.  Calls that share a workspace must not
+ *     overlap (one stream, or synchronised); overlapping calls race on it.
  * Errors as gemm_run, plus GEMM_ERR_INVALID_VALUE for a negative workspace_bytes, a NULL
  * workspace with workspace_bytes > 0, or a workspace not aligned to 256 bytes. */
 GEMM_API gemm_status_t gemm_run_ws(gemm_handle_t h, void* stream, int64_t M, int64_t N,
@@ -193,9 +195,9 @@ GEMM_API gemm_status_t gemm_run_ws(gemm_handle_t h, void* stream, int64_t M, int
                                    int64_t workspace_bytes);
 
 /* gemm_run_ws with an explicit kernel family.  GEMM_KERNEL_MFMA_256x128_SK2 takes any M, N, K
- * of fp16 / bf16 inputs that the matrix-core kernels accept, with a workspace of at least 8
- * bytes per 256 x 128 output tile (rounded up to a multiple of 256) plus 131072 bytes per tile
- * (GEMM_ERR_INVALID_VALUE otherwise); the other families ignore the workspace. */
+ * of fp16 / bf16 inputs that the matrix-core kernels accept, with a workspace of at least 131328
+ * bytes per 256 x 128 output tile (GEMM_ERR_INVALID_VALUE otherwise); the other families ignore
+ * the workspace. */
 GEMM_API gemm_status_t gemm_run_ws_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* stream,
                                           int64_t M, int64_t N, int64_t K, int transA,
                                           int transB, float alpha, const void* A, int64_t lda,
@@ -209,8 +211,9 @@ GEMM_API gemm_status_t gemm_run_ws_kernel(gemm_handle_t h, gemm_kernel_t kernel,
 /* gemm_run_ws_kernel without a workspace argument and without any allocation, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  The workspace is the library's own static device array, 16 MiB +
- * 4 KiB per device, held from the time the library's code object loads on that device until
- * the process ends, and addressed through the handle (gemm_create takes its address).  The
+ * 32 KiB (128 slots) per device, held from the time the library's code object loads on that
+ * device until the process ends, and addressed through the handle (gemm_create takes its
+ * address).  The
  * kernel that uses it, GEMM_KERNEL_MFMA_256x128_SK2, therefore takes outputs of at most 128
  * tiles of 256 x 128 (for example 2048 x 2048); a larger one returns GEMM_ERR_TOO_LARGE and
  * enqueues nothing.  AUTO and the other kernel families use no scratch and run as
@@ -228,8 +231,8 @@ GEMM_API gemm_status_t gemm_run_noalloc(gemm_handle_t h, gemm_kernel_t kernel, v
                                         const float* bias);
 
 /* Workspace bytes gemm_run_ws (AUTO) would use for these arguments: 0 when it would not split
- * the K loop (currently always), else 8 per 256 x 128 output tile (rounded up to 256) plus 131072
- * per tile.  Negative status for invalid arguments (as gemm_check_args) or an invalid handle. */
+ * the K loop (currently always), else 131328 per 256 x 128 output tile.  Negative status for
+ * invalid arguments (as gemm_check_args) or an invalid handle. */
 GEMM_API int64_t gemm_workspace_bytes(gemm_handle_t h, int64_t M, int64_t N, int64_t K,
                                       int transA, int transB, const void* A, int64_t lda,
                                       const void* B, int64_t ldb, const void* C, int64_t ldc,

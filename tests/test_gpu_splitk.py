@@ -110,7 +110,9 @@ def test_named_workloads_every_entry(g, name, n):
     d.reset_c()
     raw2, _ = H.run(g, p, kernel=KERNELS["split"], dev=d, workspace=ws, workspace_bytes=nbytes)
     assert np.array_equal(raw1, raw2)
-    sync = ws[: 2 * (-(-p.M // 256)) * (-(-p.N // 128))].cpu().numpy().view(np.uint32).reshape(-1, 2)
+    tiles, slot = (-(-p.M // 256)) * (-(-p.N // 128)), tmm.SPLIT_K_SLOT_BYTES // 4
+    words = ws.cpu().numpy().view(np.uint32)
+    sync = np.array([(words[t * slot], words[t * slot + 1]) for t in range(tiles)])
     assert (sync[:, 0] % 2 == 0).all() and (sync[:, 1] == sync[:, 0] // 2).all()
     d.reset_c()
     raw3, _ = H.run(g, p, dev=d, workspace=ws, workspace_bytes=nbytes)
@@ -163,4 +165,42 @@ def test_workspace_validation(g):
     a32 = (512, 512, 512, 0, 0, 1.0, d32.A.data_ptr(), 512, 1.0, d32.B.data_ptr(), 512, 1.0, 0.0,
            d32.C.data_ptr(), 512, tmm.GEMM_F32, tmm.GEMM_F32, tmm.GEMM_F32, 0, None)
     assert tmm.gemm_run_ws_kernel(g.handle, split, None, *a32, ws.data_ptr(), nbytes) == tmm.GEMM_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+
+
+def test_workspace_slots_survive_calls_of_other_sizes(g):
+    """Tile t's counter, flag and partial sums live in slot t whatever the size of the call, so a
+    smaller call on a shared workspace touches only its own slots: after a 32-tile call and an
+    8-tile call, slots 8..31 still hold what the first call left (counter 2, flag 1), and a third,
+    32-tile call is correct and equal to the first bit for bit."""
+    import torch
+    import tiled_matrix_multiply_amd as tmm
+    big = W.make_problem(1024, 1024, 1024, a_type="bf16", seed=41, dist_a=("normal", 1.0),
+                         dist_b=("normal", 1.0 / 32), epilogue=W.EPI_BIAS | W.EPI_GELU)
+    small = W.make_problem(512, 512, 768, a_type="bf16", seed=42, dist_a=("normal", 1.0),
+                           dist_b=("normal", 1.0 / 32), epilogue=W.EPI_BIAS | W.EPI_GELU)
+    ws, nbytes = _workspace(big.M, big.N)
+    slot = tmm.SPLIT_K_SLOT_BYTES
+    tiles_big, tiles_small = (1024 // 256) * (1024 // 128), (512 // 256) * (512 // 128)
+    assert nbytes == tiles_big * slot and tiles_small == 8
+
+    def sync_words():
+        w = ws.cpu().numpy().view(np.uint32)
+        return np.array([(w[t * slot // 4], w[t * slot // 4 + 1]) for t in range(tiles_big)])
+
+    db = H.Device(big)
+    first, _ = H.run(g, big, kernel=KERNELS["split"], dev=db, workspace=ws, workspace_bytes=nbytes)
+    assert (sync_words() == [2, 1]).all()
+    ds = H.Device(small)
+    got_small, _ = H.run(g, small, kernel=KERNELS["split"], dev=ds, workspace=ws,
+                         workspace_bytes=nbytes)
+    words = sync_words()
+    assert (words[:tiles_small] == [4, 2]).all() and (words[tiles_small:] == [2, 1]).all(), words
+    assert H.gate_full(small, oracle.decode(small.c_type, got_small)).ok
+    db.reset_c()
+    third, _ = H.run(g, big, kernel=KERNELS["split"], dev=db, workspace=ws, workspace_bytes=nbytes)
+    assert np.array_equal(first, third)
+    res = H.gate_full(big, oracle.decode(big.c_type, third))
+    _report("slots across sizes 1024^2 / 512^2 / 1024^2", res)
+    assert res.ok, res
     torch.cuda.synchronize()

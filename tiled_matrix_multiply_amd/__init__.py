@@ -282,12 +282,13 @@ def gemm_workspace_bytes(handle, M, N, K, transA, transB, A, lda, B, ldb, C, ldc
                                      a_type, b_type, c_type, epilogue, bias)
 
 
+SPLIT_K_SLOT_BYTES = 131328  # one 256 x 128 output tile: counter and flag, then fp32 partial sums
+
+
 def split_k_workspace_bytes(M: int, N: int) -> int:
     """Workspace the K-split kernel (GEMM_KERNEL_MFMA_256x128_SK2) needs for an M x N output,
-    as include/gemm.h states it: 8 bytes per 256 x 128 tile rounded up to 256, plus 131072 bytes
-    per tile."""
-    t = -(-M // 256) * -(-N // 128)
-    return -(-8 * t // 256) * 256 + t * 131072
+    as include/gemm.h states it: one 131328-byte slot per 256 x 128 tile."""
+    return -(-M // 256) * -(-N // 128) * SPLIT_K_SLOT_BYTES
 
 
 def gemm_probe_clock(handle, stream, out, workgroups, microseconds) -> int:

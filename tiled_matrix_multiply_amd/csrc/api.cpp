@@ -237,12 +237,9 @@ bool split_k_fits(const Args& a) {
 }
 int64_t split_k_tiles(const Args& a) { return ((a.M + 255) / 256) * ((a.N + 127) / 128); }
 bool split_k_wins(const Args&, int) { return false; }
-// Workspace of the split kernel: per tile a [counter, flag] pair of 32-bit words, then (from
-// the next 256-byte boundary) one 256 x 128 fp32 tile of partial sums.
-int64_t split_k_sync_bytes(const Args& a) { return ((8 * split_k_tiles(a) + 255) / 256) * 256; }
-int64_t split_k_ws_bytes(const Args& a) {
-  return split_k_sync_bytes(a) + split_k_tiles(a) * 256 * 128 * 4;
-}
+// Workspace of the split kernel: one slot per 256 x 128 output tile (tgemm::kSplitSlotBytes:
+// the tile's counter and flag, then its fp32 partial sums), tile t in slot t.
+int64_t split_k_ws_bytes(const Args& a) { return split_k_tiles(a) * tgemm::kSplitSlotBytes; }
 
 using tgemm::DeviceGuard;
 
@@ -407,8 +404,7 @@ gemm_status_t run_impl(gemm_handle_t h, gemm_kernel_t kernel, void* stream, cons
     if (wide && !split_k_fits(a)) return GEMM_ERR_UNSUPPORTED;
     if (kernel == GEMM_KERNEL_MFMA_256x128_SK2) {
       if (!ws || ws_bytes < split_k_ws_bytes(a)) return GEMM_ERR_INVALID_VALUE;
-      p.sk_sync = static_cast<uint32_t*>(ws);
-      p.sk_part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + split_k_sync_bytes(a));
+      p.sk_ws = static_cast<uint8_t*>(ws);
     }
     const int tile = kernel == GEMM_KERNEL_MFMA_32 ? 3
                      : kernel == GEMM_KERNEL_MFMA_256x128 ? 5

@@ -37,11 +37,17 @@ struct GemmParams {
   const void* qo;
   int64_t ldg;
   int group;
-  // K loop split across two workgroups: per tile a [counter, flag] pair of words and the
-  // first workgroup's fp32 accumulators (BM x BN floats).  Null otherwise.
-  uint32_t* sk_sync;
-  float* sk_part;
+  // K loop split across two workgroups: the workspace, one kSplitSlotBytes slot per output
+  // tile (below).  Null otherwise.
+  uint8_t* sk_ws;
 };
+
+// Workspace slot of one 256 x 128 output tile of the K loop split across two workgroups: its
+// [counter, flag] pair of 32-bit words in the first 256 bytes, then the first workgroup's fp32
+// partial sums (256 x 128 floats).  Slot t serves tile t whatever the size of the call, so calls
+// of different sizes can share a workspace without one call's partial sums landing on another
+// tile's counter and flag.
+constexpr int64_t kSplitSlotBytes = 256 + 256 * 128 * 4;
 
 template <int DT> struct DTypeInfo;
 template <> struct DTypeInfo<F32> { static constexpr int bytes = 4; };

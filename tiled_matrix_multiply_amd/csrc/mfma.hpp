@@ -1088,11 +1088,13 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
     // counter are device-scope atomics.  That avoids a release / acquire fence, which here would
     // write the whole L2 back and invalidate it under every workgroup still at work on the XCD.
     __shared__ uint32_t sk_old;
-    uint32_t* const sync = p.sk_sync + 2 * (int64_t)tile_id;  // [counter, flag]
+    static_assert(256 + C::BM * C::BN * 4 == kSplitSlotBytes, "one workspace slot per tile");
+    uint8_t* const slot = p.sk_ws + (int64_t)tile_id * kSplitSlotBytes;
+    uint32_t* const sync = reinterpret_cast<uint32_t*>(slot);  // [counter, flag]
     constexpr int NF = C::FM * C::FN * 4;                      // float4 pieces per lane
     constexpr int DEVICE_SCOPE = 16;                           // sc1 cache-policy bit
     const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
-        p.sk_part + (int64_t)tile_id * C::BM * C::BN, (short)0, C::BM * C::BN * 4, BUFFER_FLAGS);
+        slot + 256, (short)0, C::BM * C::BN * 4, BUFFER_FLAGS);
     const int pbase = (wave * NF * 64 + lane) * 16;            // this lane's first piece, bytes
     __syncthreads();  // every wave has left the K loop
     if (tid == 0) sk_old = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -6,17 +6,16 @@
 // (hipGetSymbolAddress with that device current), and every launch uses that address.  Each
 // device the library runs on holds its own copy of the array until the process ends.  It
 // starts zeroed (device globals are zero-initialised when the code object loads); the one
-// kernel that uses it (the K loop split across two workgroups) leaves its per-tile counters
-// even and its flags at half the counters after every call, which is the state the next call
-// needs, so nothing has to be cleared per call.  Calls on one device share the array, so calls
+// kernel that uses it (the K loop split across two workgroups) keeps tile t in slot t whatever
+// the call's size and leaves each slot it used with its counter even and its flag at half the
+// counter, which is the state the next call needs, so nothing has to be cleared per call.  Calls on one device share the array, so calls
 // that overlap on one device (different streams, unsynchronised) race on it.
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "common.hpp"
 
 namespace tgemm {
-// 4 KiB of per-tile counters and flags (up to 512 tiles) and 128 tiles of 256 x 128 fp32
-// partial sums: a 2048 x 2048 output, or any output of at most 128 such tiles.
-constexpr int64_t kScratchBytes = (int64_t(16) << 20) + 4096;
+// 128 workspace slots (each a tile's counter and flag, then its 256 x 128 fp32 partial sums):
+// a 2048 x 2048 output, or any output of at most 128 such tiles.  16 MiB + 32 KiB.
+constexpr int64_t kScratchBytes = 128 * kSplitSlotBytes;
 }  // namespace tgemm
 
 static __device__ __align__(256) uint8_t scratch[tgemm::kScratchBytes];

@@ -116,7 +116,9 @@ typedef enum gemm_kernel {
                                types return GEMM_ERR_UNSUPPORTED).  AUTO takes it when 64x64
                                tiles would leave three quarters of the compute units idle */
   GEMM_KERNEL_MFMA_256x128 = 8,     /* matrix-core kernel, 256x128 workgroup tile, 8 wavefronts
-                                       of 64x64; fp16 and bf16 only */
+                                       of 64x64; fp16 and bf16 only.  AUTO takes it when
+                                       128x128 tiles would need more than one round of the
+                                       compute units and 256x128 tiles need at most one */
   GEMM_KERNEL_MFMA_256x128_SK2 = 9  /* the 256x128 tile with its K loop split across two
                                        workgroups that meet through a workspace: gemm_run_ws /
                                        gemm_run_ws_kernel only; fp16 and bf16 only */

@@ -325,8 +325,19 @@ def test_kernel_selection(g):
     assert g.select_kernel(4096, 4096, 4096, a_type="bf16", **ptrs) == "mfma256"
     assert g.select_kernel(2048, 2048, 2048, a_type="bf16", **ptrs) == "mfma128"
     # beyond two rounds of 128 x 128 workgroups the 256 x 256 tile is faster
-    assert g.select_kernel(2816, 2816, 2816, a_type="bf16", **ptrs) == "mfma128"
     assert g.select_kernel(3072, 3072, 3072, a_type="bf16", **ptrs) == "mfma256"
+    assert g.select_kernel(3072, 4096, 4096, a_type="bf16", **ptrs) == "mfma256"
+    # 16-bit inputs whose 128 x 128 tiles need more than one round of the compute units and
+    # whose 256 x 128 tiles fit in one: the 256 x 128 tile
+    assert g.select_kernel(2816, 2816, 2816, a_type="bf16", **ptrs) == "mfma256x128"
+    assert g.select_kernel(2048, 4096, 4096, a_type="bf16", **ptrs) == "mfma256x128"
+    assert g.select_kernel(4096, 2048, 4096, a_type="f16", **ptrs) == "mfma256x128"
+    assert g.select_kernel(1100, 4104, 520, a_type="bf16", **ptrs) == "mfma256x128"
+    # ... but not other types, nor at one round of 128 x 128 tiles or fewer
+    assert g.select_kernel(2816, 2816, 2816, a_type="f32", **ptrs) == "mfma128"
+    assert g.select_kernel(2048, 4096, 4096, a_type="e4m3", **ptrs) == "mfma128"
+    assert g.select_kernel(1024, 4096, 4096, a_type="bf16", **ptrs) == "mfma128"
+    assert g.select_kernel(2048, 2048, 8192, a_type="bf16", **ptrs) == "mfma128"
     assert g.select_kernel(1024, 1024, 1024, a_type="f16", **ptrs) == "mfma64"
     assert g.select_kernel(1792, 1792, 1792, a_type="bf16", **ptrs) == "mfma128"
     assert g.select_kernel(1280, 1280, 1280, a_type="bf16", **ptrs) == "mfma64"

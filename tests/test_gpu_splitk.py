@@ -145,6 +145,23 @@ def test_split_matches_unsplit_wide_tile(g):
     assert H.gate_full(p, wide, cache=True).ok
 
 
+@pytest.mark.parametrize("dtype,M,N,K,ta,tb", [("bf16", 1100, 4104, 520, False, False),
+                                                ("f16", 2304, 2056, 200, True, True)])
+def test_auto_takes_wide_tile(g, dtype, M, N, K, ta, tb):
+    """Shapes whose 128 x 128 tiles need more than one round of the compute units and whose
+    256 x 128 tiles fit in one: gemm_run picks the 256 x 128 tile, and every entry of the
+    result (ragged M, N and K, padded leading dimensions, beta, bias and GELU) meets the
+    oracle's gate."""
+    p = W.make_problem(M, N, K, a_type=dtype, trans_a=ta, trans_b=tb, alpha=0.75, beta=0.5,
+                       seed=M + K, dist_a=("normal", 1.0), dist_b=("normal", K ** -0.5),
+                       epilogue=W.EPI_BIAS | W.EPI_GELU)
+    got, kname, pad_ok = H.run_padded(g, p)
+    res = H.gate_full(p, got)
+    _report(f"{dtype} {M}x{N}x{K} AUTO ({kname})", res)
+    assert kname == "mfma256x128"
+    assert pad_ok and res.ok, res
+
+
 def test_workspace_validation(g):
     import torch
     import tiled_matrix_multiply_amd as tmm

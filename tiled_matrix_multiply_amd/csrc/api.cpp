@@ -201,7 +201,14 @@ int k_split(const Args& a, int cu_count) {
   return (t <= 2 * (int64_t)cu_count && kt >= 4) ? 2 : 1;
 }
 
-// Largest tile that still gives every compute unit at least one workgroup.
+// The 256 x 128 tile (unsplit, GEMM_KERNEL_MFMA_256x128, and split across two workgroups) takes
+// fp16 and bf16 inputs only.
+bool split_k_fits(const Args& a) {
+  return (a.at == GEMM_F16 || a.at == GEMM_BF16) && !a.mx;
+}
+int64_t split_k_tiles(const Args& a) { return ((a.M + 255) / 256) * ((a.N + 127) / 128); }
+
+// The kernel family AUTO picks: broadly, the largest tile that still keeps the compute units busy.
 gemm_kernel_t auto_kernel(const Args& a, int cu_count) {
   if (!mfma_aligned(a)) return GEMM_KERNEL_SIMT;
   // 64 x 64 tiles would leave three quarters of the compute units idle: 32 x 32 tiles with the
@@ -209,9 +216,19 @@ gemm_kernel_t auto_kernel(const Args& a, int cu_count) {
   if ((a.at == GEMM_F32 || a.at == GEMM_F16 || a.at == GEMM_BF16) && 4 * tiles(a.M, a.N, 64) <= cu_count)
     return GEMM_KERNEL_MFMA_32;
   if (tiles(a.M, a.N, 256) >= cu_count) return GEMM_KERNEL_MFMA_256;
+  // Between one and two rounds of 128 x 128 workgroups, the 256 x 128 tile (16-bit inputs) does
+  // the work in a single round whenever its own tiles fit on the compute units: every such
+  // shape measured ran faster or equal (bf16 + bias + GELU, 128 x 128 vs 256 x 128 tile:
+  // 2048 x 4096 x 4096 86.6 vs 73.2 us, 1280 x 4096 x 4096 80.1 vs 64.2 us, 2560^3 59.1 vs
+  // 45.9 us, 1100 x 4104 x 4096 105.6 vs 73.1 us, 2176^3 51.6 vs 51.9 us).  At one round of
+  // 128 x 128 workgroups or fewer the 128 tile stays far ahead (1024 x 4096 x 4096 46.7 vs
+  // 63.3 us, 2048^2 x 8192 83.2 vs 114.5 us).
+  if (split_k_fits(a) && tiles(a.M, a.N, 128) > cu_count && split_k_tiles(a) <= cu_count)
+    return GEMM_KERNEL_MFMA_256x128;
   // More than two rounds of 128 x 128 workgroups cost more than one partly filled round of
   // 256 x 256 ones (bf16 + bias + GELU: 3072^3 80 vs 98 us, 3584^3 101 vs 146 us; at two
-  // rounds or fewer the 128 tile wins, 2816^3 65 vs 73 us, 4096 x 2048 x 4096 85 vs 99 us).
+  // rounds or fewer the 128 tile beats the 256 x 256 one, 2816^3 65 vs 73 us, 4096 x 2048 x
+  // 4096 85 vs 99 us, though for 16-bit inputs the 256 x 128 tile above takes most such shapes).
   if (tiles(a.M, a.N, 128) > 2 * (int64_t)cu_count) return GEMM_KERNEL_MFMA_256;
   // The 128 tile (its K loop split between two wave groups for 16- and 32-bit types) also
   // beats 64 x 64 tiles with some compute units idle, from about 9/16 of them busy: 1792^3
@@ -232,10 +249,6 @@ gemm_kernel_t auto_kernel(const Args& a, int cu_count) {
 // The hand-off of 128 KiB of partial sums per tile through device-coherent memory, plus the
 // second half's wait, costs about what the halved K loop saves, so AUTO does not take it; it
 // stays available as an explicit kernel family (gemm_run_ws_kernel).
-bool split_k_fits(const Args& a) {
-  return (a.at == GEMM_F16 || a.at == GEMM_BF16) && !a.mx;
-}
-int64_t split_k_tiles(const Args& a) { return ((a.M + 255) / 256) * ((a.N + 127) / 128); }
 bool split_k_wins(const Args&, int) { return false; }
 // Workspace of the split kernel: one slot per 256 x 128 output tile (tgemm::kSplitSlotBytes:
 // the tile's counter and flag, then its fp32 partial sums), tile t in slot t.

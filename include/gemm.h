@@ -119,8 +119,13 @@ typedef enum gemm_kernel {
                                        of 64x64; fp16 and bf16 only.  AUTO takes it when
                                        128x128 tiles would need more than one round of the
                                        compute units and 256x128 tiles need at most one */
-  GEMM_KERNEL_MFMA_256x128_SK2 = 9  /* the 256x128 tile with its K loop split across two
+  GEMM_KERNEL_MFMA_256x128_SK2 = 9, /* the 256x128 tile with its K loop split across two
                                        workgroups that meet through a workspace: gemm_run_ws /
+                                       gemm_run_ws_kernel only; fp16 and bf16 only */
+  GEMM_KERNEL_MFMA_256_SK = 10      /* stream-K: the 256x256 tile on a persistent grid of
+                                       one workgroup per compute unit that shares out the K
+                                       tiles of all output tiles evenly; the parts of a split
+                                       tile meet through a workspace: gemm_run_ws /
                                        gemm_run_ws_kernel only; fp16 and bf16 only */
 } gemm_kernel_t;
 
@@ -198,8 +203,23 @@ GEMM_API gemm_status_t gemm_run_ws(gemm_handle_t h, void* stream, int64_t M, int
 
 /* gemm_run_ws with an explicit kernel family.  GEMM_KERNEL_MFMA_256x128_SK2 takes any M, N, K
  * of fp16 / bf16 inputs that the matrix-core kernels accept, with a workspace of at least 131328
- * bytes per 256 x 128 output tile (GEMM_ERR_INVALID_VALUE otherwise); the other families ignore
- * the workspace. */
+ * bytes per 256 x 128 output tile (GEMM_ERR_INVALID_VALUE otherwise).
+ * GEMM_KERNEL_MFMA_256_SK (stream-K, the work-sharing of Osama et al., "Stream-K: Work-centric
+ * Parallel Decomposition for Dense Matrix-Matrix Multiplication on the GPU", PPoPP 2023) takes
+ * the same arguments.  With G = min(compute units, K tiles of the whole product), where
+ * the product has T output tiles of 256 x 256 and KT = ceil(K / 64) K tiles each, workgroup L
+ * takes K tiles [floor(L T KT / G), floor((L+1) T KT / G)) of the sequence that lists each
+ * tile's K tiles in turn, and walks them one output tile (segment) at a time.  A tile that falls
+ * to several workgroups is finished by the last of them to arrive, which adds the others' fp32
+ * partial sums in the order of their K ranges (the same bits on every run) and runs the
+ * epilogue.  AUTO does not take this family: on the shapes measured (fewer 256 x 256 tiles than
+ * compute units, or a partial last round) it was not faster than the plain tiles.  Its workspace (gemm_kernel_workspace_bytes) is two 262144-
+ * byte slots of partial sums per compute unit, then an [arrive, done] pair of 32-bit counters
+ * per output tile, 256-byte aligned; it must be zero-filled before its first use, and every call
+ * leaves the counters it used at zero, so calls of any size may share it (but not with
+ * GEMM_KERNEL_MFMA_256x128_SK2, whose slots are laid out differently, without zero-filling it
+ * again).  With K = 0 it runs as GEMM_KERNEL_MFMA_256.  The other families ignore the
+ * workspace. */
 GEMM_API gemm_status_t gemm_run_ws_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* stream,
                                           int64_t M, int64_t N, int64_t K, int transA,
                                           int transB, float alpha, const void* A, int64_t lda,
@@ -233,13 +253,21 @@ GEMM_API gemm_status_t gemm_run_noalloc(gemm_handle_t h, gemm_kernel_t kernel, v
                                         const float* bias);
 
 /* Workspace bytes gemm_run_ws (AUTO) would use for these arguments: 0 when it would not split
- * the K loop (currently always), else 131328 per 256 x 128 output tile.  Negative status for
- * invalid arguments (as gemm_check_args) or an invalid handle. */
+ * the K loop across workgroups, else what gemm_kernel_workspace_bytes gives for the family it
+ * takes.  Negative status for invalid arguments (as gemm_check_args) or an invalid handle. */
 GEMM_API int64_t gemm_workspace_bytes(gemm_handle_t h, int64_t M, int64_t N, int64_t K,
                                       int transA, int transB, const void* A, int64_t lda,
                                       const void* B, int64_t ldb, const void* C, int64_t ldc,
                                       gemm_dtype_t a_type, gemm_dtype_t b_type,
                                       gemm_dtype_t c_type, uint32_t epilogue, const float* bias);
+
+/* Workspace bytes gemm_run_ws_kernel needs for an M x N output with an explicit kernel family:
+ * GEMM_KERNEL_MFMA_256x128_SK2 131328 per 256 x 128 output tile; GEMM_KERNEL_MFMA_256_SK
+ * 2 x 262144 per compute unit of the handle's device plus 8 per 256 x 256 output tile, the
+ * latter rounded up to a multiple of 256; 0 for the families that use none.
+ * GEMM_ERR_INVALID_HANDLE, or GEMM_ERR_INVALID_VALUE for a negative or too large M or N. */
+GEMM_API int64_t gemm_kernel_workspace_bytes(gemm_handle_t h, gemm_kernel_t kernel, int64_t M,
+                                             int64_t N);
 
 /* Block-scaled GEMM in the OCP microscaling (MX) formats: every run of 32 consecutive k of a
  * row of op(A) and of a column of op(B) shares one E8M0 scale byte e, worth 2^(e - 127)

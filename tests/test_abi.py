@@ -23,7 +23,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported():
     syms = declared_symbols()
-    assert len(syms) == 22, syms
+    assert len(syms) == 23, syms
     assert sorted(tmm.EXPORTS) == syms
     nm = subprocess.run(["nm", "-D", "--defined-only", tmm.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
@@ -39,6 +39,8 @@ def test_measurement_helpers_validate_without_a_gpu():
     """The clock and bandwidth probes refuse a null handle before touching a device."""
     assert tmm.gemm_probe_clock(None, None, 0x1000, 256, 40) == tmm.GEMM_ERR_INVALID_HANDLE
     assert tmm.gemm_wall_clock_khz(None) == tmm.GEMM_ERR_INVALID_HANDLE
+    assert tmm.gemm_kernel_workspace_bytes(None, tmm.GEMM_KERNEL_MFMA_256_SK, 512,
+                                           512) == tmm.GEMM_ERR_INVALID_HANDLE
     assert tmm.gemm_probe_bandwidth(None, None, 0x1000, None, 1 << 20,
                                     0x2000) == tmm.GEMM_ERR_INVALID_HANDLE
 

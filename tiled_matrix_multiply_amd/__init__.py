@@ -48,8 +48,9 @@ GEMM_KERNEL_QMFMA = 6
 GEMM_KERNEL_MFMA_32 = 7
 GEMM_KERNEL_MFMA_256x128 = 8
 GEMM_KERNEL_MFMA_256x128_SK2 = 9
+GEMM_KERNEL_MFMA_256_SK = 10
 KERNEL_NAME = {0: "auto", 1: "simt", 2: "mfma64", 3: "mfma128", 4: "mfma256", 5: "qgemv",
-               6: "qmfma", 7: "mfma32", 8: "mfma256x128", 9: "mfma256x128_sk2"}
+               6: "qmfma", 7: "mfma32", 8: "mfma256x128", 9: "mfma256x128_sk2", 10: "mfma256_sk"}
 
 # Every symbol include/gemm.h declares.
 EXPORTS = ("gemm_create", "gemm_destroy", "gemm_check_args", "gemm_run", "gemm_run_kernel",
@@ -57,7 +58,7 @@ EXPORTS = ("gemm_create", "gemm_destroy", "gemm_check_args", "gemm_run", "gemm_r
            "gemm_bias_gelu", "gemm_status_string", "gemm_run_q", "gemm_run_q_kernel",
            "gemm_check_args_q", "gemm_select_kernel_q", "gemm_probe_clock",
            "gemm_wall_clock_khz", "gemm_probe_bandwidth", "gemm_run_ws", "gemm_run_ws_kernel",
-           "gemm_workspace_bytes", "gemm_run_noalloc")
+           "gemm_workspace_bytes", "gemm_run_noalloc", "gemm_kernel_workspace_bytes")
 
 # libgemm.so must resolve its libamdhip64.so.7 dependency to the HIP runtime instance that owns
 # the caller's device pointers and streams.  PyTorch ships its own runtime (soname
@@ -129,6 +130,8 @@ _lib.gemm_run_noalloc.restype = _int
 _lib.gemm_workspace_bytes.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _i64,
                                       _vp, _i64, _int, _int, _int, _u32, _vp]
 _lib.gemm_workspace_bytes.restype = _i64
+_lib.gemm_kernel_workspace_bytes.argtypes = [_vp, _int, _i64, _i64]
+_lib.gemm_kernel_workspace_bytes.restype = _i64
 _lib.gemm_probe_clock.argtypes = [_vp, _vp, _vp, _int, _int]
 _lib.gemm_probe_clock.restype = _int
 _lib.gemm_wall_clock_khz.argtypes = [_vp]
@@ -283,6 +286,10 @@ def gemm_workspace_bytes(handle, M, N, K, transA, transB, A, lda, B, ldb, C, ldc
 
 
 SPLIT_K_SLOT_BYTES = 131328  # one 256 x 128 output tile: counter and flag, then fp32 partial sums
+
+
+def gemm_kernel_workspace_bytes(handle, kernel, M, N) -> int:
+    return _lib.gemm_kernel_workspace_bytes(handle, kernel, M, N)
 
 
 def split_k_workspace_bytes(M: int, N: int) -> int:

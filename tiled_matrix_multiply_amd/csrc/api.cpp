@@ -4,6 +4,7 @@
 #include "gemm.h"
 
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -254,6 +255,16 @@ bool split_k_wins(const Args&, int) { return false; }
 // the tile's counter and flag, then its fp32 partial sums), tile t in slot t.
 int64_t split_k_ws_bytes(const Args& a) { return split_k_tiles(a) * tgemm::kSplitSlotBytes; }
 
+// Stream-K (GEMM_KERNEL_MFMA_256_SK, 256 x 256 tiles): two slots of fp32 partial sums per
+// workgroup of the largest grid the device runs (one per compute unit), then an [arrive, done]
+// pair of counters per output tile.  The slots come first, so that the counters sit at the same
+// offset for every call on the device and calls of different sizes can share a workspace.
+int64_t stream_k_slot_region(int cu_count) { return 2 * (int64_t)cu_count * tgemm::kStreamSlotBytes; }
+int64_t stream_k_ws_bytes(const Args& a, int cu_count) {
+  return stream_k_slot_region(cu_count) + ((8 * tiles(a.M, a.N, 256) + 255) / 256) * 256;
+}
+bool stream_k_wins(const Args&, int) { return false; }
+
 using tgemm::DeviceGuard;
 
 }  // namespace
@@ -377,7 +388,12 @@ gemm_status_t run_impl(gemm_handle_t h, gemm_kernel_t kernel, void* stream, cons
     if (ws && kernel != GEMM_KERNEL_SIMT && split_k_wins(a, h->cu_count) &&
         ws_bytes >= split_k_ws_bytes(a))
       kernel = GEMM_KERNEL_MFMA_256x128_SK2;
+    else if (ws && kernel != GEMM_KERNEL_SIMT && stream_k_wins(a, h->cu_count) &&
+             ws_bytes >= stream_k_ws_bytes(a, h->cu_count))
+      kernel = GEMM_KERNEL_MFMA_256_SK;
   }
+  // with no K tiles there is nothing to share out: the plain 256 x 256 tile runs the epilogue
+  if (kernel == GEMM_KERNEL_MFMA_256_SK && a.K == 0) kernel = GEMM_KERNEL_MFMA_256;
 
   tgemm::GemmParams p{};
   p.A = a.A;
@@ -409,12 +425,13 @@ gemm_status_t run_impl(gemm_handle_t h, gemm_kernel_t kernel, void* stream, cons
     err = tgemm::launch_simt(p, a.at, a.bt, a.transA, a.transB, s);
   } else if ((kernel >= GEMM_KERNEL_MFMA_64 && kernel <= GEMM_KERNEL_MFMA_256) ||
              kernel == GEMM_KERNEL_MFMA_32 || kernel == GEMM_KERNEL_MFMA_256x128 ||
-             kernel == GEMM_KERNEL_MFMA_256x128_SK2) {
+             kernel == GEMM_KERNEL_MFMA_256x128_SK2 || kernel == GEMM_KERNEL_MFMA_256_SK) {
     if (!mfma_aligned(a)) return GEMM_ERR_UNSUPPORTED;
     if (kernel == GEMM_KERNEL_MFMA_32 && a.at != GEMM_F32 && a.at != GEMM_F16 && a.at != GEMM_BF16)
       return GEMM_ERR_UNSUPPORTED;
     const bool wide = kernel == GEMM_KERNEL_MFMA_256x128 || kernel == GEMM_KERNEL_MFMA_256x128_SK2;
-    if (wide && !split_k_fits(a)) return GEMM_ERR_UNSUPPORTED;
+    const bool stream = kernel == GEMM_KERNEL_MFMA_256_SK;
+    if ((wide || stream) && !split_k_fits(a)) return GEMM_ERR_UNSUPPORTED;
     if (kernel == GEMM_KERNEL_MFMA_256x128_SK2) {
       if (!ws || ws_bytes < split_k_ws_bytes(a)) return GEMM_ERR_INVALID_VALUE;
       p.sk_ws = static_cast<uint8_t*>(ws);
@@ -422,13 +439,24 @@ gemm_status_t run_impl(gemm_handle_t h, gemm_kernel_t kernel, void* stream, cons
     const int tile = kernel == GEMM_KERNEL_MFMA_32 ? 3
                      : kernel == GEMM_KERNEL_MFMA_256x128 ? 5
                      : kernel == GEMM_KERNEL_MFMA_256x128_SK2 ? 6
+                     : stream ? 7
                      : kernel - GEMM_KERNEL_MFMA_64;
-    const int tmr = kernel == GEMM_KERNEL_MFMA_32 ? 32 : wide ? 256 : 64 << tile;
+    const int tmr = kernel == GEMM_KERNEL_MFMA_32 ? 32 : (wide || stream) ? 256 : 64 << tile;
     const int tnc = wide ? 128 : tmr;
     const int64_t tm = (a.M + tmr - 1) / tmr, tn = (a.N + tnc - 1) / tnc;
     if (tm * tn * 2 > kMaxDim) return GEMM_ERR_UNSUPPORTED;
     p.tiles_m = (int)tm;
     p.tiles_n = (int)tn;
+    if (stream) {
+      if (!ws || ws_bytes < stream_k_ws_bytes(a, h->cu_count)) return GEMM_ERR_INVALID_VALUE;
+      // one persistent workgroup per compute unit (a 256 x 256 tile's stages fill most of its
+      // LDS, so one runs on each at a time), and no more than K tiles (64 elements of K each),
+      // so that no run is empty
+      const int64_t kt = (a.K + 63) / 64;
+      p.sk_ws = static_cast<uint8_t*>(ws);
+      p.sk_cnt_off = stream_k_slot_region(h->cu_count);
+      p.sk_grid = (int)std::min<int64_t>(h->cu_count, tm * tn * kt);
+    }
     if (a.at == GEMM_E2M1) {
       // the matrix-core kernels stage packed fp4 rows as bytes: K and the leading dimensions
       // are passed in bytes (two elements each); the block count stays in elements / 32
@@ -501,9 +529,12 @@ gemm_status_t gemm_run_noalloc(gemm_handle_t h, gemm_kernel_t kernel, void* stre
                epilogue, bias};
   const gemm_status_t st = check(a);
   if (st != GEMM_OK) return st;
-  // the one kernel that uses scratch: refuse what the static array cannot hold
+  // the kernels that use scratch: refuse what the static array cannot hold
   if (kernel == GEMM_KERNEL_MFMA_256x128_SK2 && a.M > 0 && a.N > 0 &&
       split_k_ws_bytes(a) > h->scratch_bytes)
+    return GEMM_ERR_TOO_LARGE;
+  if (kernel == GEMM_KERNEL_MFMA_256_SK && a.M > 0 && a.N > 0 && a.K > 0 &&
+      stream_k_ws_bytes(a, h->cu_count) > h->scratch_bytes)
     return GEMM_ERR_TOO_LARGE;
   return run_impl(h, kernel, stream, a, alpha, scale_a, scale_b, beta, C, h->scratch,
                   h->scratch_bytes);
@@ -529,10 +560,21 @@ int64_t gemm_workspace_bytes(gemm_handle_t h, int64_t M, int64_t N, int64_t K, i
                epilogue, bias};
   const gemm_status_t st = check(a);
   if (st != GEMM_OK) return st;
-  if (a.M == 0 || a.N == 0 || auto_kernel(a, h->cu_count) == GEMM_KERNEL_SIMT ||
-      !split_k_wins(a, h->cu_count))
-    return 0;
-  return split_k_ws_bytes(a);
+  if (a.M == 0 || a.N == 0 || auto_kernel(a, h->cu_count) == GEMM_KERNEL_SIMT) return 0;
+  if (split_k_wins(a, h->cu_count)) return split_k_ws_bytes(a);
+  if (stream_k_wins(a, h->cu_count)) return stream_k_ws_bytes(a, h->cu_count);
+  return 0;
+}
+
+int64_t gemm_kernel_workspace_bytes(gemm_handle_t h, gemm_kernel_t kernel, int64_t M, int64_t N) {
+  if (!valid(h)) return GEMM_ERR_INVALID_HANDLE;
+  if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return GEMM_ERR_INVALID_VALUE;
+  Args a{};
+  a.M = M;
+  a.N = N;
+  if (kernel == GEMM_KERNEL_MFMA_256x128_SK2) return split_k_ws_bytes(a);
+  if (kernel == GEMM_KERNEL_MFMA_256_SK) return stream_k_ws_bytes(a, h->cu_count);
+  return 0;
 }
 
 gemm_status_t gemm_run_mx_kernel(gemm_handle_t h, gemm_kernel_t kernel, void* stream, int64_t M,

@@ -37,9 +37,13 @@ struct GemmParams {
   const void* qo;
   int64_t ldg;
   int group;
-  // K loop split across two workgroups: the workspace, one kSplitSlotBytes slot per output
-  // tile (below).  Null otherwise.
+  // K loop split across workgroups: the workspace (null otherwise).  Two workgroups per tile:
+  // one kSplitSlotBytes slot per output tile (below).  Stream-K: two kStreamSlotBytes slots
+  // per workgroup of the device's largest grid (one per compute unit), then from byte
+  // sk_cnt_off an [arrive, done] pair of 32-bit counters per output tile; sk_grid workgroups.
   uint8_t* sk_ws;
+  int64_t sk_cnt_off;
+  int sk_grid;
 };
 
 // Workspace slot of one 256 x 128 output tile of the K loop split across two workgroups: its
@@ -48,6 +52,9 @@ struct GemmParams {
 // of different sizes can share a workspace without one call's partial sums landing on another
 // tile's counter and flag.
 constexpr int64_t kSplitSlotBytes = 256 + 256 * 128 * 4;
+
+// Stream-K workspace slot: one 256 x 256 tile's fp32 partial sums.
+constexpr int64_t kStreamSlotBytes = 256 * 256 * 4;
 
 template <int DT> struct DTypeInfo;
 template <> struct DTypeInfo<F32> { static constexpr int bytes = 4; };

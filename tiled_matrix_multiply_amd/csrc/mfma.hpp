@@ -32,6 +32,7 @@
 // instruction writes whole cache lines.
 #pragma once
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -201,9 +202,11 @@ constexpr int default_stages() { return TILE == 128 ? 3 : 2; }
 // each walk every KS_-th K tile with their own LDS stages and add their accumulators at the
 // end (small problems, whose time is the chain of K tiles rather than the multiplies).
 // BN_: tile width along N (0: square, BN = TILE_).  SK_: the K loop split across workgroups,
-// 1 or 2: with 2, two workgroups share a tile, each multiplying one half of its K tiles; the
+// 1, 2 or 0: with 2, two workgroups share a tile, each multiplying one half of its K tiles; the
 // first to finish hands its fp32 accumulators to the other through a workspace in device memory
-// (a pair protocol, below), and the other adds them and runs the epilogue.
+// (a pair protocol, below), and the other adds them and runs the epilogue.  With 0 (stream-K)
+// a persistent grid shares out the K tiles of all output tiles evenly, in contiguous runs that
+// may start and end inside a tile; the parts of a split tile meet through the workspace.
 template <int DT_, int TILE_, int WM_, int WN_, bool A_MN_, bool B_MN_,
           int S_ = default_stages<TILE_>(), int BT_ = DT_, bool MX_ = false, int QB_ = 0,
           int KS_ = 1, int BN_ = 0, int SK_ = 1>
@@ -216,8 +219,9 @@ struct MfmaCfg {
   static constexpr int CT = F8 ? BF16 : DT_;
   static constexpr int BM = TILE_, BN = BN_ ? BN_ : TILE_;
   static constexpr int KS = KS_, SK = SK_;
-  static_assert(SK_ == 1 || (SK_ == 2 && KS_ == 1 && !MX_ && QB_ == 0),
-                "K split across workgroups: two halves, plain inputs, no split inside");
+  static_assert(SK_ == 1 || ((SK_ == 2 || SK_ == 0) && KS_ == 1 && !MX_ && QB_ == 0),
+                "K split across workgroups: plain inputs, no split inside");
+  static_assert(SK_ != 0 || (TILE_ == 256 && BN_ == 0), "stream-K runs the 256 x 256 tile");
   static constexpr int WM = WM_, WN = WN_, NW = WM_ * WN_, NT = NW * 64 * KS_;  // NW waves per K group
   // Waves that issue the K loop's copies.  The 256 x 256 tile runs two waves per SIMD; right
   // after each barrier every wave would issue its copies at once, the address unit's queue
@@ -353,8 +357,24 @@ __device__ __forceinline__ u32x4 load_partial(const uint8_t* src, int n) {
 // Flags computed on the host: which operands need the last-K-tile fix-up.
 enum : uint32_t { FIX_A = 1u << 8, FIX_B = 1u << 9 };
 
+// One stream-K segment: K tiles [kb, ke) of output tile `tile`, taken by contributor `part`
+// of the tile's `parts` (consecutive workgroups in the renumbered order, the first of them
+// `first_w`; parts == 1: the whole tile).
+struct SkSeg {
+  int tile, kb, ke, part, parts, first_w;
+};
+
+// Workspace slot of stream-K contributor `part` of a tile whose first contributor is workgroup
+// w0: each workgroup has two slots, 2 w for the segment its run starts with (the end of a
+// tile) and 2 w + 1 for the one its run ends with (the start of a tile, part 0).
+__device__ __forceinline__ int64_t sk_slot(int w0, int part) {
+  return 2 * (int64_t)(w0 + part) + (part == 0 ? 1 : 0);
+}
+
+// The work of one workgroup on one output tile (or, with stream-K, one segment of its K tiles),
+// from the copies of its first K tile to the stores of its epilogue.
 template <class C>
-__global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
+__device__ __forceinline__ void mfma_tile(const GemmParams p, const SkSeg sg) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
   using Op = typename C::Op;
   using OA = Operand<C, true>;
@@ -362,7 +382,15 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   constexpr int ES = C::ES;
   constexpr int G = C::BKE / Op::KG;  // k-groups per staged tile
 
-  const int tid = threadIdx.x, lane = tid & 63, lane_id = lane;
+  // (stream-K: the lane index from an instruction the compiler cannot hoist out of the loop
+  // over segments; the wave's base index is scalar)
+  int tid_l = threadIdx.x;
+  if constexpr (C::SK == 0) {
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    tid_l = (int)(__builtin_amdgcn_readfirstlane(threadIdx.x) & ~63u) | ln;
+  }
+  const int tid = tid_l, lane = tid & 63, lane_id = lane;
   // K group (0 unless the K loop is split), wave-uniform so that tile addresses stay scalar
   const int kg = __builtin_amdgcn_readfirstlane((tid >> 6) / C::NW);
   const int wave = (tid >> 6) % C::NW;  // wave within the group
@@ -374,12 +402,20 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   // tiles on one XCD share A and B panels in that XCD's L2.
   // With the K loop split across workgroups, the SK workgroups of a tile get consecutive ids
   // after the renumbering, so that both halves of a tile run on one XCD and meet in its L2.
+  // With stream-K the segment names the tile (its grid is renumbered the same way, below).
   int bid = blockIdx.x;
-  const int T = p.tiles_m * p.tiles_n;
-  const int U = T * C::SK;  // workgroups
-  if ((U & 7) == 0) bid = (bid & 7) * (U >> 3) + (bid >> 3);
-  const int khalf = C::SK > 1 ? bid % C::SK : 0;  // which part of the K tiles this workgroup takes
-  if constexpr (C::SK > 1) bid /= C::SK;
+  int khalf = 0;  // which part of the K tiles this workgroup takes (K split across workgroups)
+  if constexpr (C::SK == 0) {
+    bid = sg.tile;
+  } else {
+    const int T = p.tiles_m * p.tiles_n;
+    const int U = T * C::SK;  // workgroups
+    if ((U & 7) == 0) bid = (bid & 7) * (U >> 3) + (bid >> 3);
+    if constexpr (C::SK > 1) {
+      khalf = bid % C::SK;
+      bid /= C::SK;
+    }
+  }
   const int tile_id = bid;
   const int per_group = TILE_GROUP_M * p.tiles_n;
   const int first_m = (bid / per_group) * TILE_GROUP_M;
@@ -806,10 +842,11 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
   // counts iterations, which are tiles when KS = 1.
   // With the K loop split across workgroups (SK = 2), part h takes the K tiles
   // [h KH, min((h+1) KH, KT_ALL)), KH = ceil(KT_ALL / 2).
+  // With stream-K the segment's K tiles [sg.kb, sg.ke).
   const int KT_ALL = (p.K + C::BKE - 1) / C::BKE;
-  const int KH = (KT_ALL + C::SK - 1) / C::SK;
-  const int kbeg = khalf * KH;
-  const int KT_SK = C::SK > 1 ? max(0, min(KH, KT_ALL - kbeg)) : KT_ALL;
+  const int KH = C::SK > 1 ? (KT_ALL + C::SK - 1) / C::SK : KT_ALL;
+  const int kbeg = C::SK == 0 ? sg.kb : khalf * KH;
+  const int KT_SK = C::SK == 0 ? sg.ke - sg.kb : C::SK > 1 ? max(0, min(KH, KT_ALL - kbeg)) : KT_ALL;
   const int NI = C::KS == 1 ? KT_SK : (KT_ALL + C::KS - 1) / C::KS;
   const int KT = C::KS == 1 ? KT_SK : (KT_ALL - kg + C::KS - 1) / C::KS;
   auto tile_of = [&](int i) { return C::KS == 1 ? kbeg + i : i * C::KS + kg; };
@@ -1139,6 +1176,101 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
         }
   }
 
+  if constexpr (C::SK == 0) {
+    // Stream-K: the parts of a split tile meet through the workspace.  Per tile, an [arrive,
+    // done] pair of counters (both zero between calls).  Each part takes a ticket from
+    // `arrive` when it leaves its K loop.  Every part but the last to arrive publishes its fp32
+    // accumulators in its own slot and counts itself in `done`; the last one waits until
+    // `done` shows all the others, adds their sums and runs the epilogue.  So the wait is only
+    // ever for parts that have already left their K loops and have only their stores and one
+    // atomic left: no co-residency of the grid is assumed, and the spin is bounded all the
+    // same.  The sum runs in part order whichever part arrives last (((p0 + p1) + p2) + ...;
+    // a last arriver that is not part 0 publishes its own sums too and reads them back), so the
+    // result is the same bits on every run.  The last arriver then sets both counters back to
+    // zero: every part has already counted itself in both.  Coherence as in the pair protocol
+    // above: device-scope (sc1) stores and loads of the sums, stores complete before `done`
+    // moves, device-scope atomics for the counters.
+    if (sg.parts > 1) {
+      __shared__ uint32_t sk_ticket;
+      constexpr int64_t SLOT = (int64_t)C::BM * C::BN * 4;
+      static_assert(SLOT == kStreamSlotBytes, "one workspace slot holds a tile's fp32 sums");
+      // The segment's numbers and the ticket are workgroup-uniform: read them into scalar
+      // registers, so that the slots' buffer descriptors are scalar and every load and store
+      // below is issued back to back (the compiler otherwise wrapped each in a loop over the
+      // lanes' descriptors, one access in flight at a time).
+      const int part = __builtin_amdgcn_readfirstlane(sg.part);
+      const int parts = __builtin_amdgcn_readfirstlane(sg.parts);
+      const int first_w = __builtin_amdgcn_readfirstlane(sg.first_w);
+      const int tile = __builtin_amdgcn_readfirstlane(sg.tile);
+      uint32_t* const cnt = reinterpret_cast<uint32_t*>(p.sk_ws + p.sk_cnt_off) + 2 * (int64_t)tile;
+      constexpr int NF = C::FM * C::FN * 4;  // float4 pieces per lane
+      constexpr int DEVICE_SCOPE = 16;       // sc1 cache-policy bit
+      const int pbase = (wave * NF * 64 + lane) * 16;
+      auto slot_rsrc = [&](int q) {
+        return __builtin_amdgcn_make_buffer_rsrc(p.sk_ws + sk_slot(first_w, q) * SLOT, (short)0,
+                                                 (int)SLOT, BUFFER_FLAGS);
+      };
+      __syncthreads();  // every wave has left the K loop
+      if (tid == 0) sk_ticket = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const bool last = __builtin_amdgcn_readfirstlane(sk_ticket) == (uint32_t)(parts - 1);
+      if (!last || part != 0) {
+        const __amdgpu_buffer_rsrc_t own = slot_rsrc(part);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 v = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), own,
+                                                     pbase + ((i * C::FN + j) * 4 + q) * 64 * 16, 0, DEVICE_SCOPE);
+            }
+        wait_vmcnt<0>();  // this wave's stores are complete
+        __syncthreads();
+        if (!last) {
+          if (tid == 0) __hip_atomic_fetch_add(cnt + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          return;
+        }
+      }
+      if (tid == 0) {
+        for (uint32_t n = 0; n < (1u << 22); ++n) {
+          if (__hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(parts - 1)) break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();  // the loads below are issued after the count was seen
+      // one accumulator row (FN x 4 pieces) of loads in flight before its adds
+      for (int k = part == 0 ? 1 : 0; k < parts; ++k) {
+        const __amdgpu_buffer_rsrc_t src = slot_rsrc(k);
+#pragma unroll
+        for (int i0 = 0; i0 < C::FM; i0 += 2) {
+          f32x4 v[2][C::FN][4];
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              v[ii][j][q] = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(src, pbase + (((i0 + ii) * C::FN + j) * 4 + q) * 64 * 16, 0,
+                                                              DEVICE_SCOPE));
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[i0 + ii][j][4 * q + e] = k == 0 ? v[ii][j][q][e] : acc[i0 + ii][j][4 * q + e] + v[ii][j][q][e];
+        }
+      }
+    }
+  }
+
   // Epilogue in registers.  Lane (lrow, lhalf) of accumulator (i, j) holds rows
   // m = m0 + wm*WTM + 32 i + lrow and, in register group rg, the 4 consecutive columns
   // n = n0 + wn*WTN + 32 j + 8 rg + 4 lhalf (+0..3).
@@ -1270,6 +1402,56 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
 }
 
 template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
+  if constexpr (C::SK != 0) {
+    mfma_tile<C>(p, SkSeg{});
+  } else {
+    // Stream-K: a persistent grid of G workgroups shares out the I = tiles x KT K tiles of the
+    // product, workgroup L taking the run [floor(L I / G), floor((L+1) I / G)) of the tile-major
+    // sequence (output tile t owns K tiles [t KT, (t+1) KT)) and walking it segment by segment,
+    // one output tile at a time.  K tile x belongs to workgroup floor(((x+1) G - 1) / I), which
+    // gives every segment its tile's contributors.  Workgroups are renumbered as for the other
+    // kernels, so that each XCD takes a contiguous range of runs: the parts of a tile mostly
+    // meet in one XCD's L2.
+    // Registers: held across segments, the run's bounds and the body's loop-invariant offsets
+    // made the kernel spill inside its K loop.  So the run's state lives in LDS (read again
+    // after each segment, whose barriers order it), and each segment recomputes its lane index
+    // (an opaque instruction, below), so that what derives from it is not kept from one segment
+    // to the next.  What still spills (a few scalars and three words per lane) is read once per
+    // segment, outside the K loop.
+    // (One workgroup per segment instead, in rounds, needs no loop and spills nothing, but the
+    // dispatcher then hands the later segments out unevenly: measured 3072 x 4096 x 4096 150 us
+    // against 117 us persistent.)
+    __shared__ int64_t run[4];  // [next K tile, end of the run, I, G | L << 32]
+    if (threadIdx.x == 0) {
+      const int G = (int)gridDim.x;
+      int L = (int)blockIdx.x;
+      if ((G & 7) == 0) L = (L & 7) * (G >> 3) + (L >> 3);
+      const int64_t I = (int64_t)p.tiles_m * p.tiles_n * ((p.K + C::BKE - 1) / C::BKE);
+      run[0] = (int64_t)L * I / G;
+      run[1] = (int64_t)(L + 1) * I / G;
+      run[2] = I;
+      run[3] = (int64_t)G | ((int64_t)L << 32);
+    }
+    __syncthreads();
+    for (bool first = true;; first = false) {
+      const int64_t it = run[0], end = run[1], I = run[2];
+      const int G = (int)(run[3] & 0xffffffff), L = (int)(run[3] >> 32);
+      if (it >= end) break;
+      const int KT = (p.K + C::BKE - 1) / C::BKE;
+      const int t = (int)(it / KT);
+      const int64_t t0 = (int64_t)t * KT;
+      const int kb = (int)(it - t0), ke = (int)min((int64_t)KT, end - t0);
+      const int w0 = (int)(((t0 + 1) * G - 1) / I), w1 = (int)(((t0 + KT) * G - 1) / I);
+      // every thread has read the position, and the previous segment is done with LDS
+      if (!first) __syncthreads();
+      if (threadIdx.x == 0) run[0] = t0 + ke;  // published by the segment's own barriers
+      mfma_tile<C>(p, SkSeg{t, kb, ke, L - w0, w1 - w0 + 1, w0});
+    }
+  }
+}
+
+template <class C>
 hipError_t launch_mfma_cfg(GemmParams p, hipStream_t s) {
   const int64_t T = (int64_t)p.tiles_m * p.tiles_n;
   // Last-K-tile fix-ups: a K-contiguous operand whose K is not a whole number of tiles, or an
@@ -1278,7 +1460,9 @@ hipError_t launch_mfma_cfg(GemmParams p, hipStream_t s) {
   const bool fix_a = C::A_MN ? (p.M % CE != 0) : (p.K % C::BKE != 0);
   const bool fix_b = C::B_MN ? (p.N % CE != 0) : (p.K % C::BKE != 0);
   p.epi |= (fix_a ? FIX_A : 0u) | (fix_b ? FIX_B : 0u);
-  hipLaunchKernelGGL((gemm_mfma_kernel<C>), dim3((unsigned)(T * C::SK)), dim3(C::NT), 0, s, p);
+  // stream-K: a persistent grid of p.sk_grid workgroups (at most one per K tile)
+  const int64_t grid = C::SK == 0 ? p.sk_grid : T * C::SK;
+  hipLaunchKernelGGL((gemm_mfma_kernel<C>), dim3((unsigned)grid), dim3(C::NT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1321,6 +1505,14 @@ hipError_t launch_mfma_dtype(const GemmParams& p, int tile, bool a_mn, bool b_mn
       if (ks != 1) return hipErrorInvalidValue;
       if (tile == 6) return launch_mfma_layout<DT, 256, 4, 2, BT, MX, 1, 128, 2>(p, a_mn, b_mn, s);
       return launch_mfma_layout<DT, 256, 4, 2, BT, MX, 1, 128, 1>(p, a_mn, b_mn, s);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
+  if (tile == 7) {  // 256 x 256, stream-K over a persistent grid
+    if constexpr ((DT == F16 || DT == BF16) && !MX) {
+      if (ks != 1) return hipErrorInvalidValue;
+      return launch_mfma_layout<DT, 256, 2, 4, BT, MX, 1, 0, 0>(p, a_mn, b_mn, s);
     } else {
       return hipErrorInvalidValue;
     }

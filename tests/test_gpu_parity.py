@@ -356,6 +356,25 @@ SHAPES = [(1, 1, 1), (31, 33, 17), (64, 64, 64), (65, 63, 129), (257, 255, 1), (
           (1000, 777, 333), (130, 1030, 40)]
 
 
+@pytest.mark.parametrize("dtype,kernel", [(d, k) for d in ("f32", "bf16")
+                                           for k in ("mfma64", "mfma128", "mfma256")])
+def test_edge_granules(g, dtype, kernel):
+    """Edge tiles store whole 16-byte granules where they lie inside the matrix and the one
+    granule that straddles column N element by element: N of every remainder class against the
+    granule (1, 2, 3, 6 and 7 elements past a boundary of 8 for 16-bit outputs, 1 to 3 of 4 for
+    fp32), ragged M, beta (masked C loads at the edge), bias and GELU; padding poisoned with NaN
+    must come back intact."""
+    for i, N in enumerate((257, 258, 259, 262, 263, 513)):
+        M, K = 300 + 17 * i, 96 + 8 * i
+        p = W.make_problem(M, N, K, a_type=dtype, alpha=0.75, beta=0.5, seed=700 + i,
+                           dist_a=("normal", 1.0), dist_b=("normal", K ** -0.5),
+                           epilogue=W.EPI_BIAS | W.EPI_GELU)
+        got, kname, pad_ok = H.run_padded(g, p, kernel=KERNELS[kernel])
+        res = H.gate_full(p, got)
+        _report(f"{dtype} {M}x{N}x{K} {kname} edge granules", res)
+        assert kname and pad_ok and res.ok, (N, res)
+
+
 @pytest.mark.parametrize("dtype,kernel",
                          [(d, k) for d in ("f32", "f16", "bf16", "e4m3")
                           for k in ("auto", "simt", "mfma64", "mfma128", "mfma256", "mfma32")

@@ -1279,24 +1279,38 @@ __device__ __forceinline__ void mfma_tile(const GemmParams p, const SkSeg sg) {
   const uint32_t epi = p.epi & (EPI_BIAS | EPI_GELU);
   const int mw = m0 + wm * C::WTM + lrow;
   const int nw = n0 + wn * C::WTN + lhalf * 4;
-  if (full) {
-    // Interior tile: no masks.  The bias values of the lane's columns are fetched in one batch
-    // (a single wait), each row's C values (beta != 0) likewise, and the element loop is
-    // specialised on (beta != 0, GELU) so that it carries no branches: this loop runs on the
-    // vector ALUs after the last multiply, so every instruction in it is paid in full.
+  {
+    // Interior tiles carry no masks.  The bias values of the lane's columns are fetched in one
+    // batch (a single wait), each row's C values (beta != 0) likewise, and the element loop is
+    // specialised on (beta != 0, GELU, edge) so that it carries no branches: this loop runs on
+    // the vector ALUs after the last multiply, so every instruction in it is paid in full.
+    // Edge tiles (past M or N) take the same path with masked bias and C loads and masked
+    // stores, so that their stores are full granules too wherever the granule lies inside.
     // With GELU and a 16-bit output the element loop computes y = x / 2 (alpha, beta and the
     // bias halved, an exact scaling) and gelu16_half(y).
     const bool half = C::CT != F32 && (epi & EPI_GELU);
     const float hs = half ? 0.5f : 1.0f;
     float bj[C::FN][4][4];
+    if (full) {
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
+      for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        // four scalar loads (the bias need only be 4-byte aligned); they merge into one
+        for (int rg = 0; rg < 4; ++rg) {
+          // four scalar loads (the bias need only be 4-byte aligned); they merge into one
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bj[j][rg][e] = (epi & EPI_BIAS) ? hs * p.bias[nw + 32 * j + 8 * rg + e] : 0.0f;
-      }
+          for (int e = 0; e < 4; ++e) bj[j][rg][e] = (epi & EPI_BIAS) ? hs * p.bias[nw + 32 * j + 8 * rg + e] : 0.0f;
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int n = nw + 32 * j + 8 * rg + e;
+            bj[j][rg][e] = ((epi & EPI_BIAS) && n < p.N) ? hs * p.bias[n] : 0.0f;
+          }
+    }
     const float alpha_e = hs * alpha, beta_e = hs * beta;
     // Output staging.  In the accumulator layout one store instruction would write 32 rows x
     // 16 bytes, 32 partial cache lines that L2 merges one request at a time.  Instead each wave
@@ -1306,25 +1320,34 @@ __device__ __forceinline__ void mfma_tile(const GemmParams p, const SkSeg sg) {
     // which LDS is not read, and no copy is in flight.  Granule g of staged row r sits at
     // position g ^ (r % GPR), which keeps the row-wise read-back free of bank conflicts.
     constexpr int OES = C::CT == F32 ? 4 : 2;           // output element bytes
+    constexpr int EPG = 16 / OES;                        // elements per granule
     constexpr int ROWB = C::WTN * OES, GPR = ROWB / 16;  // staged row bytes, granules per row
     constexpr int CHUNK = 32 * ROWB;                      // one wave's region
     static_assert(C::STG_OFF + C::NW * CHUNK <= C::LDS_BYTES, "output staging fits the K loop's LDS");
     uint8_t* const ostage = smem + C::STG_OFF + wave_u * CHUNK;
     const int m_w0 = m0 + wm * C::WTM, n_w0 = n0 + wn * C::WTN;
     typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-    auto store_tile = [&](auto has_beta, auto has_gelu) {
+    auto store_tile = [&](auto has_beta, auto has_gelu, auto is_edge) {
       constexpr bool HB = decltype(has_beta)::value, HG = decltype(has_gelu)::value;
+      constexpr bool EDGE = decltype(is_edge)::value;
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
-        const int64_t row = (int64_t)(mw + 32 * i) * p.ldc;  // this lane's row (beta != 0 loads)
+        const int m = mw + 32 * i;                     // this lane's row (beta != 0 loads)
+        const int64_t row = (int64_t)m * p.ldc;
         float cin[C::FN][4][4];
         if constexpr (HB) {
 #pragma unroll
           for (int j = 0; j < C::FN; ++j)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-              const int64_t idx = row + nw + 32 * j + 8 * rg;
-              if constexpr (C::CT == F32) {
+              const int n = nw + 32 * j + 8 * rg;
+              const int64_t idx = row + n;
+              if (EDGE && !(m < p.M && n + 3 < p.N)) {
+                // a run of four that leaves the matrix: element by element
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  cin[j][rg][e] = (m < p.M && n + e < p.N) ? load_as_float<C::CT>(p.C, idx + e) : 0.0f;
+              } else if constexpr (C::CT == F32) {
                 const float4 c4 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.C) + idx);
                 cin[j][rg][0] = c4.x; cin[j][rg][1] = c4.y; cin[j][rg][2] = c4.z; cin[j][rg][3] = c4.w;
               } else {
@@ -1360,44 +1383,33 @@ __device__ __forceinline__ void mfma_tile(const GemmParams p, const SkSeg sg) {
         for (int q = 0; q < GPR / 2; ++q) {
           const int L = 64 * q + lane, r = L / GPR, g = L % GPR;
           const u32x4 val = *reinterpret_cast<const u32x4*>(ostage + r * ROWB + 16 * (g ^ (r % GPR)));
-          uint8_t* dst = reinterpret_cast<uint8_t*>(p.C) +
-                         ((int64_t)(m_w0 + 32 * i + r) * p.ldc + n_w0 + g * (16 / OES)) * OES;
-          // non-temporal: C is not read again here, and lines the L2 does not keep dirty
-          // need no write-back when the kernel ends (1.3 us less per 4096^3 launch)
-          __builtin_nontemporal_store(val, reinterpret_cast<u32x4_a4*>(dst));
-        }
-      }
-    };
-    if (beta != 0.0f) {
-      if (epi & EPI_GELU) store_tile(std::true_type{}, std::true_type{});
-      else store_tile(std::true_type{}, std::false_type{});
-    } else {
-      if (epi & EPI_GELU) store_tile(std::false_type{}, std::true_type{});
-      else store_tile(std::false_type{}, std::false_type{});
-    }
-  } else {
-    // Edge tile: per-element masks on both axes.
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-      const int m = mw + 32 * i;
-      if (m >= p.M) continue;
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int n = nw + 32 * j + 8 * rg;
-          const int64_t idx = (int64_t)m * p.ldc + n;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (n + e < p.N) {
-              const float cin = beta != 0.0f ? load_as_float<C::CT>(p.C, idx + e) : 0.0f;
-              const float bj = (epi & EPI_BIAS) ? p.bias[n + e] : 0.0f;
-              store_from_float<C::CT>(p.C, idx + e,
-                                      epilogue_value<C::CT>(acc[i][j][rg * 4 + e], alpha, beta, cin, bj, epi));
+          const int gm = m_w0 + 32 * i + r, gn = n_w0 + g * EPG;
+          uint8_t* dst = reinterpret_cast<uint8_t*>(p.C) + ((int64_t)gm * p.ldc + gn) * OES;
+          if (!EDGE || (gm < p.M && gn + EPG <= p.N)) {
+            // non-temporal: C is not read again here, and lines the L2 does not keep dirty
+            // need no write-back when the kernel ends (1.3 us less per 4096^3 launch)
+            __builtin_nontemporal_store(val, reinterpret_cast<u32x4_a4*>(dst));
+          } else if (gm < p.M && gn < p.N) {
+            // the granule that straddles column N: its elements up to N one by one
+            for (int e = 0; e < p.N - gn; ++e) {
+              if constexpr (OES == 4) reinterpret_cast<uint32_t*>(dst)[e] = val[e];
+              else reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(val[e >> 1] >> ((e & 1) * 16));
             }
           }
         }
-    }
+      }
+    };
+    auto store_any = [&](auto is_edge) {
+      if (beta != 0.0f) {
+        if (epi & EPI_GELU) store_tile(std::true_type{}, std::true_type{}, is_edge);
+        else store_tile(std::true_type{}, std::false_type{}, is_edge);
+      } else {
+        if (epi & EPI_GELU) store_tile(std::false_type{}, std::true_type{}, is_edge);
+        else store_tile(std::false_type{}, std::false_type{}, is_edge);
+      }
+    };
+    if (full) store_any(std::false_type{});
+    else store_any(std::true_type{});
   }
 }
 

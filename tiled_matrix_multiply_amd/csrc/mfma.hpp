@@ -759,21 +759,30 @@ __device__ __forceinline__ void mfma_tile(const GemmParams p, const SkSeg sg) {
   // the scales of tile kt (read by read_tile_scales(kt)) into the registers the multiplies use
   auto next_tile_scales = [&](int kt) {
     if constexpr (C::MX) {
-      uint32_t fix = 0;  // bytes of blocks past K
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-        if (kt * C::BPT + 2 * g + lhalf >= p.kblocks) fix |= 0xFFu << (8 * OPS(g));
       auto pack = [&](const uint32_t (&w)[RW]) {
         // 8 blocks: this lane half's four (bytes h, 2+h, 4+h, 6+h); 4 blocks: its two, to
         // bytes 0 and 2
-        const uint32_t v = RW == 2 ? __builtin_amdgcn_perm(w[RW - 1], w[0], lhalf ? 0x07050301u : 0x06040200u)
-                                   : w[0] >> (8 * lhalf);
-        return (v & ~fix) | (0x7F7F7F7Fu & fix);
+        return RW == 2 ? __builtin_amdgcn_perm(w[RW - 1], w[0], lhalf ? 0x07050301u : 0x06040200u)
+                       : w[0] >> (8 * lhalf);
       };
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) scAc[i] = pack(rAn[i]);
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) scBc[j] = pack(rBn[j]);
+      // Only a tile that reaches past K (the last, when K is not a whole number of tiles) has
+      // blocks to force to 2^0: a uniform branch, so that the other tiles' first multiplies
+      // wait on nothing but the byte permutes.
+      // (block-scaled kernels never split K, so iteration kt is K tile kt)
+      if (kt * C::BPT + C::BPT > p.kblocks) {
+        uint32_t fix = 0;  // bytes of blocks past K
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          if (kt * C::BPT + 2 * g + lhalf >= p.kblocks) fix |= 0xFFu << (8 * OPS(g));
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) scAc[i] = (scAc[i] & ~fix) | (0x7F7F7F7Fu & fix);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) scBc[j] = (scBc[j] & ~fix) | (0x7F7F7F7Fu & fix);
+      }
     }
   };
   auto load_a = [&](uint32_t aoff, int g, int i, Frag& dst) {

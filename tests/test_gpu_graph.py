@@ -1,8 +1,9 @@
 """The library's calls allocate nothing, keep no per-call host state and record no memset, so a
-HIP graph can capture them: a captured gemm_run (bf16 GEMM + bias + GELU, and block-scaled fp8)
-and a captured gemm_run_q (the quantized decode) are replayed several times, with the program's
-own eager work and synchronisations between replays, and every replay must equal the eager
-result bit for bit."""
+HIP graph can capture them: a captured gemm_run (bf16 GEMM + bias + GELU, and block-scaled fp8),
+a captured gemm_run_q (the quantized decode) and the two kernels that meet through a caller
+workspace (the K loop split across two workgroups, and stream-K) are replayed several times,
+with the program's own eager work and synchronisations between replays, and every replay must
+equal the eager result bit for bit."""
 import numpy as np
 import pytest
 
@@ -89,3 +90,41 @@ def test_gemm_run_q_in_a_graph(g):
     assert np.any(eager != 0)
     for i, o in enumerate(outs):
         assert np.array_equal(o, eager), f"replay {i}"
+
+
+@pytest.mark.parametrize("kernel", [9, 10])  # GEMM_KERNEL_MFMA_256x128_SK2, GEMM_KERNEL_MFMA_256_SK
+def test_split_kernels_in_a_graph(g, kernel):
+    """The two kernels that exchange partial sums through a workspace leave it ready for the
+    next call from inside the kernel (no memset to record), so a captured call replays
+    correctly: every replay equals the eager run bit for bit, and the workspace's counters come
+    back ready each time.  1000 x 1304 x 3000 cuts stream-K's tiles into up to 11 parts."""
+    import torch
+    import tiled_matrix_multiply_amd as tmm
+    p = W.make_problem(1000, 1304, 3000, a_type="bf16", seed=81, dist_a=("normal", 1.0),
+                       dist_b=("normal", 3000 ** -0.5), epilogue=W.EPI_BIAS | W.EPI_GELU)
+    d = H.Device(p)
+    nbytes = tmm.gemm_kernel_workspace_bytes(g.handle, kernel, p.M, p.N)
+    ws = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda:0")
+
+    def call():
+        tmm.run(g.handle, d.A, d.B, d.C, M=p.M, N=p.N, K=p.K, alpha=p.alpha, beta=p.beta,
+                a_type=p.a_type, c_type=p.c_type, epilogue=p.epilogue, bias=d.bias,
+                kernel=kernel, workspace=ws, workspace_bytes=nbytes)
+
+    eager, outs = _capture_and_replay(call, d.C, p.c_type)
+    assert np.any(eager != 0)
+    for i, o in enumerate(outs):
+        assert np.array_equal(o, eager), f"replay {i}"
+    res = H.gate_full(p, __import__("oracle").decode(p.c_type, eager))
+    assert res.ok, res
+    words = ws.cpu().numpy().view(np.uint32)
+    if kernel == 10:
+        cu = torch.cuda.get_device_properties(0).multi_processor_count
+        tiles = (-(-p.M // 256)) * (-(-p.N // 256))
+        off = 2 * cu * 256 * 256
+        assert (words[off:off + 2 * tiles] == 0).all()
+    else:
+        slot = tmm.SPLIT_K_SLOT_BYTES // 4
+        tiles = (-(-p.M // 256)) * (-(-p.N // 128))
+        sync = np.array([(words[t * slot], words[t * slot + 1]) for t in range(tiles)])
+        assert (sync[:, 0] % 2 == 0).all() and (sync[:, 1] == sync[:, 0] // 2).all()

@@ -110,6 +110,9 @@ def test_integer_inputs_bit_exact(g, dtype, ta, tb):
     ("bf16", 4352, 4352, 520, False, False),   # 289 tiles, more than compute units; ragged K
     ("bf16", 2304, 2560, 2048, True, True),    # 90 tiles
     ("f16", 100, 100, 20000, False, True),     # one tile cut into 256 parts
+    ("bf16", 520, 1000, 1, True, False),       # K = 1: one K tile per output tile, none split
+    ("f16", 4352, 1000, 64, False, False),     # 68 tiles of one K tile each
+    ("bf16", 4352, 4352, 130, True, True),     # 289 tiles of 3 K tiles: runs span whole tiles
 ])
 def test_gated_every_entry(g, dtype, M, N, K, ta, tb):
     """Random operands with beta, bias and GELU: every entry of the result meets the oracle's

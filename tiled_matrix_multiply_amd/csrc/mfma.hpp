@@ -1455,7 +1455,7 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
       run[3] = (int64_t)G | ((int64_t)L << 32);
     }
     __syncthreads();
-    for (bool first = true;; first = false) {
+    for (;;) {
       const int64_t it = run[0], end = run[1], I = run[2];
       const int G = (int)(run[3] & 0xffffffff), L = (int)(run[3] >> 32);
       if (it >= end) break;
@@ -1464,8 +1464,9 @@ __global__ __launch_bounds__(C::NT) void gemm_mfma_kernel(GemmParams p) {
       const int64_t t0 = (int64_t)t * KT;
       const int kb = (int)(it - t0), ke = (int)min((int64_t)KT, end - t0);
       const int w0 = (int)(((t0 + 1) * G - 1) / I), w1 = (int)(((t0 + KT) * G - 1) / I);
-      // every thread has read the position, and the previous segment is done with LDS
-      if (!first) __syncthreads();
+      // Every thread has read the position (so that all walk the same segment and meet the
+      // same barriers), and the previous segment is done with LDS.
+      __syncthreads();
       if (threadIdx.x == 0) run[0] = t0 + ke;  // published by the segment's own barriers
       mfma_tile<C>(p, SkSeg{t, kb, ke, L - w0, w1 - w0 + 1, w0});
     }

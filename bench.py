@@ -158,6 +158,7 @@ class Cell:
         self.p = p
         self.unfused = unfused
         self.launches_per_step = 2 if unfused else 1
+        self._dev, self._C0 = dev, p.C  # to restore C before the gate's fresh step
         self.A, self.B, self.C = dev(p.A), dev(p.B), dev(p.C)
         self.bias = dev(p.bias) if p.bias is not None else None
         self.stream = torch.cuda.current_stream()
@@ -256,6 +257,21 @@ class Cell:
         self.sclk = clock.read() if clock is not None else None
         return ms
 
+    def result_sample(self, n: int = 512, seed: int = 0) -> dict:
+        """One fresh step (C first restored to its initial contents when beta != 0, since the
+        timed steps fed each result back in) and the stored output words at n seeded points,
+        for the checksum gate of the CPU leg."""
+        import torch
+        p = self.p
+        if p.beta != 0:
+            self.C.copy_(self._dev(self._C0))
+        self.step()
+        torch.cuda.synchronize()
+        out = self.C.cpu().numpy()
+        rows, cols = gate_points(p.M, p.N, n, seed)
+        raw = out[rows, cols]
+        return {"rows": rows, "cols": cols, "raw": raw.view(np.uint16) if raw.dtype == np.int16 else raw}
+
     def algorithmic_bytes(self) -> int:
         p = self.p
         import workloads as W
@@ -289,6 +305,7 @@ class QCell:
 
         self.p = q
         self.launches_per_step = 1
+        self._dev, self._C0 = dev, q.C
         self.X, self.C = dev(q.X), dev(q.C)
         self.bias = dev(q.bias) if q.bias is not None else None
         self.W = [(dev(q.Wq), dev(q.scales), dev(q.offsets)) for _ in range(copies)]
@@ -319,6 +336,7 @@ class QCell:
 
     settle = Cell.settle
     time = Cell.time
+    result_sample = Cell.result_sample
 
     def algorithmic_bytes(self) -> int:
         q = self.p
@@ -436,7 +454,7 @@ def summarize(name, cell: Cell, ms: np.ndarray, dtype: str) -> dict:
     tf = p.flops / (med * 1e-3) / 1e12
     row = {"cell": name, "kernel": cell.kernel, "M": p.M, "N": p.N, "K": p.K, "dtype": dtype,
            "seed": p.recipe.get("seed"), "recipe_hash": recipe_hash(p.recipe),
-           "reps": int(len(ms)), "median_us": round(med * 1e3, 3),
+           "flops": int(p.flops), "reps": int(len(ms)), "median_us": round(med * 1e3, 3),
            "ci95_us": [round(hi_ * 1e3, 3) for hi_ in (lo, hi)],
            "tflops": round(tf, 2),
            "tflops_ci95": [round(p.flops / (hi * 1e-3) / 1e12, 2),
@@ -475,6 +493,141 @@ def read_counters(src_hash: str) -> dict:
     return out
 
 
+def gate_points(M: int, N: int, n: int, seed: int):
+    """n output coordinates for the checksum gate: the four corners, then seeded uniform
+    draws (numpy PCG64)."""
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([[0, 0, M - 1, M - 1], rng.integers(0, M, max(0, n - 4))])
+    cols = np.concatenate([[0, N - 1, 0, N - 1], rng.integers(0, N, max(0, n - 4))])
+    return rows.astype(np.int64), cols.astype(np.int64)
+
+
+def gate_sample(p, sample: dict, quantized: bool, unfused: bool):
+    """The checksum gate ("Rigel" section 3: a float64 reference from the same stored bytes,
+    per-dtype tolerance) on a cell's sampled outputs: part of the CPU leg, which alone calls
+    the oracle.  Returns the gate's verdict as a dict."""
+    import oracle
+    from oracle import gate
+    import workloads as W
+    rows, cols = sample["rows"], sample["cols"]
+    if quantized:
+        Cref, D = oracle.qgemm_points(p, rows, cols)
+        ct = p.x_type
+    else:
+        Cref, D = oracle.gemm_points(p, rows, cols)
+        ct = p.c_type
+    gelu = bool(p.epilogue & W.EPI_GELU)
+    tol = gate.tolerance(p.K, ct, 2 if unfused else 1, gelu)
+    cin = oracle.decode(ct, p.C[rows, cols]) if p.beta != 0 else None
+    res = gate.check(oracle.decode(ct, sample["raw"]), Cref, D, tol, ct, p.beta, cin)
+    return {"n": res.n_checked, "max_err": res.max_err, "tol": res.tol, "pass": res.ok,
+            "c_type": ct, "roundings": 2 if unfused else 1, "gelu": gelu}
+
+
+CSV_FIELDS = ("cell", "kernel", "dtype", "c_type", "M", "N", "K", "flops", "seed", "recipe_hash",
+              "reps", "median_us", "ci95_lo_us", "ci95_hi_us", "tflops", "peak_tflops",
+              "pct_peak", "graph_us", "gate_n", "gate_max_err", "gate_tol", "gate_roundings",
+              "gate_gelu", "gate_pass", "commit", "sources", "gpu", "cus")
+
+
+def write_csv(path: str, rows: list, prov: dict, src_hash: str) -> None:
+    """One line per cell (the headline first): the raw measurements, the derived rates and the
+    gate's numbers, with the provenance each line needs to be used ("Rigel" section 3)."""
+    import csv
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=CSV_FIELDS)
+        w.writeheader()
+        for r in rows:
+            gt = r.get("gate") or {}
+            w.writerow({"cell": r["cell"], "kernel": r["kernel"], "dtype": r["dtype"],
+                        "c_type": gt.get("c_type", ""), "M": r["M"], "N": r["N"], "K": r["K"],
+                        "flops": r["flops"], "seed": r["seed"], "recipe_hash": r["recipe_hash"],
+                        "reps": r["reps"], "median_us": r["median_us"],
+                        "ci95_lo_us": r["ci95_us"][0], "ci95_hi_us": r["ci95_us"][1],
+                        "tflops": r["tflops"], "peak_tflops": PEAK_TFLOPS[r["dtype"]],
+                        "pct_peak": r["pct_peak"], "graph_us": r.get("graph_us"),
+                        "gate_n": gt.get("n", ""), "gate_max_err": gt.get("max_err", ""),
+                        "gate_tol": gt.get("tol", ""), "gate_roundings": gt.get("roundings", ""),
+                        "gate_gelu": gt.get("gelu", ""), "gate_pass": gt.get("pass", ""),
+                        "commit": prov.get("commit", ""), "sources": src_hash,
+                        "gpu": prov.get("gpu", ""), "cus": prov.get("cus", "")})
+
+
+# The re-verifier restates what it checks from the published figures, not from the code that
+# wrote the file: the dense peaks of MI355X per input type (TFLOP/s) and the gate's tolerance,
+# K 2^-23 + (1 + (roundings - 1) 1.1289) u_out + 4 2^-24 (+ 16 2^-24 with GELU), with u_out
+# the unit roundoff of the output type.
+_RV_PEAK = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2,
+            "e2m1": 10066.3, "e2m3": 10066.3, "e3m2": 10066.3}
+_RV_U = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+def reverify(path: str) -> int:
+    """Re-derive every line's rates and gate verdict from its raw columns and report the lines
+    that disagree (no GPU, no oracle): flops = 2 M N K; TFLOP/s from the median; the % of the
+    type's peak; the median inside its 95% interval; pass exactly when max_err <= tol, with the
+    tolerance recomputed; provenance present.  Returns the number of disagreeing lines."""
+    import csv
+    bad = 0
+    with open(path, newline="") as fh:
+        lines = list(csv.DictReader(fh))
+    for ln in lines:
+        why = []
+        M, N, K = int(ln["M"]), int(ln["N"]), int(ln["K"])
+        med = float(ln["median_us"])
+        if int(float(ln["flops"])) != 2 * M * N * K:
+            why.append("flops")
+        tf = 2.0 * M * N * K / (med * 1e-6) / 1e12
+        if abs(tf - float(ln["tflops"])) > 0.01 + 1e-3 * tf:
+            why.append(f"tflops {ln['tflops']} vs {tf:.2f}")
+        peak = _RV_PEAK.get(ln["dtype"])
+        if peak is None or abs(float(ln["peak_tflops"]) - peak) > 1e-6:
+            why.append("peak")
+        elif abs(100 * tf / peak - float(ln["pct_peak"])) > 0.02:
+            why.append(f"pct_peak {ln['pct_peak']} vs {100 * tf / peak:.2f}")
+        if not float(ln["ci95_lo_us"]) <= med <= float(ln["ci95_hi_us"]):
+            why.append("median outside its interval")
+        if ln["gate_pass"] == "":
+            why.append("not gated")
+        else:
+            u = _RV_U.get(ln["c_type"])
+            rnd = int(ln["gate_roundings"])
+            gelu = ln["gate_gelu"] == "True"
+            tol = (K * 2.0 ** -23 + (1.0 + (rnd - 1) * 1.1289) * u + 4 * 2.0 ** -24
+                   + (16 * 2.0 ** -24 if gelu else 0.0)) if u is not None else None
+            if tol is None or abs(tol - float(ln["gate_tol"])) > 1e-12 * max(1.0, tol):
+                why.append("tolerance")
+            verdict = float(ln["gate_max_err"]) <= float(ln["gate_tol"])
+            if verdict != (ln["gate_pass"] == "True"):
+                why.append("verdict")
+            if not verdict:
+                why.append("fails the gate")
+        # a tree copied without its history has no commit; the source hash names it instead
+        for f in ("sources", "gpu", "cus", "recipe_hash", "seed"):
+            if ln[f] in ("", "None"):
+                why.append(f"no {f}")
+        if why:
+            bad += 1
+            print(f"[reverify] {ln['cell']}: " + "; ".join(why))
+    print(f"[reverify] {len(lines) - bad} of {len(lines)} lines agree")
+    return bad
+
+
+def replot(path: str) -> str:
+    """The table of cells regenerated from the CSV alone (no GPU): markdown, one row per cell."""
+    import csv
+    with open(path, newline="") as fh:
+        lines = list(csv.DictReader(fh))
+    out = ["| Cell | Kernel | Median (95% CI) | TFLOP/s | % of peak | Gate |", "|---|---|---|---|---|---|"]
+    for ln in lines:
+        gate = ("—" if ln["gate_pass"] == "" else
+                f"{'pass' if ln['gate_pass'] == 'True' else 'FAIL'} ({float(ln['gate_max_err']) / float(ln['gate_tol']):.1%} of tol, n={ln['gate_n']})")
+        out.append(f"| {ln['cell']} | {ln['kernel']} | {float(ln['median_us']):.2f} µs "
+                   f"({float(ln['ci95_lo_us']):.2f}–{float(ln['ci95_hi_us']):.2f}) | "
+                   f"{float(ln['tflops']):.1f} | {float(ln['pct_peak']):.1f} | {gate} |")
+    return "\n".join(out)
+
+
 def cpu_baseline(p, target_s: float) -> dict:
     """The oracle, as it stands, on a bounded sample of the headline problem: the first rows
     of the M x N result (all N columns, full K), timed with a monotonic clock."""
@@ -485,9 +638,10 @@ def cpu_baseline(p, target_s: float) -> dict:
     t_probe = time.perf_counter() - t0
     rows = int(max(8, min(p.M, 8 * target_s / max(t_probe, 1e-3))))
     t0 = time.perf_counter()
-    oracle.gemm_rows(p, 0, rows)
+    ref = oracle.gemm_rows(p, 0, rows)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * p.N * p.K
+    cpu_baseline.computed = (rows, ref)  # the rows it computed, for the headline's gate
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"rows 0..{rows - 1} of the {p.M}x{p.N}x{p.K} bf16+bias+GELU problem "
@@ -548,7 +702,22 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --headline-only-loop: also run a plain device copy of this many "
                          "bytes three times (a known-size reference for HBM byte counters)")
+    ap.add_argument("--csv", default="",
+                    help="also write one line per cell (measurements, rates, gate, provenance) "
+                         "to this CSV file")
+    ap.add_argument("--reverify", default="",
+                    help="re-derive every rate and gate verdict of a results CSV and exit "
+                         "(no GPU); nonzero exit status when a line disagrees")
+    ap.add_argument("--replot", default="",
+                    help="print the table of cells regenerated from a results CSV and exit "
+                         "(no GPU)")
     args = ap.parse_args()
+
+    if args.reverify:
+        sys.exit(1 if reverify(args.reverify) else 0)
+    if args.replot:
+        print(replot(args.replot))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -639,10 +808,14 @@ def main():
 
     hbm = None if args.no_sweeps else hbm_ceiling(g)
     sweeps = []
+    gate_in = []  # (sweep index, problem, quantized, unfused, sampled outputs)
     if not args.no_sweeps:
         for name, dtype, make in sweep_cells():
             c = make(g)
             row = summarize(name, c, c.time(args.reps, clock=clock), dtype)
+            if not args.no_cpu:
+                gate_in.append((len(sweeps), c.p, isinstance(c, QCell), getattr(c, "unfused", False),
+                                c.result_sample(seed=len(sweeps))))
             gms = graph_time(c)
             row["graph_us"] = round(gms * 1e3, 3) if gms is not None else None
             if gms is not None:
@@ -662,10 +835,27 @@ def main():
             torch.cuda.empty_cache()
 
     cpu = None
+    head_gate = None
     if not args.no_cpu:
         print("[bench] timing the oracle on the host (bounded sample) ...", file=sys.stderr,
               flush=True)
         cpu = cpu_baseline(head_p, args.cpu_seconds)
+        # The checksum gate on what the oracle computed here: the headline's sampled rows (all
+        # columns), and each sweep cell's sampled outputs.
+        import oracle
+        from oracle import gate
+        rows, (Cref, D) = cpu_baseline.computed
+        got = head.C[:rows].cpu().numpy().view(np.uint16)
+        tol = gate.tolerance(head_p.K, "bf16", 1, True)
+        res = gate.check(oracle.decode("bf16", got), Cref, D, tol, "bf16")
+        head_gate = {"n": res.n_checked, "max_err": res.max_err, "tol": res.tol, "pass": res.ok,
+                     "c_type": "bf16", "roundings": 1, "gelu": True}
+        head_row["gate"] = head_gate
+        for i, pp, quantized, unfused, sample in gate_in:
+            sweeps[i]["gate"] = gate_sample(pp, sample, quantized, unfused)
+        n_pass = sum(1 for r in sweeps if r.get("gate", {}).get("pass")) + int(head_gate["pass"])
+        print(f"[bench] checksum gate: {n_pass} of {len(sweeps) + 1} cells pass "
+              f"(headline: {res})", file=sys.stderr, flush=True)
 
     counters = read_counters(src_hash)
     kclk = counters["sclk_in_kernel_mhz"]
@@ -709,9 +899,12 @@ def main():
         "hbm_read_gbs": hbm["read_gbs"] if hbm else None,
         "hbm_ceiling": hbm,
         "cpu_baseline": cpu,
+        "gate": head_gate,
         "sweeps": sweeps,
         "provenance": provenance(src_hash),
     }
+    if args.csv:
+        write_csv(args.csv, [head_row] + sweeps, out["provenance"], src_hash)
     print(json.dumps(out), flush=True)
     g.close()
 

@@ -1,5 +1,6 @@
 """Host-side pieces of bench.py that need no GPU: the counter-summary reader, the bootstrap
-confidence interval, the source hash and the single-GPU refusal."""
+confidence interval, the source hash, the single-GPU refusal, the gate's sample points, and the
+re-verifier and replot of a results CSV."""
 import os
 import subprocess
 import sys
@@ -65,3 +66,74 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, env=env, timeout=120)
     assert r.returncode == 2
     assert "single-GPU" in r.stderr and r.stdout == ""
+
+
+def _results_csv(path, **override):
+    """A two-line results CSV whose derived columns follow from its raw ones."""
+    import csv
+    M = N = K = 4096
+    med = 113.2
+    tf = 2.0 * M * N * K / (med * 1e-6) / 1e12
+    tol = K * 2.0 ** -23 + 2.0 ** -8 + 4 * 2.0 ** -24 + 16 * 2.0 ** -24
+    base = {"cell": "bf16+bias+GELU fused 4096 (headline)", "kernel": "mfma256", "dtype": "bf16",
+            "c_type": "bf16", "M": M, "N": N, "K": K, "flops": 2 * M * N * K, "seed": 3,
+            "recipe_hash": "abc", "reps": 300, "median_us": med, "ci95_lo_us": 113.0,
+            "ci95_hi_us": 113.5, "tflops": round(tf, 2), "peak_tflops": 2516.6,
+            "pct_peak": round(100 * tf / 2516.6, 2), "graph_us": 113.1, "gate_n": 4096,
+            "gate_max_err": tol / 10, "gate_tol": tol, "gate_roundings": 1, "gate_gelu": True,
+            "gate_pass": True, "commit": "deadbee", "sources": "0123", "gpu": "MI355X",
+            "cus": 256}
+    M2, K2 = 1000, 1000
+    med2 = 27.0
+    tf2 = 2.0 * M2 * M2 * K2 / (med2 * 1e-6) / 1e12
+    second = dict(base, cell="fp32 1000", kernel="mfma64", dtype="f32", c_type="f32", M=M2, N=M2,
+                  K=K2, flops=2 * M2 * M2 * K2, median_us=med2, ci95_lo_us=26.9, ci95_hi_us=27.1,
+                  tflops=round(tf2, 2), peak_tflops=157.3, pct_peak=round(100 * tf2 / 157.3, 2),
+                  gate_tol=K2 * 2.0 ** -23 + 2.0 ** -24 + 4 * 2.0 ** -24, gate_gelu=False,
+                  gate_max_err=1e-7)
+    second.update(override)
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=bench.CSV_FIELDS)
+        w.writeheader()
+        w.writerow(base)
+        w.writerow(second)
+
+
+def test_reverify_agrees_with_a_consistent_csv(tmp_path):
+    path = tmp_path / "cells.csv"
+    _results_csv(path)
+    assert bench.reverify(str(path)) == 0
+    table = bench.replot(str(path))
+    assert "fp32 1000" in table and "mfma256" in table and "pass" in table
+
+
+@pytest.mark.parametrize("override", [
+    {"tflops": 80.0},                        # a rate that does not follow from the median
+    {"pct_peak": 50.0},                      # a fraction of the wrong peak
+    {"flops": 2 * 1000 ** 3 + 2},            # flops that are not 2 M N K
+    {"gate_pass": False},                    # a verdict the numbers contradict
+    {"gate_max_err": 1.0, "gate_pass": False},  # an honest failure still counts as a bad line
+    {"gate_tol": 1e-3},                      # a tolerance not recomputable from K and the type
+    {"ci95_lo_us": 27.5},                    # a median outside its interval
+    {"sources": ""},                         # missing provenance
+])
+def test_reverify_catches_each_inconsistency(tmp_path, override):
+    path = tmp_path / "cells.csv"
+    _results_csv(path, **override)
+    assert bench.reverify(str(path)) == 1
+
+
+def test_gate_points_include_the_corners():
+    rows, cols = bench.gate_points(300, 500, 64, 0)
+    assert len(rows) == len(cols) == 64
+    assert {(0, 0), (0, 499), (299, 0), (299, 499)} <= set(zip(rows.tolist(), cols.tolist()))
+    assert rows.max() < 300 and cols.max() < 500
+
+
+def test_the_committed_results_csv_reverifies(capsys):
+    """The results CSV kept beside the profiles re-derives line by line, every cell passes its
+    gate, and every sweep cell is present."""
+    path = os.path.join(ROOT, "profiles", "bench_cells.csv")
+    assert bench.reverify(path) == 0
+    out = capsys.readouterr().out
+    assert out.strip().splitlines()[-1] == "[reverify] 24 of 24 lines agree"

@@ -549,8 +549,9 @@ def write_csv(path: str, rows: list, prov: dict, src_hash: str) -> None:
                         "gate_n": gt.get("n", ""), "gate_max_err": gt.get("max_err", ""),
                         "gate_tol": gt.get("tol", ""), "gate_roundings": gt.get("roundings", ""),
                         "gate_gelu": gt.get("gelu", ""), "gate_pass": gt.get("pass", ""),
-                        "commit": prov.get("commit", ""), "sources": src_hash,
-                        "gpu": prov.get("gpu", ""), "cus": prov.get("cus", "")})
+                        "commit": prov.get("git_commit") or "", "sources": src_hash,
+                        "gpu": f'{prov.get("gpu", "")} {prov.get("gcn_arch", "")}'.strip(),
+                        "cus": prov.get("cus", "")})
 
 
 # The re-verifier restates what it checks from the published figures, not from the code that

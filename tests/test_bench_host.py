@@ -137,3 +137,29 @@ def test_the_committed_results_csv_reverifies(capsys):
     assert bench.reverify(path) == 0
     out = capsys.readouterr().out
     assert out.strip().splitlines()[-1] == "[reverify] 24 of 24 lines agree"
+
+
+def test_write_csv_carries_the_provenance(tmp_path):
+    """The commit, the architecture and the CU count reach their columns; the derived columns
+    of the line written re-verify."""
+    import csv
+    M = N = K = 1024
+    med = 10.0
+    row = {"cell": "fp16 1024", "kernel": "mfma64", "dtype": "f16", "M": M, "N": N, "K": K,
+           "flops": 2 * M * N * K, "seed": 2, "recipe_hash": "abc", "reps": 300,
+           "median_us": med, "ci95_us": (9.9, 10.1),
+           "tflops": round(2.0 * M * N * K / (med * 1e-6) / 1e12, 2),
+           "pct_peak": round(100 * 2.0 * M * N * K / (med * 1e-6) / 1e12 / 2516.6, 2),
+           "graph_us": 9.0,
+           "gate": {"n": 512, "max_err": 1e-5, "tol": K * 2.0 ** -23 + 2.0 ** -11 + 4 * 2.0 ** -24,
+                    "pass": True, "c_type": "f16", "roundings": 1, "gelu": False}}
+    prov = {"git_commit": "abc1234", "gpu": "AMD Radeon Graphics", "gcn_arch": "gfx950:sramecc+",
+            "cus": 256}
+    path = tmp_path / "cells.csv"
+    bench.write_csv(str(path), [row], prov, "0123456789abcdef")
+    with open(path) as fh:
+        line = next(csv.DictReader(fh))
+    assert line["commit"] == "abc1234"
+    assert line["gpu"] == "AMD Radeon Graphics gfx950:sramecc+"
+    assert line["cus"] == "256" and line["sources"] == "0123456789abcdef"
+    assert bench.reverify(str(path)) == 0

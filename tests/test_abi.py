@@ -21,11 +21,14 @@ def declared_symbols():
     return sorted(set(re.findall(r"GEMM_API\s+[\w\s\*]*?\b(gemm_\w+)\s*\(", text)))
 
 
-def test_every_declared_symbol_is_exported():
+@pytest.mark.parametrize("lib", ["libgemm.so", "libgemm_lds_poison.so"])
+def test_every_declared_symbol_is_exported(lib):
+    """The library and its LDS race-check build both export exactly the C ABI."""
     syms = declared_symbols()
     assert len(syms) == 23, syms
     assert sorted(tmm.EXPORTS) == syms
-    nm = subprocess.run(["nm", "-D", "--defined-only", tmm.LIB_PATH], capture_output=True,
+    path = os.path.join(os.path.dirname(tmm.LIB_PATH), lib)
+    nm = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
                         text=True, check=True).stdout
     exported = {line.split()[-1] for line in nm.splitlines() if " T " in line}
     for s in syms:

@@ -2,6 +2,11 @@
 
 Every source is compiled in parallel into _build/, then linked into one shared library whose
 exported symbols are exactly the C ABI of include/gemm.h.
+
+Beside it, libgemm_lds_poison.so: the same library with the matrix-core kernels of the main
+families (fp32, fp16, bf16, per-tensor and block-scaled E4M3, quantized B) built with
+GEMM_DEBUG_POISON_LDS, which fills every LDS stage with all-ones words before it is refilled.
+It is a race check for the staged K loop: its results must equal libgemm.so's bit for bit.
 """
 import concurrent.futures as cf
 import os
@@ -15,6 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm.so")
+LIB_POISON = os.path.join(PKG, "libgemm_lds_poison.so")
+POISON_SOURCES = ("mfma_f32.hip", "mfma_f16.hip", "mfma_bf16.hip", "mfma_e4m3.hip",
+                  "mfma_mx_e4m3.hip", "qmfma.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -31,10 +39,11 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, verbose: bool, poison: bool = False) -> str:
+    stem = os.path.splitext(src)[0] + ("_lds_poison" if poison else "")
+    obj = os.path.join(BUILD, stem + ".o")
     path = os.path.join(CSRC, src)
-    cmd = [HIPCC, *COMMON]
+    cmd = [HIPCC, *COMMON] + (["-DGEMM_DEBUG_POISON_LDS"] if poison else [])
     if src.endswith(".hip"):
         cmd += ["-x", "hip", *DEVICE]
     cmd += ["-c", path, "-o", obj]
@@ -49,21 +58,30 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 0) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    t0 = time.time()
-    srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, os.cpu_count() or 1), 16)
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs: list, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, capture_output=not verbose)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    t0 = time.time()
+    srcs = sources()
+    poison = [s for s in srcs if s in POISON_SOURCES]
+    assert len(poison) == len(POISON_SOURCES), "a race-check source is missing from csrc/"
+    # the largest translation units first, so the pool does not end on one of them
+    work = [(s, True) for s in poison] + [(s, False) for s in srcs]
+    jobs = jobs or min(len(work), max(1, os.cpu_count() or 1), 16)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        built = dict(zip(work, ex.map(lambda w: _compile(w[0], verbose, w[1]), work)))
+    _link([built[(s, False)] for s in srcs], LIB, verbose)
+    _link([built[(s, s in POISON_SOURCES)] for s in srcs], LIB_POISON, verbose)
     if verbose:
-        print(f"built {LIB} in {time.time() - t0:.1f}s", flush=True)
+        print(f"built {LIB} and {LIB_POISON} in {time.time() - t0:.1f}s", flush=True)
     return LIB
 
 

@@ -909,11 +909,32 @@ __device__ __forceinline__ void mfma_tile(const GemmParams p, const SkSeg sg) {
   // on the SIMD with multiplies to issue and could not hide its own fragment reads.  The B
   // copies still land a good half tile before the boundary that waits for them.
   constexpr bool DEFER_B = C::NCW < C::NW && GROUPED && !C::MX && C::QB == 0 && C::S == 2;
+#ifdef GEMM_DEBUG_POISON_LDS
+  // Race check (a debug build of the library): a stage about to be refilled is first
+  // overwritten with all-ones words, a NaN in every floating-point type staged here (a wrong
+  // value in the 4- and 6-bit ones), between two barriers.  A fragment read of a stage before
+  // its copies have landed, or of a tile's stage after its refill began, then reads the poison
+  // instead of stale data that may happen to be right, and the result differs from the
+  // library's own.  Only the data stages are poisoned (not the MX scale rows).
+  auto poison_stage = [&](int buf) {
+    const int gt = tid % (C::NW * 64);
+    uint8_t* const a = gsm + OA::LDS_OFF + buf * C::A_BYTES;
+    uint8_t* const b = gsm + OB::LDS_OFF + buf * C::B_BYTES;
+    for (int o = gt * 16; o < C::A_BYTES; o += C::NW * 64 * 16)
+      *reinterpret_cast<u32x4*>(a + o) = u32x4{~0u, ~0u, ~0u, ~0u};
+    for (int o = gt * 16; o < C::B_BYTES; o += C::NW * 64 * 16)
+      *reinterpret_cast<u32x4*>(b + o) = u32x4{~0u, ~0u, ~0u, ~0u};
+  };
+#endif
   auto tile_boundary = [&](int kt, int abuf, int anext) {
     // tiles kt+2 .. min(kt+S-1, KT-1) may stay in flight
     wait_vm<0, MAXC>(copies(kt + 2, min(kt + C::S - 1, KT - 1)));
     if (kt + 2 == KT && need_fix && tile_of(kt + 1) == KT_ALL - 1) fixup(tile_of(kt + 1), anext, anext);
     __syncthreads();
+#ifdef GEMM_DEBUG_POISON_LDS
+    if (kt + C::S < KT) poison_stage(abuf);
+    __syncthreads();  // outside the condition: the groups of a split K loop count tiles apart
+#endif
     if (kt + C::S < KT) {  // into the buffers tile kt has released
       if constexpr (DEFER_B) issue_a(tile_of(kt + C::S), abuf);
       else issue(kt + C::S, abuf);
@@ -992,6 +1013,11 @@ __device__ __forceinline__ void mfma_tile(const GemmParams p, const SkSeg sg) {
     asm volatile("" : "+v"(q.s), "+v"(q.o));
   };
   // Prologue: copies of tiles 0 .. S-1, then wait for tile 0.
+#ifdef GEMM_DEBUG_POISON_LDS
+#pragma unroll
+  for (int t = 0; t < C::S; ++t) poison_stage(t);
+  __syncthreads();
+#endif
   if constexpr (C::QB != 0) {
     const QCodes q0 = qload(0);
     qcur = qload(1);

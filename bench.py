@@ -460,6 +460,7 @@ def summarize(name, cell: Cell, ms: np.ndarray, dtype: str) -> dict:
            "tflops_ci95": [round(p.flops / (hi * 1e-3) / 1e12, 2),
                            round(p.flops / (lo * 1e-3) / 1e12, 2)],
            "pct_peak": round(100 * tf / PEAK_TFLOPS[dtype], 2),
+           "alg_bytes": int(cell.algorithmic_bytes()),
            "gbs": round(cell.algorithmic_bytes() / (med * 1e-3) / 1e9, 1),
            "back_to_back_us": round(getattr(cell, "b2b_ms", float("nan")) * 1e3, 3),
            "sclk_after_run_mhz": getattr(cell, "sclk", None)}
@@ -526,8 +527,9 @@ def gate_sample(p, sample: dict, quantized: bool, unfused: bool):
 
 CSV_FIELDS = ("cell", "kernel", "dtype", "c_type", "M", "N", "K", "flops", "seed", "recipe_hash",
               "reps", "median_us", "ci95_lo_us", "ci95_hi_us", "tflops", "peak_tflops",
-              "pct_peak", "graph_us", "gate_n", "gate_max_err", "gate_tol", "gate_roundings",
-              "gate_gelu", "gate_pass", "commit", "sources", "gpu", "cus")
+              "pct_peak", "alg_bytes", "gbs", "graph_us", "sclk_after_run_mhz", "gate_n",
+              "gate_max_err", "gate_tol", "gate_roundings", "gate_gelu", "gate_pass", "commit",
+              "sources", "gpu", "cus", "hip", "torch")
 
 
 def write_csv(path: str, rows: list, prov: dict, src_hash: str) -> None:
@@ -545,13 +547,16 @@ def write_csv(path: str, rows: list, prov: dict, src_hash: str) -> None:
                         "reps": r["reps"], "median_us": r["median_us"],
                         "ci95_lo_us": r["ci95_us"][0], "ci95_hi_us": r["ci95_us"][1],
                         "tflops": r["tflops"], "peak_tflops": PEAK_TFLOPS[r["dtype"]],
-                        "pct_peak": r["pct_peak"], "graph_us": r.get("graph_us"),
+                        "pct_peak": r["pct_peak"], "alg_bytes": r.get("alg_bytes", ""),
+                        "gbs": r.get("gbs", ""), "graph_us": r.get("graph_us"),
+                        "sclk_after_run_mhz": (r.get("sclk_after_run_mhz") or {}).get("mean", ""),
                         "gate_n": gt.get("n", ""), "gate_max_err": gt.get("max_err", ""),
                         "gate_tol": gt.get("tol", ""), "gate_roundings": gt.get("roundings", ""),
                         "gate_gelu": gt.get("gelu", ""), "gate_pass": gt.get("pass", ""),
                         "commit": prov.get("git_commit") or "", "sources": src_hash,
                         "gpu": f'{prov.get("gpu", "")} {prov.get("gcn_arch", "")}'.strip(),
-                        "cus": prov.get("cus", "")})
+                        "cus": prov.get("cus", ""), "hip": prov.get("hip", ""),
+                        "torch": prov.get("torch", "")})
 
 
 # The re-verifier restates what it checks from the published figures, not from the code that
@@ -566,8 +571,9 @@ _RV_U = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 def reverify(path: str) -> int:
     """Re-derive every line's rates and gate verdict from its raw columns and report the lines
     that disagree (no GPU, no oracle): flops = 2 M N K; TFLOP/s from the median; the % of the
-    type's peak; the median inside its 95% interval; pass exactly when max_err <= tol, with the
-    tolerance recomputed; provenance present.  Returns the number of disagreeing lines."""
+    type's peak; GB/s from the algorithmic bytes and the median; the median inside its 95%
+    interval; pass exactly when max_err <= tol, with the tolerance recomputed; provenance
+    present.  Returns the number of disagreeing lines."""
     import csv
     bad = 0
     with open(path, newline="") as fh:
@@ -588,6 +594,10 @@ def reverify(path: str) -> int:
             why.append(f"pct_peak {ln['pct_peak']} vs {100 * tf / peak:.2f}")
         if not float(ln["ci95_lo_us"]) <= med <= float(ln["ci95_hi_us"]):
             why.append("median outside its interval")
+        if ln.get("alg_bytes") not in (None, ""):
+            gbs = int(float(ln["alg_bytes"])) / (med * 1e-6) / 1e9
+            if abs(gbs - float(ln["gbs"])) > 0.1 + 1e-3 * gbs:
+                why.append(f"gbs {ln['gbs']} vs {gbs:.1f}")
         if ln["gate_pass"] == "":
             why.append("not gated")
         else:
@@ -619,13 +629,15 @@ def replot(path: str) -> str:
     import csv
     with open(path, newline="") as fh:
         lines = list(csv.DictReader(fh))
-    out = ["| Cell | Kernel | Median (95% CI) | TFLOP/s | % of peak | Gate |", "|---|---|---|---|---|---|"]
+    out = ["| Cell | Kernel | Median (95% CI) | TFLOP/s | % of peak | GB/s | Gate |",
+           "|---|---|---|---|---|---|---|"]
     for ln in lines:
         gate = ("—" if ln["gate_pass"] == "" else
                 f"{'pass' if ln['gate_pass'] == 'True' else 'FAIL'} ({float(ln['gate_max_err']) / float(ln['gate_tol']):.1%} of tol, n={ln['gate_n']})")
         out.append(f"| {ln['cell']} | {ln['kernel']} | {float(ln['median_us']):.2f} µs "
                    f"({float(ln['ci95_lo_us']):.2f}–{float(ln['ci95_hi_us']):.2f}) | "
-                   f"{float(ln['tflops']):.1f} | {float(ln['pct_peak']):.1f} | {gate} |")
+                   f"{float(ln['tflops']):.1f} | {float(ln['pct_peak']):.1f} | "
+                   f"{ln.get('gbs') or '—'} | {gate} |")
     return "\n".join(out)
 
 

@@ -79,7 +79,9 @@ def _results_csv(path, **override):
             "c_type": "bf16", "M": M, "N": N, "K": K, "flops": 2 * M * N * K, "seed": 3,
             "recipe_hash": "abc", "reps": 300, "median_us": med, "ci95_lo_us": 113.0,
             "ci95_hi_us": 113.5, "tflops": round(tf, 2), "peak_tflops": 2516.6,
-            "pct_peak": round(100 * tf / 2516.6, 2), "graph_us": 113.1, "gate_n": 4096,
+            "pct_peak": round(100 * tf / 2516.6, 2), "alg_bytes": 100663296 + 16384,
+            "gbs": round((100663296 + 16384) / (med * 1e-6) / 1e9, 1), "graph_us": 113.1,
+            "sclk_after_run_mhz": 2410.0, "gate_n": 4096,
             "gate_max_err": tol / 10, "gate_tol": tol, "gate_roundings": 1, "gate_gelu": True,
             "gate_pass": True, "commit": "deadbee", "sources": "0123", "gpu": "MI355X",
             "cus": 256}
@@ -89,6 +91,7 @@ def _results_csv(path, **override):
     second = dict(base, cell="fp32 1000", kernel="mfma64", dtype="f32", c_type="f32", M=M2, N=M2,
                   K=K2, flops=2 * M2 * M2 * K2, median_us=med2, ci95_lo_us=26.9, ci95_hi_us=27.1,
                   tflops=round(tf2, 2), peak_tflops=157.3, pct_peak=round(100 * tf2 / 157.3, 2),
+                  alg_bytes=16000000, gbs=round(16000000 / (med2 * 1e-6) / 1e9, 1),
                   gate_tol=K2 * 2.0 ** -23 + 2.0 ** -24 + 4 * 2.0 ** -24, gate_gelu=False,
                   gate_max_err=1e-7)
     second.update(override)
@@ -115,6 +118,7 @@ def test_reverify_agrees_with_a_consistent_csv(tmp_path):
     {"gate_max_err": 1.0, "gate_pass": False},  # an honest failure still counts as a bad line
     {"gate_tol": 1e-3},                      # a tolerance not recomputable from K and the type
     {"ci95_lo_us": 27.5},                    # a median outside its interval
+    {"gbs": 1000.0},                         # a bandwidth that does not follow from the median
     {"sources": ""},                         # missing provenance
 ])
 def test_reverify_catches_each_inconsistency(tmp_path, override):

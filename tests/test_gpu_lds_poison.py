@@ -8,8 +8,8 @@ hold no NaN.
 
 Covered: the 32, 64, 128, 256 and 256 x 128 tiles (with their in-workgroup K splits and the
 256 tile's copying waves), the split across two workgroups, stream-K, per-tensor and
-block-scaled E4M3 and quantized B (the prefill kernel, whose B stages are written by the
-waves), in several layouts, with ragged M, N and K, beta and bias + GELU.
+block-scaled E4M3, E2M1 and E2M3 and quantized B (the prefill kernel, whose B stages are
+written by the waves), in several layouts, with ragged M, N and K, beta and bias + GELU.
 """
 import contextlib
 import ctypes
@@ -138,6 +138,22 @@ def test_fp8_tiles(libs, kernel, mx):
     p = W.make_problem(520, 700, 1056, a_type="e4m3", c_type="bf16", seed=30 + kernel, mx=mx,
                        dist_a=("normal", 1.0), dist_b=("normal", 1.0), epilogue=W.EPI_BIAS)
     _check(f"e4m3 kernel {kernel} mx={mx}", *_both(libs, p, kernel))
+
+
+@pytest.mark.parametrize("kernel", [2, 3, 4])
+@pytest.mark.parametrize("a_type", ["e2m1", "e2m3"])
+@pytest.mark.parametrize("mx", [False, True])
+def test_four_and_six_bit_tiles(libs, kernel, a_type, mx):
+    """Packed 4- and 6-bit operands (both stored K-contiguous, as the matrix-core kernels take
+    them).  The 6-bit tiles fill 96 bytes of each 128-byte LDS row; on the 256 tile only those
+    are copied, so the other 32 keep the poison, which no fragment read may touch."""
+    # 4 bits: K = 1056, whole blocks of 32 and a partial last K tile of 256 elements; 6 bits:
+    # K = 1152, the matrix-core kernels take only whole 128-element K tiles
+    K = 1056 if a_type == "e2m1" else 1152
+    p = W.make_problem(520, 700, K, a_type=a_type, c_type="bf16", trans_b=True, mx=mx,
+                       seed=40 + kernel + 10 * mx, dist_a=("normal", 1.0), dist_b=("normal", 1.0),
+                       epilogue=W.EPI_BIAS)
+    _check(f"{a_type} kernel {kernel} mx={mx}", *_both(libs, p, kernel))
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 700, 1024), (1000, 1300, 2048)])

@@ -4,7 +4,8 @@ Every source is compiled in parallel into _build/, then linked into one shared l
 exported symbols are exactly the C ABI of include/gemm.h.
 
 Beside it, libgemm_lds_poison.so: the same library with the matrix-core kernels of the main
-families (fp32, fp16, bf16, per-tensor and block-scaled E4M3, quantized B) built with
+families (fp32, fp16, bf16, per-tensor and block-scaled E4M3, E2M1 and E2M3, quantized B)
+built with
 GEMM_DEBUG_POISON_LDS, which fills every LDS stage with all-ones words before it is refilled.
 It is a race check for the staged K loop: its results must equal libgemm.so's bit for bit.
 """
@@ -22,7 +23,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm.so")
 LIB_POISON = os.path.join(PKG, "libgemm_lds_poison.so")
 POISON_SOURCES = ("mfma_f32.hip", "mfma_f16.hip", "mfma_bf16.hip", "mfma_e4m3.hip",
-                  "mfma_mx_e4m3.hip", "qmfma.hip")
+                  "mfma_mx_e4m3.hip", "mfma_e2m1.hip", "mfma_e2m3.hip", "qmfma.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

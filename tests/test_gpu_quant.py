@@ -197,3 +197,38 @@ def test_q_prefill_full_size(g):
     r = qgate(q, qrun(g, q))
     print(r)
     assert r.ok, r
+
+
+@pytest.mark.parametrize("epilogue", [False, True])
+def test_q_prefill_equals_the_bf16_gemm_of_its_weights(g, epilogue):
+    """The prefill kernel dequantises each weight as it stages B (w = s q + o in one fp32 fused
+    multiply-add, rounded once to bf16) and multiplies on the 256 x 256 tile like the plain bf16
+    kernel.  Given those weights, dequantised on the host and stored N x K, the plain kernel on
+    the same tile must return the same bits.  On the host the exact s q + o (float64) is rounded
+    to fp32, as the fused multiply-add rounds it, and then to bf16.  4096^3, where the prefill
+    kernel takes the 256 tile."""
+    import torch
+    import tiled_matrix_multiply_amd as tmm
+    if epilogue:
+        q = W.make_qproblem(4096, 4096, 4096, bits=4, group=64, alpha=0.75, beta=0.5, seed=17,
+                            epilogue=W.EPI_BIAS | W.EPI_GELU)
+    else:
+        q = W.q4_prefill()
+    codes = np.empty((q.N, q.K), dtype=np.float64)
+    codes[:, 0::2] = q.Wq & 15
+    codes[:, 1::2] = q.Wq >> 4
+    s = np.repeat(oracle.decode("bf16", q.scales), q.group, axis=1)
+    o = np.repeat(oracle.decode("bf16", q.offsets), q.group, axis=1)
+    w = (s * codes + o).astype(np.float32)
+    wb = W.encode(w.astype(np.float64), "bf16")
+    fused = qrun(g, q, kernel=tmm.GEMM_KERNEL_QMFMA)
+    X, Wd, C = to_device(q.X), to_device(wb), to_device(q.C)
+    bias = to_device(q.bias) if q.bias is not None else None
+    tmm.run(g.handle, X, Wd, C, M=q.M, N=q.N, K=q.K, trans_b=True, alpha=q.alpha, beta=q.beta,
+            a_type="bf16", epilogue=q.epilogue, bias=bias, kernel=tmm.GEMM_KERNEL_MFMA_256)
+    torch.cuda.synchronize()
+    plain = oracle.decode("bf16", from_device(C, "bf16"))
+    same = fused.view(np.uint64) == plain.view(np.uint64)
+    print(f"[quant] prefill vs bf16 GEMM of its weights (epilogue={epilogue}): "
+          f"{same.mean():.6f} of {same.size} outputs bit-identical", flush=True)
+    assert same.all(), f"{(~same).sum()} outputs differ, first at {np.argwhere(~same)[0]}"

@@ -456,6 +456,9 @@ def summarize(name, cell: Cell, ms: np.ndarray, dtype: str) -> dict:
            "seed": p.recipe.get("seed"), "recipe_hash": recipe_hash(p.recipe),
            "flops": int(p.flops), "reps": int(len(ms)), "median_us": round(med * 1e3, 3),
            "ci95_us": [round(hi_ * 1e3, 3) for hi_ in (lo, hi)],
+           # the spread of single reps: a second clock state would show as a wide p5..p95
+           "p05_us": round(float(np.percentile(ms, 5)) * 1e3, 3),
+           "p95_us": round(float(np.percentile(ms, 95)) * 1e3, 3),
            "tflops": round(tf, 2),
            "tflops_ci95": [round(p.flops / (hi * 1e-3) / 1e12, 2),
                            round(p.flops / (lo * 1e-3) / 1e12, 2)],
@@ -526,7 +529,8 @@ def gate_sample(p, sample: dict, quantized: bool, unfused: bool):
 
 
 CSV_FIELDS = ("cell", "kernel", "dtype", "c_type", "M", "N", "K", "flops", "seed", "recipe_hash",
-              "reps", "median_us", "ci95_lo_us", "ci95_hi_us", "tflops", "peak_tflops",
+              "reps", "median_us", "ci95_lo_us", "ci95_hi_us", "p05_us", "p95_us", "tflops",
+              "peak_tflops",
               "pct_peak", "alg_bytes", "gbs", "graph_us", "sclk_after_run_mhz", "gate_n",
               "gate_max_err", "gate_tol", "gate_roundings", "gate_gelu", "gate_pass", "commit",
               "sources", "gpu", "cus", "hip", "torch")
@@ -546,6 +550,7 @@ def write_csv(path: str, rows: list, prov: dict, src_hash: str) -> None:
                         "flops": r["flops"], "seed": r["seed"], "recipe_hash": r["recipe_hash"],
                         "reps": r["reps"], "median_us": r["median_us"],
                         "ci95_lo_us": r["ci95_us"][0], "ci95_hi_us": r["ci95_us"][1],
+                        "p05_us": r.get("p05_us", ""), "p95_us": r.get("p95_us", ""),
                         "tflops": r["tflops"], "peak_tflops": PEAK_TFLOPS[r["dtype"]],
                         "pct_peak": r["pct_peak"], "alg_bytes": r.get("alg_bytes", ""),
                         "gbs": r.get("gbs", ""), "graph_us": r.get("graph_us"),
@@ -572,8 +577,9 @@ def reverify(path: str) -> int:
     """Re-derive every line's rates and gate verdict from its raw columns and report the lines
     that disagree (no GPU, no oracle): flops = 2 M N K; TFLOP/s from the median; the % of the
     type's peak; GB/s from the algorithmic bytes and the median; the median inside its 95%
-    interval; pass exactly when max_err <= tol, with the tolerance recomputed; provenance
-    present.  Returns the number of disagreeing lines."""
+    interval and between the 5th and 95th percentiles of the reps; pass exactly when
+    max_err <= tol, with the tolerance recomputed; provenance present.  Returns the number of
+    disagreeing lines."""
     import csv
     bad = 0
     with open(path, newline="") as fh:
@@ -594,6 +600,9 @@ def reverify(path: str) -> int:
             why.append(f"pct_peak {ln['pct_peak']} vs {100 * tf / peak:.2f}")
         if not float(ln["ci95_lo_us"]) <= med <= float(ln["ci95_hi_us"]):
             why.append("median outside its interval")
+        if ln.get("p05_us") not in (None, "") and not (
+                float(ln["p05_us"]) <= med <= float(ln["p95_us"])):
+            why.append("median outside p5..p95")
         if ln.get("alg_bytes") not in (None, ""):
             gbs = int(float(ln["alg_bytes"])) / (med * 1e-6) / 1e9
             if abs(gbs - float(ln["gbs"])) > 0.1 + 1e-3 * gbs:
@@ -624,18 +633,25 @@ def reverify(path: str) -> int:
     return bad
 
 
+def _span(ln: dict) -> str:
+    if ln.get("p05_us") in (None, ""):
+        return "—"
+    return f"{float(ln['p05_us']):.2f}–{float(ln['p95_us']):.2f}"
+
+
 def replot(path: str) -> str:
     """The table of cells regenerated from the CSV alone (no GPU): markdown, one row per cell."""
     import csv
     with open(path, newline="") as fh:
         lines = list(csv.DictReader(fh))
-    out = ["| Cell | Kernel | Median (95% CI) | TFLOP/s | % of peak | GB/s | Gate |",
-           "|---|---|---|---|---|---|---|"]
+    out = ["| Cell | Kernel | Median (95% CI) | p5–p95 | TFLOP/s | % of peak | GB/s | Gate |",
+           "|---|---|---|---|---|---|---|---|"]
     for ln in lines:
         gate = ("—" if ln["gate_pass"] == "" else
                 f"{'pass' if ln['gate_pass'] == 'True' else 'FAIL'} ({float(ln['gate_max_err']) / float(ln['gate_tol']):.1%} of tol, n={ln['gate_n']})")
         out.append(f"| {ln['cell']} | {ln['kernel']} | {float(ln['median_us']):.2f} µs "
                    f"({float(ln['ci95_lo_us']):.2f}–{float(ln['ci95_hi_us']):.2f}) | "
+                   f"{_span(ln)} | "
                    f"{float(ln['tflops']):.1f} | {float(ln['pct_peak']):.1f} | "
                    f"{ln.get('gbs') or '—'} | {gate} |")
     return "\n".join(out)

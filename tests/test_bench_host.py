@@ -78,7 +78,7 @@ def _results_csv(path, **override):
     base = {"cell": "bf16+bias+GELU fused 4096 (headline)", "kernel": "mfma256", "dtype": "bf16",
             "c_type": "bf16", "M": M, "N": N, "K": K, "flops": 2 * M * N * K, "seed": 3,
             "recipe_hash": "abc", "reps": 300, "median_us": med, "ci95_lo_us": 113.0,
-            "ci95_hi_us": 113.5, "tflops": round(tf, 2), "peak_tflops": 2516.6,
+            "ci95_hi_us": 113.5, "p05_us": 112.1, "p95_us": 115.0, "tflops": round(tf, 2), "peak_tflops": 2516.6,
             "pct_peak": round(100 * tf / 2516.6, 2), "alg_bytes": 100663296 + 16384,
             "gbs": round((100663296 + 16384) / (med * 1e-6) / 1e9, 1), "graph_us": 113.1,
             "sclk_after_run_mhz": 2410.0, "gate_n": 4096,
@@ -90,6 +90,7 @@ def _results_csv(path, **override):
     tf2 = 2.0 * M2 * M2 * K2 / (med2 * 1e-6) / 1e12
     second = dict(base, cell="fp32 1000", kernel="mfma64", dtype="f32", c_type="f32", M=M2, N=M2,
                   K=K2, flops=2 * M2 * M2 * K2, median_us=med2, ci95_lo_us=26.9, ci95_hi_us=27.1,
+                  p05_us=26.5, p95_us=27.6,
                   tflops=round(tf2, 2), peak_tflops=157.3, pct_peak=round(100 * tf2 / 157.3, 2),
                   alg_bytes=16000000, gbs=round(16000000 / (med2 * 1e-6) / 1e9, 1),
                   gate_tol=K2 * 2.0 ** -23 + 2.0 ** -24 + 4 * 2.0 ** -24, gate_gelu=False,
@@ -119,6 +120,7 @@ def test_reverify_agrees_with_a_consistent_csv(tmp_path):
     {"gate_tol": 1e-3},                      # a tolerance not recomputable from K and the type
     {"ci95_lo_us": 27.5},                    # a median outside its interval
     {"gbs": 1000.0},                         # a bandwidth that does not follow from the median
+    {"p95_us": 26.95},                       # a median above the 95th percentile
     {"sources": ""},                         # missing provenance
 ])
 def test_reverify_catches_each_inconsistency(tmp_path, override):

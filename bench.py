@@ -719,7 +719,8 @@ def main():
                          "steps, whatever --warmup says (clocks and power settle)")
     ap.add_argument("--reps", type=int, default=300, help="timed reps per sweep cell")
     ap.add_argument("--no-sweeps", action="store_true")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the oracle CPU baseline and, with it, the checksum gate")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--headline-only-loop", type=int, default=0,
                     help="run only N headline steps (for profiler passes) and exit")

@@ -866,6 +866,7 @@ def main():
 
     cpu = None
     head_gate = None
+    gate_failures = None  # None: not gated (--no-cpu)
     if not args.no_cpu:
         print("[bench] timing the oracle on the host (bounded sample) ...", file=sys.stderr,
               flush=True)
@@ -886,6 +887,12 @@ def main():
         n_pass = sum(1 for r in sweeps if r.get("gate", {}).get("pass")) + int(head_gate["pass"])
         print(f"[bench] checksum gate: {n_pass} of {len(sweeps) + 1} cells pass "
               f"(headline: {res})", file=sys.stderr, flush=True)
+        # a cell that fails its gate is reported by name: its rate is not a result
+        gate_failures = [r["cell"] for r in [head_row] + sweeps
+                         if r.get("gate") is not None and not r["gate"]["pass"]]
+        if gate_failures:
+            print(f"[bench] FAIL: these cells do not match the oracle: {gate_failures}",
+                  file=sys.stderr, flush=True)
 
     counters = read_counters(src_hash)
     kclk = counters["sclk_in_kernel_mhz"]
@@ -930,6 +937,7 @@ def main():
         "hbm_ceiling": hbm,
         "cpu_baseline": cpu,
         "gate": head_gate,
+        "gate_failures": gate_failures,
         "sweeps": sweeps,
         "provenance": provenance(src_hash),
     }
